@@ -1,0 +1,198 @@
+#!/usr/bin/env python3
+"""Throughput of the convolution hot path on one MI355X.
+
+A step is one forward convolution through the C ABI (host dispatch ->
+implicit-GEMM kernel: padded-window gather, LDS staging, fp32 MFMA, split
+reduction, epilogue, store) on the 1x512x7x7 -> 512, 3x3, stride 1, pad 1
+fp32 layer (the final ResNet layer of the TVM tutorial's tuning example),
+with seeded synthetic inputs already resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
+                    [--tune] [--no-cpu-baseline]
+
+K steps are captured in one HIP graph and replayed (default) or launched
+eagerly (--eager); HIP events on the launch stream bracket the K steps.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}  # dense matrix peaks, MI355X
+PEAK_HBM_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not a graph")
+    ap.add_argument("--tune", action="store_true", help="run the tile-config search first")
+    ap.add_argument("--tune-trials", type=int, default=0)
+    ap.add_argument("--tune-ms", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def _ensure_built():
+    from tensor_compiler_tiling_amd import convtile as ct
+    if not os.path.exists(ct.LIB_PATH):
+        from tensor_compiler_tiling_amd import build
+        build.build()
+
+
+def cpu_baseline(w, seconds: float) -> dict:
+    """The fp64 oracle as it stands, on this host's cores, on the same
+    workload (whole passes, repeated until about `seconds` have elapsed)."""
+    from oracle import oracle as O
+    from tensor_compiler_tiling_amd import workloads as wl
+    inp = wl.conv_inputs(w)
+    x = inp["x"].astype(np.float64)
+    k = inp["w"].astype(np.float64)
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.conv2d_nchw(x, k, w.stride, w.pad)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    tflops = w.flops * reps / el / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full passes of the fp64 seven-loop oracle on {w.name} "
+                      f"({el:.1f} s)"}
+
+
+def main():
+    a = _parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    _ensure_built()
+    import torch
+    from tensor_compiler_tiling_amd import convtile as ct
+    from tensor_compiler_tiling_amd import workloads as wl
+
+    name = a.workload or wl.HEADLINE
+    w = wl.CONV_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    inp = wl.conv_inputs(w)
+    x = torch.from_numpy(inp["x"]).to(dev).to(tdt)
+    k = torch.from_numpy(inp["w"]).to(dev).to(tdt)
+    b = torch.from_numpy(inp["bias"]).to(dev)
+    v = torch.from_numpy(inp["var"]).to(dev)
+    y = torch.empty((w.N, w.CO, w.OH, w.OW), dtype=torch.float32, device=dev)
+    dt = ct.dtype_code(tdt)
+    args = w.shape_args() + (dt, w.epilogue)
+
+    tune_info = None
+    if a.tune:
+        t0 = time.perf_counter()
+        st, best, recs = ct.ct_conv2d_tune(*args, max_trials=a.tune_trials,
+                                           min_repeat_ms=a.tune_ms)
+        ct.check(st, "tune")
+        tune_info = {"trials": len(recs), "seconds": round(time.perf_counter() - t0, 2),
+                     "best_us": round(best.us, 3)}
+    st, cfg, from_cache = ct.ct_conv2d_query(*args)
+    ct.check(st, "query")
+    vdesc = ct.variants()[cfg.variant]
+
+    stream = torch.cuda.current_stream()
+
+    def step():
+        st = ct.ct_conv2d_nchw_fwd(x, k, y, *args, b, v, 1e-5, stream.cuda_stream)
+        if st != 0:
+            raise ct.ConvTileError(st, "fwd")
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    graph = None
+    if not a.eager:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(a.steps):
+                step()
+        torch.cuda.synchronize()
+        graph.replay()  # warm replay
+        torch.cuda.synchronize()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(a.steps):
+            step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / a.steps
+    tflops = w.flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    # eager launch rate through the C ABI, for reference
+    eager_ms = None
+    if graph is not None:
+        e0.record(stream)
+        for _ in range(a.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / a.steps
+
+    out = {
+        "metric": "conv2d TFLOP/s per shape (fp32, batch 1) and % of MFMA peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded U[-1,1] inputs, He-normal weights)",
+        "config": {"workload": name, "N": w.N, "CI": w.CI, "H": w.H, "W": w.W, "CO": w.CO,
+                   "KH": w.KH, "KW": w.KW, "stride": w.stride, "pad": w.pad,
+                   "epilogue": w.epilogue, "flops_per_step": w.flops,
+                   "launch": "hip_graph" if graph is not None else "eager",
+                   "kernel": vdesc["name"], "split_k": cfg.split_k, "stages": cfg.stages,
+                   "kc": cfg.kc, "config_index": cfg.index, "from_cache": bool(from_cache)},
+        "pct_of_peak": round(100.0 * tflops / peak, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+        "eager_ms_per_step": round(eager_ms, 6) if eager_ms else None,
+        "wall_s": round(wall, 4),
+    }
+    if tune_info:
+        out["tune"] = tune_info
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

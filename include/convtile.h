@@ -1,0 +1,231 @@
+/*
+ * convtile -- NCHW 2-D convolution (implicit GEMM on CDNA4 matrix cores) and
+ * per-channel broadcast for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (TVM tutorial "Tuning High Performance Convolution on NVIDIA
+ * GPUs", Step 1, the conv2d_nchw compute of the template):
+ *
+ *   y[n][f][oy][ox] = sum_{c<CI} sum_{ky<KH} sum_{kx<KW}
+ *                     xp[n][c][oy*stride+ky][ox*stride+kx] * w[f][c][ky][kx]
+ *
+ *   xp = x zero-padded by `pad` on every side (never materialised: padding is
+ *   applied inline while gathering), dilation 1, no kernel flip, and
+ *   OH = (H + 2 pad - KH) / stride + 1, OW likewise (integer division).
+ *   Output is always fp32 (the template's out_dtype='float32'), also for fp16 /
+ *   bf16 inputs, which are multiplied exactly and accumulated in fp32.
+ *
+ * Optional per-channel epilogue (Paddle PR "[CINN] Add the TileBroadcastTactic
+ * for NCHW broadcast", Performance Impact: per-channel div/exp/rsqrt chains,
+ * with the channel bound to a grid axis so its value is computed once per
+ * workgroup):
+ *   CT_EPI_NONE            out = y
+ *   CT_EPI_BIAS            out = y + bias[f]
+ *   CT_EPI_EXP_BIAS_RSQRT  out = exp(y + bias[f]) * rsqrt(var[f] + eps)
+ *
+ * Layouts (all contiguous, row-major, device memory owned by the caller):
+ *   x    [N][CI][H][W]      dtype CT_F32 (float), CT_F16 (IEEE half), CT_BF16
+ *   w    [CO][CI][KH][KW]   same dtype as x
+ *   y    [N][CO][OH][OW]    float; must not alias x, w, bias or var
+ *   bias [CO], var [CO]     float (NULL when the epilogue does not read them)
+ *
+ * Conventions
+ *   - Every entry point returns a status (CT_OK = 0, negative on error) and
+ *     never throws across the ABI.  ct_last_error() gives a message for the
+ *     last failure on the calling thread.
+ *   - Argument errors are reported with CT_ERR_INVALID_ARG before any HIP call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Launch calls are
+ *     asynchronous on that stream and never synchronise.
+ *   - The library owns: the compiled kernels, a process-wide tile-config cache
+ *     (mutex-protected), and per-(device, stream) split-reduction workspaces
+ *     (grow-only; allocated with hipMalloc on first need, never freed before
+ *     ct_release()).  Two launches that use split reduction on the same stream
+ *     are ordered by the stream; launches on different streams get different
+ *     workspaces.
+ */
+#ifndef CONVTILE_H
+#define CONVTILE_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ---------------------------------------------------- */
+#define CT_OK 0
+#define CT_ERR_INVALID_ARG (-1)  /* bad shape, NULL pointer, unknown enum      */
+#define CT_ERR_UNSUPPORTED (-2)  /* legal arguments no kernel here can run    */
+#define CT_ERR_HIP (-3)          /* a HIP runtime call failed                 */
+#define CT_ERR_NO_MEMORY (-4)    /* workspace / scratch allocation failed     */
+#define CT_ERR_IO (-5)           /* cache file could not be read or written   */
+#define CT_ERR_TUNE_FAILED (-6)  /* no candidate of the search ran correctly  */
+
+/* ---- enums ------------------------------------------------------------ */
+enum ct_dtype { CT_F32 = 0, CT_F16 = 1, CT_BF16 = 2 };
+enum ct_epilogue { CT_EPI_NONE = 0, CT_EPI_BIAS = 1, CT_EPI_EXP_BIAS_RSQRT = 2 };
+enum ct_bcast_op { CT_BC_EXP = 0 };
+enum ct_bcast_mode {
+    CT_BC_AUTO = 0,    /* channel-bound when it applies, else flat            */
+    CT_BC_CHANNEL = 1, /* channel index on a grid axis; value computed once   */
+    CT_BC_FLAT = 2     /* all axes fused; value loaded and computed per element */
+};
+
+/* Measurement outcome codes of a tuning trial (the meanings of the autotvm
+ * MeasureResult error_no values printed in the tutorial's tuning log). */
+enum ct_trial_error {
+    CT_TRIAL_OK = 0,
+    CT_TRIAL_ILLEGAL = 1,  /* rejected by the legality check, never launched */
+    CT_TRIAL_RUNTIME = 4,  /* HIP error, or output differs from the reference */
+    CT_TRIAL_TIMEOUT = 6   /* exceeded the per-trial time limit               */
+};
+
+/* One point of a shape's tile-config space. */
+typedef struct ct_tile_config {
+    int variant;     /* kernel variant id (see ct_variant_info)               */
+    int split_k;     /* S: workgroups that share one output tile's reduction  */
+    int stages;      /* LDS stages each workgroup runs                        */
+    int kc;          /* input channels per LDS stage                          */
+    long long index; /* flat index in the shape's space; -1 = not from space  */
+    float us;        /* mean microseconds per launch when measured, else 0    */
+    int error_no;    /* ct_trial_error of the measurement, 0 if never timed   */
+} ct_tile_config;
+
+/* A compiled kernel variant (one instantiation of the tiled template). */
+typedef struct ct_variant_desc {
+    char name[48];
+    int dtype;        /* ct_dtype it accepts                                   */
+    int kind;         /* 0 = direct (one lane per output), 1 = implicit GEMM   */
+    int mfma_m, mfma_n, mfma_k; /* matrix-core instruction shape (0 for direct) */
+    int waves_m, waves_n, waves_k; /* waves per workgroup along CO, P, K       */
+    int reps_m, reps_n;  /* MFMA tiles per wave along CO and P                 */
+    int tile_m, tile_n;  /* workgroup output tile: CO x P                      */
+    int kc_max;          /* most input channels one LDS stage holds            */
+    int threads;         /* workgroup size                                     */
+} ct_variant_desc;
+
+/* One timed candidate of ct_conv2d_tune (autotvm MeasureResult analogue). */
+typedef struct ct_tune_record {
+    ct_tile_config cfg;
+    float costs_us[3];   /* mean us per launch of each repeat                  */
+    int n_costs;
+    int error_no;        /* ct_trial_error                                     */
+    double all_cost_s;   /* wall seconds spent on this trial                   */
+    double timestamp;    /* seconds since the epoch when the trial ended       */
+} ct_tune_record;
+
+/* ---- convolution ----------------------------------------------------- */
+
+/* Forward convolution with the cached tile config for this shape (or the
+ * built-in default when none is cached).  Shapes/layouts as above; `eps` is
+ * used only by CT_EPI_EXP_BIAS_RSQRT.  Errors: CT_ERR_INVALID_ARG for any
+ * dimension <= 0, stride <= 0, pad < 0, OH or OW <= 0, NULL x/w/y, unknown
+ * dtype/epilogue, or bias/var missing when the epilogue reads them;
+ * CT_ERR_NO_MEMORY if the split workspace cannot grow; CT_ERR_HIP on a launch
+ * failure. */
+int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y,
+                       int N, int CI, int H, int W, int CO, int KH, int KW,
+                       int stride, int pad, int dtype, int epilogue,
+                       const float* bias, const float* var, float eps,
+                       void* stream);
+
+/* The same with an explicit tile config (cfg->variant, split_k, stages, kc);
+ * cfg->index is ignored.  Returns CT_ERR_UNSUPPORTED when the config is not
+ * legal for the shape (the check of ct_conv2d_space_entity). */
+int ct_conv2d_nchw_fwd_config(const void* x, const void* w, float* y,
+                              int N, int CI, int H, int W, int CO, int KH, int KW,
+                              int stride, int pad, int dtype, int epilogue,
+                              const float* bias, const float* var, float eps,
+                              const ct_tile_config* cfg, void* stream);
+
+/* Reference kernel: one lane per output, fp32 fused multiply-add over the
+ * taps in definition order.  Slow; used as the on-device check of every
+ * tuning candidate.  Same arguments and errors as ct_conv2d_nchw_fwd. */
+int ct_conv2d_nchw_direct(const void* x, const void* w, float* y,
+                          int N, int CI, int H, int W, int CO, int KH, int KW,
+                          int stride, int pad, int dtype, int epilogue,
+                          const float* bias, const float* var, float eps,
+                          void* stream);
+
+/* ---- tile-config search ----------------------------------------------
+ * The space of a shape follows the TVM tutorial's template (Step 1): ordered
+ * knobs, each a split (all ordered factorizations of an extent, the
+ * "policy=all" of the gist's ConfigSpace dump) or an option list, and a flat
+ * index that is mixed radix over the knobs with the first knob least
+ * significant.  Knobs here, in order:
+ *   tile_ci = split(CI, 3) -> [split_k, stages, kc]
+ *   variant = option(ids of the compiled variants for the dtype)
+ */
+
+/* Number of points in the space of this shape (legal or not); < 0 on error. */
+long long ct_conv2d_space_size(int N, int CI, int H, int W, int CO, int KH, int KW,
+                               int stride, int pad, int dtype, int epilogue);
+
+/* Decode flat `index` into *cfg_out and report in *legal (1/0) whether the
+ * point passes the legality check (LDS bytes within 160 KiB, workgroup size
+ * within 1024, channels per stage within the variant's limit, ...).  The
+ * check never launches anything.  CT_ERR_INVALID_ARG for an index outside
+ * [0, size). */
+int ct_conv2d_space_entity(int N, int CI, int H, int W, int CO, int KH, int KW,
+                           int stride, int pad, int dtype, int epilogue,
+                           long long index, ct_tile_config* cfg_out, int* legal);
+
+/* Enumerate the legal points, time up to `max_trials` of them on `stream`
+ * (0 = all legal points), keep the fastest whose output matches the direct
+ * reference kernel, store it in the cache and in *best_out.  Timing follows
+ * the tutorial's runner: a warm-up, then `repeat` (3) measurements each of at
+ * least `min_repeat_ms` milliseconds of back-to-back launches, a per-trial
+ * limit of 4 s.  Scratch inputs are allocated and filled on the device by the
+ * library.  `records` (may be NULL) receives up to `max_records` trial records
+ * and *n_records their count.  Synchronises the stream; may take seconds.
+ * Returns CT_ERR_TUNE_FAILED if no candidate ran correctly. */
+int ct_conv2d_tune(int N, int CI, int H, int W, int CO, int KH, int KW,
+                   int stride, int pad, int dtype, int epilogue,
+                   int max_trials, float min_repeat_ms, void* stream,
+                   ct_tile_config* best_out,
+                   ct_tune_record* records, int max_records, int* n_records);
+
+/* The config ct_conv2d_nchw_fwd would use for this shape; *from_cache = 1
+ * when it came from a tuning record, 0 when it is the built-in default. */
+int ct_conv2d_query(int N, int CI, int H, int W, int CO, int KH, int KW,
+                    int stride, int pad, int dtype, int epilogue,
+                    ct_tile_config* cfg_out, int* from_cache);
+
+/* Compiled variants. */
+int ct_variant_count(void);
+int ct_variant_info(int variant, ct_variant_desc* out);
+
+/* Ordered factorizations of n into k factors ("policy=all" split): count, and
+ * the i-th one written to out[0..k-1] in the space's order (ascending by
+ * (x_k, ..., x_2)).  Count < 0 for n <= 0 or k outside [1, 8]. */
+long long ct_split_count(long long n, int k);
+int ct_split_entity(long long n, int k, long long i, long long* out);
+
+/* ---- per-channel broadcast --------------------------------------------
+ * out[n][c][h][w] = exp(var[c])  (Paddle PR, Introduction and Example:
+ * [1,C,1,1] => [N,C,H,W]).  var: C floats on the device; out: N*C*H*W
+ * elements of out_dtype (CT_F32 or CT_F16, rounded to nearest even).  The
+ * channel-bound form needs H*W % 32 == 0 and a 16-byte aligned `out`;
+ * CT_BC_AUTO falls back to the flat form otherwise, CT_BC_CHANNEL returns
+ * CT_ERR_UNSUPPORTED.  Results are identical in every mode. */
+int ct_broadcast_nchw(const float* var, void* out, int N, int C, int H, int W,
+                      int out_dtype, int op, int mode, void* stream);
+
+/* ---- cache, lifetime, errors ----------------------------------------- */
+
+/* Append-only JSON-lines cache of tuning winners (one record per line).
+ * load merges the file into memory (lines that do not parse are skipped);
+ * save appends every in-memory record to the file.  CT_ERR_IO on failure. */
+int ct_cache_load(const char* path);
+int ct_cache_save(const char* path);
+int ct_cache_clear(void);
+int ct_cache_size(void);
+
+/* Free the library's device workspaces (all devices, all streams). */
+int ct_release(void);
+
+const char* ct_status_string(int status);
+const char* ct_last_error(void);
+const char* ct_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CONVTILE_H */

@@ -1,0 +1,339 @@
+"""ctypes binding of libconvtile.so (include/convtile.h).
+
+Argument marshalling only: every computation runs in the library's HIP
+kernels.  The functions named like the C entry points take device pointers
+(ints) or torch tensors and return the C status; the short helpers
+(``conv2d``, ``broadcast``, ``tune``, ``query``) allocate outputs with torch
+and raise ``ConvTileError`` on a non-zero status.  There is no fallback: if
+the library is missing, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libconvtile.so")
+
+CT_OK = 0
+CT_ERR_INVALID_ARG = -1
+CT_ERR_UNSUPPORTED = -2
+CT_ERR_HIP = -3
+CT_ERR_NO_MEMORY = -4
+CT_ERR_IO = -5
+CT_ERR_TUNE_FAILED = -6
+
+CT_F32, CT_F16, CT_BF16 = 0, 1, 2
+CT_EPI_NONE, CT_EPI_BIAS, CT_EPI_EXP_BIAS_RSQRT = 0, 1, 2
+CT_BC_EXP = 0
+CT_BC_AUTO, CT_BC_CHANNEL, CT_BC_FLAT = 0, 1, 2
+CT_TRIAL_OK, CT_TRIAL_ILLEGAL, CT_TRIAL_RUNTIME, CT_TRIAL_TIMEOUT = 0, 1, 4, 6
+
+
+class ct_tile_config(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int), ("split_k", ctypes.c_int), ("stages", ctypes.c_int),
+                ("kc", ctypes.c_int), ("index", ctypes.c_longlong), ("us", ctypes.c_float),
+                ("error_no", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class ct_variant_desc(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("dtype", ctypes.c_int), ("kind", ctypes.c_int),
+                ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int),
+                ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int), ("waves_k", ctypes.c_int),
+                ("reps_m", ctypes.c_int), ("reps_n", ctypes.c_int), ("tile_m", ctypes.c_int),
+                ("tile_n", ctypes.c_int), ("kc_max", ctypes.c_int), ("threads", ctypes.c_int)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["name"] = self.name.decode()
+        return d
+
+
+class ct_tune_record(ctypes.Structure):
+    _fields_ = [("cfg", ct_tile_config), ("costs_us", ctypes.c_float * 3), ("n_costs", ctypes.c_int),
+                ("error_no", ctypes.c_int), ("all_cost_s", ctypes.c_double),
+                ("timestamp", ctypes.c_double)]
+
+
+class ConvTileError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        lib = _load()
+        msg = lib.ct_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {lib.ct_status_string(status).decode()} ({status}): {msg}")
+
+
+_I, _LL, _F, _P = ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_void_p
+_SHAPE = [_I] * 11  # N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue
+
+_SIGS = {
+    "ct_conv2d_nchw_fwd": (_I, [_P, _P, _P] + [_I] * 11 + [_P, _P, _F, _P]),
+    "ct_conv2d_nchw_fwd_config": (_I, [_P, _P, _P] + [_I] * 11 +
+                                  [_P, _P, _F, ctypes.POINTER(ct_tile_config), _P]),
+    "ct_conv2d_nchw_direct": (_I, [_P, _P, _P] + [_I] * 11 + [_P, _P, _F, _P]),
+    "ct_conv2d_space_size": (_LL, _SHAPE),
+    "ct_conv2d_space_entity": (_I, _SHAPE + [_LL, ctypes.POINTER(ct_tile_config),
+                                             ctypes.POINTER(_I)]),
+    "ct_conv2d_tune": (_I, _SHAPE + [_I, _F, _P, ctypes.POINTER(ct_tile_config),
+                                     ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
+    "ct_conv2d_query": (_I, _SHAPE + [ctypes.POINTER(ct_tile_config), ctypes.POINTER(_I)]),
+    "ct_variant_count": (_I, []),
+    "ct_variant_info": (_I, [_I, ctypes.POINTER(ct_variant_desc)]),
+    "ct_split_count": (_LL, [_LL, _I]),
+    "ct_split_entity": (_I, [_LL, _I, _LL, ctypes.POINTER(_LL)]),
+    "ct_broadcast_nchw": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "ct_cache_load": (_I, [ctypes.c_char_p]),
+    "ct_cache_save": (_I, [ctypes.c_char_p]),
+    "ct_cache_clear": (_I, []),
+    "ct_cache_size": (_I, []),
+    "ct_release": (_I, []),
+    "ct_status_string": (ctypes.c_char_p, [_I]),
+    "ct_last_error": (ctypes.c_char_p, []),
+    "ct_version": (ctypes.c_char_p, []),
+}
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m tensor_compiler_tiling_amd.build` (no CPU fallback exists)")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def exported_names() -> List[str]:
+    return list(_SIGS)
+
+
+# ---------------------------------------------------------------- marshal --
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a torch tensor or a device pointer, got {type(t)}")
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def dtype_code(torch_dtype) -> int:
+    import torch
+    m = {torch.float32: CT_F32, torch.float16: CT_F16, torch.bfloat16: CT_BF16}
+    if torch_dtype not in m:
+        raise ValueError(f"unsupported dtype {torch_dtype}")
+    return m[torch_dtype]
+
+
+def out_extent(inp: int, k: int, stride: int, pad: int) -> int:
+    return (inp + 2 * pad - k) // stride + 1
+
+
+# ------------------------------------------------- entry points (same names) --
+def ct_conv2d_nchw_fwd(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,
+                       bias=None, var=None, eps=1e-5, stream=None) -> int:
+    return _load().ct_conv2d_nchw_fwd(_ptr(x), _ptr(w), _ptr(y), N, CI, H, W, CO, KH, KW, stride,
+                                      pad, dtype, epilogue, _ptr(bias), _ptr(var), eps,
+                                      _stream(stream))
+
+
+def ct_conv2d_nchw_fwd_config(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,
+                              bias, var, eps, cfg: ct_tile_config, stream=None) -> int:
+    return _load().ct_conv2d_nchw_fwd_config(_ptr(x), _ptr(w), _ptr(y), N, CI, H, W, CO, KH, KW,
+                                             stride, pad, dtype, epilogue, _ptr(bias), _ptr(var),
+                                             eps, ctypes.byref(cfg), _stream(stream))
+
+
+def ct_conv2d_nchw_direct(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,
+                          bias=None, var=None, eps=1e-5, stream=None) -> int:
+    return _load().ct_conv2d_nchw_direct(_ptr(x), _ptr(w), _ptr(y), N, CI, H, W, CO, KH, KW,
+                                         stride, pad, dtype, epilogue, _ptr(bias), _ptr(var), eps,
+                                         _stream(stream))
+
+
+def ct_conv2d_space_size(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue) -> int:
+    return _load().ct_conv2d_space_size(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue)
+
+
+def ct_conv2d_space_entity(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,
+                           index) -> Tuple[int, ct_tile_config, int]:
+    cfg = ct_tile_config()
+    legal = _I(0)
+    st = _load().ct_conv2d_space_entity(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,
+                                        index, ctypes.byref(cfg), ctypes.byref(legal))
+    return st, cfg, legal.value
+
+
+def ct_conv2d_tune(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials=0,
+                   min_repeat_ms=100.0, stream=None, max_records=4096):
+    best = ct_tile_config()
+    recs = (ct_tune_record * max(max_records, 1))()
+    n = _I(0)
+    st = _load().ct_conv2d_tune(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials,
+                                min_repeat_ms, _stream(stream), ctypes.byref(best), recs,
+                                max_records, ctypes.byref(n))
+    return st, best, [recs[i] for i in range(n.value)]
+
+
+def ct_conv2d_query(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue):
+    cfg = ct_tile_config()
+    fc = _I(0)
+    st = _load().ct_conv2d_query(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,
+                                 ctypes.byref(cfg), ctypes.byref(fc))
+    return st, cfg, fc.value
+
+
+def ct_variant_count() -> int:
+    return _load().ct_variant_count()
+
+
+def ct_variant_info(v: int):
+    d = ct_variant_desc()
+    st = _load().ct_variant_info(v, ctypes.byref(d))
+    return st, d
+
+
+def ct_split_count(n: int, k: int) -> int:
+    return _load().ct_split_count(n, k)
+
+
+def ct_split_entity(n: int, k: int, i: int):
+    out = (_LL * k)()
+    st = _load().ct_split_entity(n, k, i, out)
+    return st, list(out)
+
+
+def ct_broadcast_nchw(var, out, N, C, H, W, out_dtype, op=CT_BC_EXP, mode=CT_BC_AUTO,
+                      stream=None) -> int:
+    return _load().ct_broadcast_nchw(_ptr(var), _ptr(out), N, C, H, W, out_dtype, op, mode,
+                                     _stream(stream))
+
+
+def ct_cache_load(path: str) -> int:
+    return _load().ct_cache_load(path.encode())
+
+
+def ct_cache_save(path: str) -> int:
+    return _load().ct_cache_save(path.encode())
+
+
+def ct_cache_clear() -> int:
+    return _load().ct_cache_clear()
+
+
+def ct_cache_size() -> int:
+    return _load().ct_cache_size()
+
+
+def ct_release() -> int:
+    return _load().ct_release()
+
+
+def ct_status_string(st: int) -> str:
+    return _load().ct_status_string(st).decode()
+
+
+def ct_last_error() -> str:
+    return _load().ct_last_error().decode(errors="replace")
+
+
+def ct_version() -> str:
+    return _load().ct_version().decode()
+
+
+def check(status: int, where: str = "convtile") -> None:
+    if status != CT_OK:
+        raise ConvTileError(status, where)
+
+
+# ------------------------------------------------------------ helpers --------
+def variants() -> List[dict]:
+    out = []
+    for v in range(ct_variant_count()):
+        st, d = ct_variant_info(v)
+        check(st, "ct_variant_info")
+        out.append(dict(d.as_dict(), id=v))
+    return out
+
+
+def variant_id(name: str) -> int:
+    for d in variants():
+        if d["name"] == name:
+            return d["id"]
+    raise KeyError(name)
+
+
+def conv2d(x, w, stride: int = 1, pad: int = 0, epilogue: int = CT_EPI_NONE, bias=None, var=None,
+           eps: float = 1e-5, config: Optional[ct_tile_config] = None, out=None, stream=None,
+           direct: bool = False):
+    """y = conv2d_nchw(x, w) (+ epilogue), fp32 output allocated with torch."""
+    import torch
+    N, CI, H, W = x.shape
+    CO, CI2, KH, KW = w.shape
+    if CI2 != CI or w.dtype != x.dtype:
+        raise ValueError("x and w disagree in channels or dtype")
+    OH, OW = out_extent(H, KH, stride, pad), out_extent(W, KW, stride, pad)
+    y = out if out is not None else torch.empty((N, CO, OH, OW), dtype=torch.float32,
+                                                device=x.device)
+    dt = dtype_code(x.dtype)
+    if direct:
+        st = ct_conv2d_nchw_direct(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dt, epilogue,
+                                   bias, var, eps, stream)
+    elif config is not None:
+        st = ct_conv2d_nchw_fwd_config(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dt,
+                                       epilogue, bias, var, eps, config, stream)
+    else:
+        st = ct_conv2d_nchw_fwd(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dt, epilogue, bias,
+                                var, eps, stream)
+    check(st, "conv2d")
+    return y
+
+
+def broadcast(var, N: int, H: int, W: int, out_dtype=None, mode: int = CT_BC_AUTO, out=None,
+              stream=None):
+    """[1,C,1,1] -> [N,C,H,W] of exp(var[c])."""
+    import torch
+    out_dtype = out_dtype or torch.float16
+    C = var.numel()
+    o = out if out is not None else torch.empty((N, C, H, W), dtype=out_dtype, device=var.device)
+    st = ct_broadcast_nchw(var, o, N, C, H, W, dtype_code(o.dtype), CT_BC_EXP, mode, stream)
+    check(st, "broadcast")
+    return o
+
+
+def make_config(variant, split_k: int, stages: int, kc: int) -> ct_tile_config:
+    c = ct_tile_config()
+    c.variant = variant if isinstance(variant, int) else variant_id(variant)
+    c.split_k, c.stages, c.kc, c.index = split_k, stages, kc, -1
+    return c

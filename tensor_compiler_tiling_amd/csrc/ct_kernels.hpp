@@ -1,0 +1,74 @@
+// Host-visible declarations shared by the C-ABI runtime and the HIP kernel
+// files.  No torch types anywhere: plain pointers and sizes.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace ct {
+
+// Everything a convolution launch needs, resolved on the host.
+struct ConvParams {
+    const void* x;
+    const void* w;
+    float* y;
+    const float* bias;
+    const float* var;
+    float eps;
+    int N, CI, H, W, CO, KH, KW, stride, pad, OH, OW;
+    int T;          // KH * KW taps
+    int K;          // CI * T, the GEMM reduction length
+    long long P;    // N * OH * OW, the GEMM column count
+    int OHW;        // OH * OW
+    int epilogue;   // ct_epilogue
+    // implicit-GEMM tiling (resolved from a ct_tile_config)
+    int kc;         // input channels per LDS stage
+    int stages;     // LDS stages per workgroup
+    int S;          // workgroups sharing one output tile's reduction
+    int tiles_m;    // ceil(CO / tile_m)
+    int tiles_n;    // ceil(P / tile_n)
+    int R;          // padded-input window rows held in LDS per stage
+    int Hp, Wp;     // padded input height / width (H + 2 pad, W + 2 pad)
+    float* ws;      // S partial tiles per output tile (S > 1 only)
+    unsigned* tickets;  // one arrival counter per output tile (S > 1 only)
+};
+
+// Static description of one compiled implicit-GEMM instantiation.
+struct IgemmVariant {
+    const char* name;
+    int dtype;
+    int mfma_m, mfma_n, mfma_k;
+    int waves_m, waves_n, waves_k;
+    int reps_m, reps_n;
+    int kc_max;
+    // LDS bytes the variant needs for a stage of `kc` channels with a window
+    // of R rows by Wp columns and T taps.
+    int (*lds_bytes)(int kc, int R, int Wp, int T);
+    hipError_t (*launch)(const ConvParams& p, hipStream_t stream);
+};
+
+// Kernel-file registries.
+const IgemmVariant* igemm_f32_variants(int* count);
+const IgemmVariant* igemm_f16_variants(int* count);
+
+// Direct (one lane per output) reference kernel.
+hipError_t launch_conv_direct(const ConvParams& p, int dtype, hipStream_t stream);
+
+// Broadcast out[n][c][hw] = exp(var[c]).
+//   channel-bound: grid axis over channels, rows_per_block images per block.
+//   flat: fused index, value recomputed per element.
+hipError_t launch_bcast_channel(const float* var, void* out, int N, int C, int HW,
+                                int out_dtype, hipStream_t stream);
+hipError_t launch_bcast_flat(const float* var, void* out, int N, int C, int HW,
+                             int out_dtype, hipStream_t stream);
+
+// Deterministic device fill used by the tuner's scratch inputs:
+// v[i] = lo + (hi - lo) * u(i, seed), u a counter-based hash in [0, 1).
+hipError_t launch_fill_uniform(void* dst, long long n, int dtype, float lo, float hi,
+                               unsigned seed, hipStream_t stream);
+
+// max over i of |a[i] - b[i]| / (atol + rtol * |b[i]|) > 1 ?  writes a flag.
+hipError_t launch_compare(const float* a, const float* b, long long n, float atol,
+                          float rtol, unsigned* bad_count, hipStream_t stream);
+
+}  // namespace ct

@@ -1,0 +1,1115 @@
+// C-ABI runtime of convtile: argument checking, the tile-config space and its
+// legality check, the built-in default config, the tuning search, the
+// per-shape cache (append-only JSON lines), split-reduction workspaces and
+// dispatch to the HIP kernels.
+//
+// The search space and its bookkeeping follow the TVM tutorial "Tuning High
+// Performance Convolution on NVIDIA GPUs" (Step 1: define_split with all
+// ordered factorizations, define_knob option lists; Step 2: LocalRunner with
+// repeat=3, min_repeat_ms=100, timeout=4 and a log file of measure records;
+// the final part: apply_history_best / query of the best record per
+// workload).  Measurement outcome codes keep the meanings printed in the
+// tuning log of the gist that reproduces it (0 ok, 1 rejected as an invalid
+// kernel before running, 4 runtime error, 6 timeout).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <map>
+#include <mutex>
+#include <sstream>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/convtile.h"
+#include "ct_kernels.hpp"
+#include "igemm_common.hpp"
+
+namespace ct {
+namespace {
+
+constexpr int kMaxLds = 163840;       // bytes of LDS per workgroup on gfx950
+constexpr int kMaxThreads = 1024;     // workgroup size limit
+constexpr int kNumCU = 256;           // compute units of an MI355X
+constexpr long long kMaxWorkspace = 1LL << 30;  // split partials, bytes
+constexpr const char* kArch = "gfx950";
+constexpr int kSpaceVersion = 1;
+
+// ---------------------------------------------------------------- errors --
+thread_local char g_last_error[512] = "";
+
+void set_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+}
+
+int fail(int status, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(CT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool log_debug() {
+    static int v = -1;
+    if (v < 0) {
+        const char* s = getenv("CT_LOG");
+        v = (s && strcmp(s, "debug") == 0) ? 1 : 0;
+    }
+    return v == 1;
+}
+
+// ---------------------------------------------------------------- shapes --
+struct Shape {
+    int N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue;
+    int OH, OW;
+    long long P;
+    int T, K;
+
+    std::string key() const {
+        char buf[256];
+        snprintf(buf, sizeof(buf), "%d,%d,%d,%d,%d,%d,%d,%d,%d,%d,%d,%s,v%d", N, CI, H, W, CO, KH,
+                 KW, stride, pad, dtype, epilogue, kArch, kSpaceVersion);
+        return buf;
+    }
+};
+
+int make_shape(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad,
+               int dtype, int epilogue, Shape* s) {
+    if (N <= 0 || CI <= 0 || H <= 0 || W <= 0 || CO <= 0 || KH <= 0 || KW <= 0)
+        return fail(CT_ERR_INVALID_ARG, "every dimension must be positive");
+    if (stride <= 0) return fail(CT_ERR_INVALID_ARG, "stride must be positive");
+    if (pad < 0) return fail(CT_ERR_INVALID_ARG, "pad must be non-negative");
+    if (dtype != CT_F32 && dtype != CT_F16 && dtype != CT_BF16)
+        return fail(CT_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+    if (epilogue != CT_EPI_NONE && epilogue != CT_EPI_BIAS && epilogue != CT_EPI_EXP_BIAS_RSQRT)
+        return fail(CT_ERR_INVALID_ARG, "unknown epilogue %d", epilogue);
+    const long long Hp = (long long)H + 2LL * pad, Wp = (long long)W + 2LL * pad;
+    if (Hp < KH || Wp < KW) return fail(CT_ERR_INVALID_ARG, "kernel larger than padded input");
+    if (Hp > (1 << 24) || Wp > (1 << 24)) return fail(CT_ERR_INVALID_ARG, "input too large");
+    s->N = N; s->CI = CI; s->H = H; s->W = W; s->CO = CO; s->KH = KH; s->KW = KW;
+    s->stride = stride; s->pad = pad; s->dtype = dtype; s->epilogue = epilogue;
+    s->OH = (int)((Hp - KH) / stride + 1);
+    s->OW = (int)((Wp - KW) / stride + 1);
+    if (s->OH <= 0 || s->OW <= 0) return fail(CT_ERR_INVALID_ARG, "empty output");
+    const long long T = (long long)KH * KW;
+    const long long K = (long long)CI * T;
+    if (K > (1LL << 30)) return fail(CT_ERR_INVALID_ARG, "reduction too long");
+    s->T = (int)T;
+    s->K = (int)K;
+    s->P = (long long)N * s->OH * s->OW;
+    if ((long long)s->OH * s->OW > (1LL << 30)) return fail(CT_ERR_INVALID_ARG, "output too large");
+    if (s->P * CO > (1LL << 40)) return fail(CT_ERR_INVALID_ARG, "output too large");
+    return CT_OK;
+}
+
+int check_pointers(const void* x, const void* w, const float* y, int epilogue, const float* bias,
+                   const float* var) {
+    if (!x || !w || !y) return fail(CT_ERR_INVALID_ARG, "x, w and y must not be NULL");
+    if (epilogue != CT_EPI_NONE && !bias)
+        return fail(CT_ERR_INVALID_ARG, "the epilogue reads bias, which is NULL");
+    if (epilogue == CT_EPI_EXP_BIAS_RSQRT && !var)
+        return fail(CT_ERR_INVALID_ARG, "the epilogue reads var, which is NULL");
+    return CT_OK;
+}
+
+// -------------------------------------------------------------- variants --
+struct Variant {
+    ct_variant_desc desc;
+    const IgemmVariant* ig;  // nullptr for the direct kernel
+};
+
+const std::vector<Variant>& variants() {
+    static std::vector<Variant> v = [] {
+        std::vector<Variant> out;
+        const char* dnames[3] = {"direct_f32", "direct_f16", "direct_bf16"};
+        for (int dt = 0; dt < 3; ++dt) {
+            Variant d{};
+            snprintf(d.desc.name, sizeof(d.desc.name), "%s", dnames[dt]);
+            d.desc.dtype = dt;
+            d.desc.kind = 0;
+            d.desc.threads = 256;
+            d.ig = nullptr;
+            out.push_back(d);
+        }
+        int n32 = 0, n16 = 0;
+        const IgemmVariant* t32 = igemm_f32_variants(&n32);
+        const IgemmVariant* t16 = igemm_f16_variants(&n16);
+        auto add = [&](const IgemmVariant* t, int n) {
+            for (int i = 0; i < n; ++i) {
+                Variant v{};
+                snprintf(v.desc.name, sizeof(v.desc.name), "%s", t[i].name);
+                v.desc.dtype = t[i].dtype;
+                v.desc.kind = 1;
+                v.desc.mfma_m = t[i].mfma_m;
+                v.desc.mfma_n = t[i].mfma_n;
+                v.desc.mfma_k = t[i].mfma_k;
+                v.desc.waves_m = t[i].waves_m;
+                v.desc.waves_n = t[i].waves_n;
+                v.desc.waves_k = t[i].waves_k;
+                v.desc.reps_m = t[i].reps_m;
+                v.desc.reps_n = t[i].reps_n;
+                v.desc.tile_m = t[i].waves_m * t[i].reps_m * t[i].mfma_m;
+                v.desc.tile_n = t[i].waves_n * t[i].reps_n * t[i].mfma_n;
+                v.desc.kc_max = t[i].kc_max;
+                v.desc.threads = t[i].waves_m * t[i].waves_n * t[i].waves_k * 64;
+                v.ig = &t[i];
+                out.push_back(v);
+            }
+        };
+        add(t32, n32);
+        add(t16, n16);
+        return out;
+    }();
+    return v;
+}
+
+int find_variant(const char* name) {
+    const auto& vs = variants();
+    for (size_t i = 0; i < vs.size(); ++i)
+        if (strcmp(vs[i].desc.name, name) == 0) return (int)i;
+    return -1;
+}
+
+// Tiled variants that accept a dtype, in registry order: the option list of
+// the "variant" knob.
+std::vector<int> tiled_variants_for(int dtype) {
+    std::vector<int> ids;
+    const auto& vs = variants();
+    for (size_t i = 0; i < vs.size(); ++i)
+        if (vs[i].ig && vs[i].desc.dtype == dtype) ids.push_back((int)i);
+    return ids;
+}
+
+// --------------------------------------------------------------- splits ---
+// All ordered k-factorizations of n, ascending by (x_k, ..., x_2) with
+// x_1 = n / (x_2 ... x_k): the order of the "policy=all" split in the
+// tutorial's ConfigSpace (the flat indices printed in the tuning log follow
+// it).
+void gen_splits(long long n, int k, const std::vector<long long>& divs, int depth,
+                std::vector<long long>& tail_rev, std::vector<std::vector<long long>>& out) {
+    // tail_rev holds x_k, x_{k-1}, ... (outermost loop = x_k)
+    if (depth == k - 1) {
+        long long prod = 1;
+        for (long long f : tail_rev) prod *= f;
+        if (n % prod) return;
+        std::vector<long long> e(k);
+        e[0] = n / prod;
+        for (int i = 0; i < k - 1; ++i) e[k - 1 - i] = tail_rev[i];
+        out.push_back(e);
+        return;
+    }
+    long long prod = 1;
+    for (long long f : tail_rev) prod *= f;
+    for (long long d : divs) {
+        if ((n / prod) % d) continue;  // prefix must still divide n
+        tail_rev.push_back(d);
+        gen_splits(n, k, divs, depth + 1, tail_rev, out);
+        tail_rev.pop_back();
+    }
+}
+
+const std::vector<std::vector<long long>>& splits(long long n, int k) {
+    static std::mutex mu;
+    static std::map<std::pair<long long, int>, std::vector<std::vector<long long>>> memo;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = memo.find({n, k});
+    if (it != memo.end()) return it->second;
+    std::vector<long long> divs;
+    for (long long d = 1; d * d <= n; ++d)
+        if (n % d == 0) {
+            divs.push_back(d);
+            if (d != n / d) divs.push_back(n / d);
+        }
+    std::sort(divs.begin(), divs.end());
+    std::vector<std::vector<long long>> out;
+    std::vector<long long> tail;
+    if (k == 1)
+        out.push_back({n});
+    else
+        gen_splits(n, k, divs, 0, tail, out);
+    return memo.emplace(std::make_pair(n, k), std::move(out)).first->second;
+}
+
+// ---------------------------------------------------------------- space ---
+// knobs: tile_ci = split(CI, 3) -> [split_k, stages, kc]; variant = option.
+struct Space {
+    const std::vector<std::vector<long long>>* ci;
+    std::vector<int> var_ids;
+    long long size() const { return (long long)ci->size() * (long long)var_ids.size(); }
+};
+
+Space space_of(const Shape& s) {
+    Space sp;
+    sp.ci = &splits(s.CI, 3);
+    sp.var_ids = tiled_variants_for(s.dtype);
+    return sp;
+}
+
+bool decode(const Space& sp, long long index, ct_tile_config* cfg) {
+    if (index < 0 || index >= sp.size()) return false;
+    const long long nci = (long long)sp.ci->size();
+    const auto& e = (*sp.ci)[index % nci];
+    cfg->split_k = (int)e[0];
+    cfg->stages = (int)e[1];
+    cfg->kc = (int)e[2];
+    cfg->variant = sp.var_ids[index / nci];
+    cfg->index = index;
+    cfg->us = 0.0f;
+    cfg->error_no = 0;
+    return true;
+}
+
+long long encode(const Space& sp, const ct_tile_config& c) {
+    const long long nci = (long long)sp.ci->size();
+    long long ici = -1, iv = -1;
+    for (long long i = 0; i < nci; ++i) {
+        const auto& e = (*sp.ci)[i];
+        if (e[0] == c.split_k && e[1] == c.stages && e[2] == c.kc) {
+            ici = i;
+            break;
+        }
+    }
+    for (size_t i = 0; i < sp.var_ids.size(); ++i)
+        if (sp.var_ids[i] == c.variant) iv = (long long)i;
+    if (ici < 0 || iv < 0) return -1;
+    return ici + nci * iv;
+}
+
+// Largest padded-input window (rows) any column tile of width tile_n needs.
+int window_rows(const Shape& s, int tile_n) {
+    static std::mutex mu;
+    static std::map<std::pair<std::string, int>, int> memo;
+    const std::string k = s.key();
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        auto it = memo.find({k, tile_n});
+        if (it != memo.end()) return it->second;
+    }
+    const int Hp = s.H + 2 * s.pad;
+    const int OHW = s.OH * s.OW;
+    long long best = 0;
+    for (long long p0 = 0; p0 < s.P; p0 += tile_n) {
+        const long long p1 = std::min(s.P, p0 + tile_n);
+        best = std::max(best, window_rows_for(p0, p1, OHW, s.OW, Hp, s.stride, s.KH));
+    }
+    const int r = (int)std::min<long long>(best, 1 << 30);
+    std::lock_guard<std::mutex> lk(mu);
+    memo[{k, tile_n}] = r;
+    return r;
+}
+
+struct Resolved {
+    const Variant* v;
+    int tiles_m, tiles_n, R, lds;
+    long long grid, ws_bytes;
+};
+
+// Legality of a tile config for a shape; never launches anything.
+bool legal(const Shape& s, const ct_tile_config& c, Resolved* out, std::string* why) {
+    const auto& vs = variants();
+    auto no = [&](const char* m) {
+        if (why) *why = m;
+        return false;
+    };
+    if (c.variant < 0 || c.variant >= (int)vs.size()) return no("unknown variant");
+    const Variant& v = vs[c.variant];
+    if (!v.ig) return no("not a tiled variant");
+    if (v.desc.dtype != s.dtype) return no("variant dtype differs");
+    if (c.kc < 1 || c.stages < 1 || c.split_k < 1) return no("non-positive split factor");
+    if (c.kc > v.desc.kc_max) return no("kc above the variant's limit");
+    // every split must own at least one channel
+    const long long per_split = (long long)c.stages * c.kc;
+    if ((long long)(c.split_k - 1) * per_split >= s.CI) return no("an empty split");
+    if ((long long)c.split_k * per_split < s.CI) return no("splits do not cover CI");
+    if (v.desc.threads > kMaxThreads) return no("workgroup too large");
+    const int R = window_rows(s, v.desc.tile_n);
+    const long long Wp = (long long)s.W + 2 * s.pad;
+    if ((long long)c.kc * R * Wp > (1LL << 28)) return no("window too large");
+    const int lds = v.ig->lds_bytes(c.kc, R, (int)Wp, s.T);
+    if (lds > kMaxLds || lds <= 0) return no("LDS above 160 KiB");
+    const long long tiles_m = (s.CO + v.desc.tile_m - 1) / v.desc.tile_m;
+    const long long tiles_n = (s.P + v.desc.tile_n - 1) / v.desc.tile_n;
+    const long long grid = tiles_m * tiles_n * c.split_k;
+    if (tiles_m * tiles_n > (1LL << 30) || grid > 0x7fffffffLL) return no("grid too large");
+    const long long ws = c.split_k > 1 ? grid * v.desc.tile_m * v.desc.tile_n * 4LL : 0;
+    if (ws > kMaxWorkspace) return no("split workspace too large");
+    if (out) {
+        out->v = &v;
+        out->tiles_m = (int)tiles_m;
+        out->tiles_n = (int)tiles_n;
+        out->R = R;
+        out->lds = lds;
+        out->grid = grid;
+        out->ws_bytes = ws;
+    }
+    return true;
+}
+
+// Rough time model used to pick the default config and to order the search.
+double predict_us(const Shape& s, const ct_tile_config& c, const Resolved& r) {
+    const auto& d = r.v->desc;
+    const double clk = 2.4e9;
+    const int kpi = d.mfma_k;
+    const int ksp = round_up(c.kc * s.T, kpi);
+    const double wg_flops = 2.0 * d.tile_m * d.tile_n * (double)ksp * c.stages;
+    int occ = std::max(1, std::min(kMaxLds / std::max(r.lds, 1), 2048 / d.threads));
+    occ = std::min(occ, 4);
+    const double slots = (double)kNumCU * occ;
+    const double rounds = std::ceil((double)r.grid / slots);
+    // waves per SIMD decide how well MFMA latency is hidden
+    const double waves_per_simd = (double)d.threads / 64.0 * occ / 4.0;
+    const double eff = std::min(1.0, 0.35 + 0.25 * waves_per_simd) * (s.dtype == CT_F32 ? 1.0 : 0.7);
+    const double flop_per_clk_cu = s.dtype == CT_F32 ? 256.0 : 4096.0;
+    const double t_mma = rounds * occ * wg_flops / (flop_per_clk_cu * eff * clk);
+    const double elem = s.dtype == CT_F32 ? 4.0 : 2.0;
+    const double stage_bytes = (d.tile_m * (double)c.kc * s.T + (double)c.kc * r.R * (s.W + 2 * s.pad)) * elem;
+    const double t_load = rounds * occ * c.stages * (stage_bytes / (64.0 * clk) + 1.0e-6);
+    const double t_fix = c.split_k > 1 ? (1.5e-6 + c.split_k * d.tile_m * (double)d.tile_n * 4.0 / 100e9) : 0.0;
+    const double t_out = (double)s.P * s.CO * 4.0 / 5e12;
+    return 1e6 * (t_mma + t_load + t_fix + t_out) + 2.0;
+}
+
+// --------------------------------------------------------------- cache ----
+struct CacheEntry {
+    std::string variant_name;
+    ct_tile_config cfg;
+    std::string line;  // JSON record as written / read
+};
+
+std::mutex g_cache_mu;
+std::map<std::string, CacheEntry> g_cache;
+std::map<std::string, ct_tile_config> g_default_memo;
+
+std::string json_record(const Shape& s, const ct_tile_config& c, const char* vname,
+                        const float* costs, int ncost, double all_cost, double ts) {
+    std::ostringstream o;
+    o << "{\"key\":\"" << s.key() << "\",\"N\":" << s.N << ",\"CI\":" << s.CI << ",\"H\":" << s.H
+      << ",\"W\":" << s.W << ",\"CO\":" << s.CO << ",\"KH\":" << s.KH << ",\"KW\":" << s.KW
+      << ",\"stride\":" << s.stride << ",\"pad\":" << s.pad << ",\"dtype\":" << s.dtype
+      << ",\"epilogue\":" << s.epilogue << ",\"arch\":\"" << kArch << "\",\"variant\":\"" << vname
+      << "\",\"split_k\":" << c.split_k << ",\"stages\":" << c.stages << ",\"kc\":" << c.kc
+      << ",\"index\":" << c.index << ",\"us\":" << c.us << ",\"error_no\":" << c.error_no
+      << ",\"costs_us\":[";
+    for (int i = 0; i < ncost; ++i) o << (i ? "," : "") << costs[i];
+    o << "],\"all_cost\":" << all_cost << ",\"timestamp\":" << std::fixed << ts << "}";
+    return o.str();
+}
+
+// Minimal reader for the flat records written above: "name": value pairs
+// where a value is a string, a number or a list of numbers.
+bool parse_record(const std::string& line, std::map<std::string, std::string>* kv) {
+    size_t i = 0;
+    auto ws = [&] {
+        while (i < line.size() && isspace((unsigned char)line[i])) ++i;
+    };
+    ws();
+    if (i >= line.size() || line[i] != '{') return false;
+    ++i;
+    while (true) {
+        ws();
+        if (i < line.size() && line[i] == '}') return true;
+        if (i >= line.size() || line[i] != '"') return false;
+        size_t e = line.find('"', i + 1);
+        if (e == std::string::npos) return false;
+        std::string name = line.substr(i + 1, e - i - 1);
+        i = e + 1;
+        ws();
+        if (i >= line.size() || line[i] != ':') return false;
+        ++i;
+        ws();
+        if (i >= line.size()) return false;
+        std::string val;
+        if (line[i] == '"') {
+            size_t q = line.find('"', i + 1);
+            if (q == std::string::npos) return false;
+            val = line.substr(i + 1, q - i - 1);
+            i = q + 1;
+        } else if (line[i] == '[') {
+            size_t q = line.find(']', i);
+            if (q == std::string::npos) return false;
+            val = line.substr(i, q - i + 1);
+            i = q + 1;
+        } else {
+            size_t q = i;
+            while (q < line.size() && line[q] != ',' && line[q] != '}') ++q;
+            val = line.substr(i, q - i);
+            while (!val.empty() && isspace((unsigned char)val.back())) val.pop_back();
+            if (val.empty()) return false;
+            i = q;
+        }
+        (*kv)[name] = val;
+        ws();
+        if (i < line.size() && line[i] == ',') {
+            ++i;
+            continue;
+        }
+        if (i < line.size() && line[i] == '}') return true;
+        return false;
+    }
+}
+
+bool to_int(const std::string& s, long long* v) {
+    char* end = nullptr;
+    errno = 0;
+    long long r = strtoll(s.c_str(), &end, 10);
+    if (errno || end == s.c_str() || *end) return false;
+    *v = r;
+    return true;
+}
+
+// Insert a record if it parses, names a known variant, is legal for its shape
+// and is faster than what the cache holds for that key.
+bool cache_insert_line(const std::string& line) {
+    std::map<std::string, std::string> kv;
+    if (!parse_record(line, &kv)) return false;
+    const char* need[] = {"N", "CI", "H", "W", "CO", "KH", "KW", "stride", "pad", "dtype",
+                          "epilogue", "split_k", "stages", "kc", "error_no"};
+    long long v[15];
+    for (int i = 0; i < 15; ++i) {
+        auto it = kv.find(need[i]);
+        if (it == kv.end() || !to_int(it->second, &v[i])) return false;
+    }
+    if (kv["arch"] != kArch) return false;
+    if (v[14] != 0) return false;  // only successful measurements are kept
+    Shape s;
+    if (make_shape((int)v[0], (int)v[1], (int)v[2], (int)v[3], (int)v[4], (int)v[5], (int)v[6],
+                   (int)v[7], (int)v[8], (int)v[9], (int)v[10], &s) != CT_OK)
+        return false;
+    const int vid = find_variant(kv["variant"].c_str());
+    if (vid < 0) return false;
+    ct_tile_config c{};
+    c.variant = vid;
+    c.split_k = (int)v[11];
+    c.stages = (int)v[12];
+    c.kc = (int)v[13];
+    c.us = (float)atof(kv["us"].c_str());
+    c.error_no = 0;
+    if (!legal(s, c, nullptr, nullptr)) return false;
+    c.index = encode(space_of(s), c);
+    const std::string key = s.key();
+    auto it = g_cache.find(key);
+    if (it != g_cache.end() && it->second.cfg.us > 0 && it->second.cfg.us <= c.us) return true;
+    g_cache[key] = CacheEntry{kv["variant"], c, line};
+    return true;
+}
+
+// --------------------------------------------------------- workspaces -----
+struct Workspace {
+    float* ws = nullptr;
+    long long ws_bytes = 0;
+    unsigned* tickets = nullptr;
+    long long n_tickets = 0;
+};
+
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(hipStream_t stream, long long ws_bytes, long long n_tickets, Workspace* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.ws_bytes < ws_bytes || w.n_tickets < n_tickets) {
+        // in-flight launches on this stream may still use the old buffers
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    }
+    if (w.ws_bytes < ws_bytes) {
+        if (w.ws) (void)hipFree(w.ws);
+        w.ws = nullptr;
+        w.ws_bytes = 0;
+        const long long b = std::max<long long>(ws_bytes, 1 << 20);
+        e = hipMalloc((void**)&w.ws, (size_t)b);
+        if (e != hipSuccess) return fail(CT_ERR_NO_MEMORY, "split workspace of %lld bytes: %s", b,
+                                         hipGetErrorString(e));
+        w.ws_bytes = b;
+    }
+    if (w.n_tickets < n_tickets) {
+        if (w.tickets) (void)hipFree(w.tickets);
+        w.tickets = nullptr;
+        w.n_tickets = 0;
+        const long long n = std::max<long long>(n_tickets, 4096);
+        e = hipMalloc((void**)&w.tickets, (size_t)n * sizeof(unsigned));
+        if (e != hipSuccess) return fail(CT_ERR_NO_MEMORY, "ticket array: %s", hipGetErrorString(e));
+        // zero once; every launch leaves the counters it used at zero again
+        e = hipMemset(w.tickets, 0, (size_t)n * sizeof(unsigned));
+        if (e != hipSuccess) return hip_fail(e, "hipMemset");
+        e = hipDeviceSynchronize();
+        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        w.n_tickets = n;
+    }
+    *out = w;
+    return CT_OK;
+}
+
+// ------------------------------------------------------------- launches ---
+ConvParams base_params(const Shape& s, const void* x, const void* w, float* y, const float* bias,
+                       const float* var, float eps) {
+    ConvParams p{};
+    p.x = x; p.w = w; p.y = y; p.bias = bias; p.var = var; p.eps = eps;
+    p.N = s.N; p.CI = s.CI; p.H = s.H; p.W = s.W; p.CO = s.CO; p.KH = s.KH; p.KW = s.KW;
+    p.stride = s.stride; p.pad = s.pad; p.OH = s.OH; p.OW = s.OW;
+    p.T = s.T; p.K = s.K; p.P = s.P; p.OHW = s.OH * s.OW; p.epilogue = s.epilogue;
+    p.Hp = s.H + 2 * s.pad; p.Wp = s.W + 2 * s.pad;
+    return p;
+}
+
+int launch_direct(const Shape& s, const void* x, const void* w, float* y, const float* bias,
+                  const float* var, float eps, hipStream_t stream) {
+    ConvParams p = base_params(s, x, w, y, bias, var, eps);
+    if ((s.P * s.CO + 255) / 256 > 0x7fffffffLL)
+        return fail(CT_ERR_UNSUPPORTED, "output too large for the direct kernel");
+    hipError_t e = launch_conv_direct(p, s.dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "direct convolution launch");
+    return CT_OK;
+}
+
+int launch_tiled(const Shape& s, const ct_tile_config& c, const void* x, const void* w, float* y,
+                 const float* bias, const float* var, float eps, hipStream_t stream) {
+    Resolved r;
+    std::string why;
+    if (!legal(s, c, &r, &why))
+        return fail(CT_ERR_UNSUPPORTED, "tile config not legal for this shape: %s", why.c_str());
+    ConvParams p = base_params(s, x, w, y, bias, var, eps);
+    p.kc = c.kc;
+    p.stages = c.stages;
+    p.S = c.split_k;
+    p.tiles_m = r.tiles_m;
+    p.tiles_n = r.tiles_n;
+    p.R = r.R;
+    if (c.split_k > 1) {
+        Workspace ws;
+        int st = get_workspace(stream, r.ws_bytes, (long long)r.tiles_m * r.tiles_n, &ws);
+        if (st != CT_OK) return st;
+        p.ws = ws.ws;
+        p.tickets = ws.tickets;
+    }
+    hipError_t e = r.v->ig->launch(p, stream);
+    if (e != hipSuccess) return hip_fail(e, r.v->desc.name);
+    return CT_OK;
+}
+
+// Built-in default: the legal point with the smallest predicted time.
+bool default_config(const Shape& s, ct_tile_config* out) {
+    const std::string key = s.key();
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        auto it = g_default_memo.find(key);
+        if (it != g_default_memo.end()) {
+            *out = it->second;
+            return out->variant >= 0;
+        }
+    }
+    Space sp = space_of(s);
+    double best = 1e300;
+    ct_tile_config bc{};
+    bc.variant = -1;
+    for (long long i = 0; i < sp.size(); ++i) {
+        ct_tile_config c;
+        decode(sp, i, &c);
+        Resolved r;
+        if (!legal(s, c, &r, nullptr)) continue;
+        const double t = predict_us(s, c, r);
+        if (t < best) {
+            best = t;
+            bc = c;
+        }
+    }
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    g_default_memo[key] = bc;
+    *out = bc;
+    return bc.variant >= 0;
+}
+
+// The config fwd uses: cached winner, else default; variant -1 = direct.
+ct_tile_config choose(const Shape& s, int* from_cache) {
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        auto it = g_cache.find(s.key());
+        if (it != g_cache.end()) {
+            if (from_cache) *from_cache = 1;
+            return it->second.cfg;
+        }
+    }
+    if (from_cache) *from_cache = 0;
+    ct_tile_config c{};
+    if (!default_config(s, &c)) {
+        c.variant = (int)s.dtype;  // the direct kernel of this dtype
+        c.split_k = c.stages = c.kc = 1;
+        c.index = -1;
+    }
+    return c;
+}
+
+double now_s() {
+    return std::chrono::duration<double>(std::chrono::system_clock::now().time_since_epoch())
+        .count();
+}
+
+}  // namespace
+}  // namespace ct
+
+using namespace ct;
+
+// ===================================================================== ABI ==
+extern "C" {
+
+int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y, int N, int CI, int H, int W, int CO,
+                       int KH, int KW, int stride, int pad, int dtype, int epilogue,
+                       const float* bias, const float* var, float eps, void* stream) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    st = check_pointers(x, w, y, epilogue, bias, var);
+    if (st != CT_OK) return st;
+    ct_tile_config c = choose(s, nullptr);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (!variants()[c.variant].ig) return launch_direct(s, x, w, y, bias, var, eps, hs);
+    return launch_tiled(s, c, x, w, y, bias, var, eps, hs);
+}
+
+int ct_conv2d_nchw_fwd_config(const void* x, const void* w, float* y, int N, int CI, int H, int W,
+                              int CO, int KH, int KW, int stride, int pad, int dtype, int epilogue,
+                              const float* bias, const float* var, float eps,
+                              const ct_tile_config* cfg, void* stream) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    st = check_pointers(x, w, y, epilogue, bias, var);
+    if (st != CT_OK) return st;
+    if (!cfg) return fail(CT_ERR_INVALID_ARG, "cfg must not be NULL");
+    if (cfg->variant < 0 || cfg->variant >= (int)variants().size())
+        return fail(CT_ERR_INVALID_ARG, "unknown variant %d", cfg->variant);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const Variant& v = variants()[cfg->variant];
+    if (!v.ig) {
+        if (v.desc.dtype != dtype) return fail(CT_ERR_UNSUPPORTED, "direct variant dtype differs");
+        return launch_direct(s, x, w, y, bias, var, eps, hs);
+    }
+    return launch_tiled(s, *cfg, x, w, y, bias, var, eps, hs);
+}
+
+int ct_conv2d_nchw_direct(const void* x, const void* w, float* y, int N, int CI, int H, int W,
+                          int CO, int KH, int KW, int stride, int pad, int dtype, int epilogue,
+                          const float* bias, const float* var, float eps, void* stream) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    st = check_pointers(x, w, y, epilogue, bias, var);
+    if (st != CT_OK) return st;
+    return launch_direct(s, x, w, y, bias, var, eps, static_cast<hipStream_t>(stream));
+}
+
+long long ct_conv2d_space_size(int N, int CI, int H, int W, int CO, int KH, int KW, int stride,
+                               int pad, int dtype, int epilogue) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    return space_of(s).size();
+}
+
+int ct_conv2d_space_entity(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad,
+                           int dtype, int epilogue, long long index, ct_tile_config* cfg_out,
+                           int* is_legal) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    if (!cfg_out) return fail(CT_ERR_INVALID_ARG, "cfg_out must not be NULL");
+    Space sp = space_of(s);
+    if (!decode(sp, index, cfg_out)) return fail(CT_ERR_INVALID_ARG, "index outside the space");
+    if (is_legal) *is_legal = legal(s, *cfg_out, nullptr, nullptr) ? 1 : 0;
+    return CT_OK;
+}
+
+int ct_conv2d_query(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad,
+                    int dtype, int epilogue, ct_tile_config* cfg_out, int* from_cache) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    if (!cfg_out) return fail(CT_ERR_INVALID_ARG, "cfg_out must not be NULL");
+    int fc = 0;
+    *cfg_out = choose(s, &fc);
+    if (from_cache) *from_cache = fc;
+    return CT_OK;
+}
+
+int ct_variant_count(void) { return (int)variants().size(); }
+
+int ct_variant_info(int variant, ct_variant_desc* out) {
+    if (!out) return fail(CT_ERR_INVALID_ARG, "out must not be NULL");
+    if (variant < 0 || variant >= (int)variants().size())
+        return fail(CT_ERR_INVALID_ARG, "unknown variant %d", variant);
+    *out = variants()[variant].desc;
+    return CT_OK;
+}
+
+long long ct_split_count(long long n, int k) {
+    if (n <= 0 || k < 1 || k > 8) return fail(CT_ERR_INVALID_ARG, "need n > 0 and 1 <= k <= 8");
+    if (n > (1LL << 40)) return fail(CT_ERR_INVALID_ARG, "n too large");
+    return (long long)splits(n, k).size();
+}
+
+int ct_split_entity(long long n, int k, long long i, long long* out) {
+    if (!out) return fail(CT_ERR_INVALID_ARG, "out must not be NULL");
+    long long cnt = ct_split_count(n, k);
+    if (cnt < 0) return (int)cnt;
+    if (i < 0 || i >= cnt) return fail(CT_ERR_INVALID_ARG, "index outside the split");
+    const auto& e = splits(n, k)[i];
+    for (int j = 0; j < k; ++j) out[j] = e[j];
+    return CT_OK;
+}
+
+int ct_broadcast_nchw(const float* var, void* out, int N, int C, int H, int W, int out_dtype, int op,
+                      int mode, void* stream) {
+    if (!var || !out) return fail(CT_ERR_INVALID_ARG, "var and out must not be NULL");
+    if (N <= 0 || C <= 0 || H <= 0 || W <= 0)
+        return fail(CT_ERR_INVALID_ARG, "every dimension must be positive");
+    if (out_dtype != CT_F32 && out_dtype != CT_F16)
+        return fail(CT_ERR_INVALID_ARG, "out_dtype must be CT_F32 or CT_F16");
+    if (op != CT_BC_EXP) return fail(CT_ERR_INVALID_ARG, "unknown op %d", op);
+    if (mode != CT_BC_AUTO && mode != CT_BC_CHANNEL && mode != CT_BC_FLAT)
+        return fail(CT_ERR_INVALID_ARG, "unknown mode %d", mode);
+    const long long HW = (long long)H * W;
+    if (HW > (1LL << 30) || (long long)N * C * HW > (1LL << 46))
+        return fail(CT_ERR_INVALID_ARG, "output too large");
+    // channel-bound applies to static H*W that is a multiple of 32, with
+    // 16-byte aligned rows (the PR's Init checks, as read here)
+    const bool aligned = (reinterpret_cast<uintptr_t>(out) % 16) == 0;
+    const bool channel_ok = (HW % 32 == 0) && aligned && N <= 0x7fffffff / 1;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (mode == CT_BC_CHANNEL && !channel_ok)
+        return fail(CT_ERR_UNSUPPORTED, "channel-bound broadcast needs H*W %% 32 == 0 and 16-byte "
+                                        "aligned output");
+    if (mode == CT_BC_FLAT || !channel_ok)
+        e = launch_bcast_flat(var, out, N, C, (int)HW, out_dtype, hs);
+    else
+        e = launch_bcast_channel(var, out, N, C, (int)HW, out_dtype, hs);
+    if (e != hipSuccess) return hip_fail(e, "broadcast launch");
+    return CT_OK;
+}
+
+int ct_cache_load(const char* path) {
+    if (!path) return fail(CT_ERR_INVALID_ARG, "path must not be NULL");
+    std::ifstream f(path);
+    if (!f) return fail(CT_ERR_IO, "cannot open %s", path);
+    std::string line;
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    while (std::getline(f, line)) {
+        if (line.empty()) continue;
+        (void)cache_insert_line(line);  // unparsable or stale lines are skipped
+    }
+    return CT_OK;
+}
+
+int ct_cache_save(const char* path) {
+    if (!path) return fail(CT_ERR_INVALID_ARG, "path must not be NULL");
+    std::ofstream f(path, std::ios::app);
+    if (!f) return fail(CT_ERR_IO, "cannot open %s", path);
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    for (const auto& kv : g_cache) f << kv.second.line << "\n";
+    f.flush();
+    if (!f) return fail(CT_ERR_IO, "write to %s failed", path);
+    return CT_OK;
+}
+
+int ct_cache_clear(void) {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    g_cache.clear();
+    return CT_OK;
+}
+
+int ct_cache_size(void) {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    return (int)g_cache.size();
+}
+
+int ct_release(void) {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    int st = CT_OK;
+    for (auto& kv : g_ws) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess) st = CT_ERR_HIP;
+        (void)hipSetDevice(kv.first.first);
+        (void)hipStreamSynchronize(kv.first.second);
+        if (kv.second.ws) (void)hipFree(kv.second.ws);
+        if (kv.second.tickets) (void)hipFree(kv.second.tickets);
+        (void)hipSetDevice(dev);
+    }
+    g_ws.clear();
+    return st;
+}
+
+const char* ct_status_string(int status) {
+    switch (status) {
+        case CT_OK: return "ok";
+        case CT_ERR_INVALID_ARG: return "invalid argument";
+        case CT_ERR_UNSUPPORTED: return "unsupported";
+        case CT_ERR_HIP: return "HIP error";
+        case CT_ERR_NO_MEMORY: return "out of device memory";
+        case CT_ERR_IO: return "I/O error";
+        case CT_ERR_TUNE_FAILED: return "tuning failed";
+        default: return "unknown status";
+    }
+}
+
+const char* ct_last_error(void) { return g_last_error; }
+
+const char* ct_version(void) { return "convtile 0.1 gfx950"; }
+
+}  // extern "C"
+
+// ================================================================ tuner ==
+namespace ct {
+namespace {
+
+struct Scratch {
+    void* x = nullptr;
+    void* w = nullptr;
+    float* y = nullptr;
+    float* y_ref = nullptr;
+    float* bias = nullptr;
+    float* var = nullptr;
+    unsigned* bad = nullptr;
+    ~Scratch() {
+        for (void* p : {x, w, (void*)y, (void*)y_ref, (void*)bias, (void*)var, (void*)bad})
+            if (p) (void)hipFree(p);
+    }
+};
+
+// "index:error_no,index:error_no" -- a host-side hook that makes the search
+// record the given outcome for a candidate instead of running it.
+std::map<long long, int> injected_errors() {
+    std::map<long long, int> m;
+    const char* s = getenv("CT_TUNE_INJECT");
+    if (!s) return m;
+    std::string str(s);
+    std::stringstream ss(str);
+    std::string item;
+    while (std::getline(ss, item, ',')) {
+        size_t c = item.find(':');
+        if (c == std::string::npos) continue;
+        m[atoll(item.substr(0, c).c_str())] = atoi(item.substr(c + 1).c_str());
+    }
+    return m;
+}
+
+}  // namespace
+
+int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad, int dtype,
+              int epilogue, int max_trials, float min_repeat_ms, void* stream,
+              ct_tile_config* best_out, ct_tune_record* records, int max_records, int* n_records) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    if (!best_out) return fail(CT_ERR_INVALID_ARG, "best_out must not be NULL");
+    if (max_trials < 0) return fail(CT_ERR_INVALID_ARG, "max_trials must be >= 0");
+    if (!(min_repeat_ms >= 0.0f)) return fail(CT_ERR_INVALID_ARG, "min_repeat_ms must be >= 0");
+    if (max_records < 0 || (max_records > 0 && !records))
+        return fail(CT_ERR_INVALID_ARG, "records / max_records mismatch");
+    if (n_records) *n_records = 0;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const double kTimeout = 4.0;  // seconds per trial
+    const int kRepeat = 3;
+
+    // search order: legal points by predicted time, then illegal points
+    Space sp = space_of(s);
+    std::vector<std::pair<double, long long>> order;
+    std::vector<long long> illegal;
+    for (long long i = 0; i < sp.size(); ++i) {
+        ct_tile_config c;
+        decode(sp, i, &c);
+        Resolved r;
+        if (legal(s, c, &r, nullptr))
+            order.push_back({predict_us(s, c, r), i});
+        else
+            illegal.push_back(i);
+    }
+    std::stable_sort(order.begin(), order.end());
+    std::vector<long long> trials;
+    for (auto& o : order) trials.push_back(o.second);
+    for (long long i : illegal) trials.push_back(i);
+    if (max_trials > 0 && (long long)trials.size() > max_trials) trials.resize(max_trials);
+
+    // scratch inputs, filled on the device
+    Scratch sc;
+    const size_t esz = dtype == CT_F32 ? 4 : 2;
+    const long long nx = (long long)N * CI * H * W, nw = (long long)CO * s.K;
+    const long long ny = s.P * CO;
+    hipError_t e;
+    if ((e = hipMalloc(&sc.x, nx * esz)) != hipSuccess ||
+        (e = hipMalloc(&sc.w, nw * esz)) != hipSuccess ||
+        (e = hipMalloc((void**)&sc.y, ny * 4)) != hipSuccess ||
+        (e = hipMalloc((void**)&sc.y_ref, ny * 4)) != hipSuccess ||
+        (e = hipMalloc((void**)&sc.bias, CO * 4)) != hipSuccess ||
+        (e = hipMalloc((void**)&sc.var, CO * 4)) != hipSuccess ||
+        (e = hipMalloc((void**)&sc.bad, 4)) != hipSuccess)
+        return fail(CT_ERR_NO_MEMORY, "tuning scratch: %s", hipGetErrorString(e));
+    const float wa = std::sqrt(6.0f / (float)s.K);
+    if ((e = launch_fill_uniform(sc.x, nx, dtype, -1.0f, 1.0f, 11u, hs)) != hipSuccess ||
+        (e = launch_fill_uniform(sc.w, nw, dtype, -wa, wa, 12u, hs)) != hipSuccess ||
+        (e = launch_fill_uniform(sc.bias, CO, CT_F32, -0.2f, 0.2f, 13u, hs)) != hipSuccess ||
+        (e = launch_fill_uniform(sc.var, CO, CT_F32, 0.5f, 2.0f, 14u, hs)) != hipSuccess)
+        return hip_fail(e, "tuning scratch fill");
+    const float eps = 1e-5f;
+    st = launch_direct(s, sc.x, sc.w, sc.y_ref, sc.bias, sc.var, eps, hs);
+    if (st != CT_OK) return st;
+    if ((e = hipStreamSynchronize(hs)) != hipSuccess) return hip_fail(e, "reference run");
+    // expected sum |x w| is about K * E|x| * E|w| = K * wa / 4; allow 1e-4 of twice that
+    const float atol = 1e-4f * (float)s.K * wa * 0.5f;
+    const float rtol = epilogue == CT_EPI_EXP_BIAS_RSQRT ? atol + 1e-5f : 1e-5f;
+
+    hipEvent_t ev0, ev1;
+    if ((e = hipEventCreate(&ev0)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+    if ((e = hipEventCreate(&ev1)) != hipSuccess) {
+        (void)hipEventDestroy(ev0);
+        return hip_fail(e, "hipEventCreate");
+    }
+    const auto inject = injected_errors();
+    ct_tile_config best{};
+    best.variant = -1;
+    double best_mean = 1e300;
+    int nrec = 0;
+    for (long long idx : trials) {
+        const auto t_start = std::chrono::steady_clock::now();
+        ct_tile_config c;
+        decode(sp, idx, &c);
+        ct_tune_record rec{};
+        int err = CT_TRIAL_OK;
+        auto inj = inject.find(idx);
+        Resolved r;
+        if (inj != inject.end()) {
+            err = inj->second;
+        } else if (!legal(s, c, &r, nullptr)) {
+            err = CT_TRIAL_ILLEGAL;
+        } else {
+            // poison the output so a kernel that writes nothing cannot pass
+            e = hipMemsetAsync(sc.y, 0xff, ny * 4, hs);
+            st = (e == hipSuccess) ? launch_tiled(s, c, sc.x, sc.w, sc.y, sc.bias, sc.var, eps, hs)
+                                   : CT_ERR_HIP;
+            if (st == CT_OK && (e = hipStreamSynchronize(hs)) != hipSuccess) st = CT_ERR_HIP;
+            if (st == CT_OK) {
+                unsigned bad = 0;
+                if (hipMemsetAsync(sc.bad, 0, 4, hs) != hipSuccess ||
+                    launch_compare(sc.y, sc.y_ref, ny, atol, rtol, sc.bad, hs) != hipSuccess ||
+                    hipMemcpyAsync(&bad, sc.bad, 4, hipMemcpyDeviceToHost, hs) != hipSuccess ||
+                    hipStreamSynchronize(hs) != hipSuccess || bad != 0)
+                    st = CT_ERR_TUNE_FAILED;
+            }
+            if (st != CT_OK) {
+                err = CT_TRIAL_RUNTIME;
+            } else {
+                // calibrate the launch count so a repeat lasts >= min_repeat_ms
+                long long number = 1;
+                float ms = 0.0f;
+                while (true) {
+                    (void)hipEventRecord(ev0, hs);
+                    for (long long i = 0; i < number && st == CT_OK; ++i)
+                        st = launch_tiled(s, c, sc.x, sc.w, sc.y, sc.bias, sc.var, eps, hs);
+                    (void)hipEventRecord(ev1, hs);
+                    if (st != CT_OK || hipEventSynchronize(ev1) != hipSuccess) {
+                        err = CT_TRIAL_RUNTIME;
+                        break;
+                    }
+                    (void)hipEventElapsedTime(&ms, ev0, ev1);
+                    const double wall = std::chrono::duration<double>(
+                                            std::chrono::steady_clock::now() - t_start).count();
+                    if (wall > kTimeout) {
+                        err = CT_TRIAL_TIMEOUT;
+                        break;
+                    }
+                    if (ms >= min_repeat_ms || number >= (1LL << 20)) break;
+                    const double want = ms > 0.0f ? 1.25 * min_repeat_ms / ms * number : 2.0 * number;
+                    number = std::max<long long>(2 * number, (long long)std::ceil(want));
+                    number = std::min<long long>(number, 1LL << 20);
+                }
+                for (int rep = 0; rep < kRepeat && err == CT_TRIAL_OK; ++rep) {
+                    (void)hipEventRecord(ev0, hs);
+                    for (long long i = 0; i < number && st == CT_OK; ++i)
+                        st = launch_tiled(s, c, sc.x, sc.w, sc.y, sc.bias, sc.var, eps, hs);
+                    (void)hipEventRecord(ev1, hs);
+                    if (st != CT_OK || hipEventSynchronize(ev1) != hipSuccess) {
+                        err = CT_TRIAL_RUNTIME;
+                        break;
+                    }
+                    (void)hipEventElapsedTime(&ms, ev0, ev1);
+                    rec.costs_us[rep] = 1000.0f * ms / (float)number;
+                    rec.n_costs = rep + 1;
+                    const double wall = std::chrono::duration<double>(
+                                            std::chrono::steady_clock::now() - t_start).count();
+                    if (wall > kTimeout) err = CT_TRIAL_TIMEOUT;
+                }
+            }
+        }
+        rec.error_no = err;
+        rec.all_cost_s =
+            std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+        rec.timestamp = now_s();
+        c.error_no = err;
+        if (err == CT_TRIAL_OK && rec.n_costs == kRepeat) {
+            double mean = 0;
+            for (int i = 0; i < kRepeat; ++i) mean += rec.costs_us[i];
+            mean /= kRepeat;
+            c.us = (float)mean;
+            if (mean < best_mean || (mean == best_mean && idx < best.index)) {
+                best_mean = mean;
+                best = c;
+            }
+        }
+        rec.cfg = c;
+        if (nrec < max_records) records[nrec] = rec;
+        ++nrec;
+        if (log_debug())
+            fprintf(stderr, "[convtile tune] No: %d index %lld %s S=%d stages=%d kc=%d  %.3f us  "
+                            "error_no=%d all_cost=%.3fs\n",
+                    nrec, idx, variants()[c.variant].desc.name, c.split_k, c.stages, c.kc,
+                    (double)c.us, err, rec.all_cost_s);
+    }
+    (void)hipEventDestroy(ev0);
+    (void)hipEventDestroy(ev1);
+    if (n_records) *n_records = std::min(nrec, max_records);
+    if (best.variant < 0) return fail(CT_ERR_TUNE_FAILED, "no candidate ran correctly");
+    *best_out = best;
+    // record the winner: in memory, and in the file named by CT_CACHE_PATH
+    float costs[1] = {best.us};
+    const std::string line = json_record(s, best, variants()[best.variant].desc.name, costs, 1,
+                                         0.0, now_s());
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        g_cache[s.key()] = CacheEntry{variants()[best.variant].desc.name, best, line};
+    }
+    const char* path = getenv("CT_CACHE_PATH");
+    if (path && *path) {
+        std::ofstream f(path, std::ios::app);
+        if (!f) return fail(CT_ERR_IO, "cannot append to %s", path);
+        f << line << "\n";
+    }
+    return CT_OK;
+}
+
+}  // namespace ct
+
+extern "C" int ct_conv2d_tune(int N, int CI, int H, int W, int CO, int KH, int KW, int stride,
+                              int pad, int dtype, int epilogue, int max_trials, float min_repeat_ms,
+                              void* stream, ct_tile_config* best_out, ct_tune_record* records,
+                              int max_records, int* n_records) {
+    return ct::tune_impl(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials,
+                         min_repeat_ms, stream, best_out, records, max_records, n_records);
+}

@@ -1,0 +1,194 @@
+"""Host-side checks that need no GPU: the C-ABI library loads and exports what
+include/convtile.h declares, argument checking, the tile-config space (against
+the oracle's plain enumerator and the gist's printed space), the legality
+check, the default config, and the JSON-lines cache."""
+import json
+import os
+import re
+
+import pytest
+
+from oracle import oracle as O
+from tensor_compiler_tiling_amd import convtile as ct
+from tensor_compiler_tiling_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(ct.LIB_PATH):
+        from tensor_compiler_tiling_amd import build
+        build.build()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "convtile.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ct_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ct.library()
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(ct.exported_names()) == names
+    assert "gfx950" in ct.ct_version()
+
+
+def test_status_strings():
+    assert ct.ct_status_string(0) == "ok"
+    assert ct.ct_status_string(ct.CT_ERR_INVALID_ARG) == "invalid argument"
+
+
+# ------------------------------------------------------------ argument checks
+BAD_SHAPES = [
+    dict(N=0), dict(CI=0), dict(H=-1), dict(CO=0), dict(KH=0), dict(stride=0), dict(pad=-1),
+    dict(H=2, W=2, KH=5, KW=5, pad=0), dict(dtype=7), dict(epilogue=9),
+]
+
+
+@pytest.mark.parametrize("bad", BAD_SHAPES)
+def test_invalid_shapes_rejected_before_any_hip_call(bad):
+    a = dict(N=1, CI=4, H=8, W=8, CO=4, KH=3, KW=3, stride=1, pad=1, dtype=0, epilogue=0)
+    a.update(bad)
+    args = [a[k] for k in ("N", "CI", "H", "W", "CO", "KH", "KW", "stride", "pad", "dtype",
+                           "epilogue")]
+    # fake non-null pointers: the call must fail on the shape before touching them
+    st = ct.library().ct_conv2d_nchw_fwd(16, 16, 16, *args, 16, 16, 1e-5, None)
+    assert st == ct.CT_ERR_INVALID_ARG
+    assert ct.ct_last_error()
+    assert ct.ct_conv2d_space_size(*args) == ct.CT_ERR_INVALID_ARG
+
+
+def test_null_pointers_rejected():
+    lib = ct.library()
+    shape = (1, 4, 8, 8, 4, 3, 3, 1, 1, 0)
+    assert lib.ct_conv2d_nchw_fwd(None, 16, 16, *shape, 0, None, None, 1e-5, None) == -1
+    assert lib.ct_conv2d_nchw_fwd(16, 16, None, *shape, 0, None, None, 1e-5, None) == -1
+    # the epilogue reads bias / var
+    assert lib.ct_conv2d_nchw_fwd(16, 16, 16, *shape, 1, None, None, 1e-5, None) == -1
+    assert lib.ct_conv2d_nchw_fwd(16, 16, 16, *shape, 2, 16, None, 1e-5, None) == -1
+    assert lib.ct_broadcast_nchw(None, 16, 1, 4, 8, 8, 0, 0, 0, None) == -1
+    assert lib.ct_broadcast_nchw(16, 16, 1, 4, 8, 8, 5, 0, 0, None) == -1
+    assert lib.ct_broadcast_nchw(16, 16, 1, 4, 8, 8, 0, 3, 0, None) == -1
+    assert lib.ct_broadcast_nchw(16, 16, 1, 4, 8, 8, 0, 0, 9, None) == -1
+
+
+# ------------------------------------------------------------ split enumerator
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 12, 49, 64, 96, 128, 256, 360, 512])
+@pytest.mark.parametrize("k", [1, 2, 3, 4])
+def test_split_enumerator_matches_oracle(n, k):
+    want = O.ordered_factorizations(n, k)
+    assert ct.ct_split_count(n, k) == len(want)
+    for i, f in enumerate(want):
+        st, got = ct.ct_split_entity(n, k, i)
+        assert st == 0 and got == f
+
+
+def test_split_counts_of_the_gist_space():
+    # ConfigSpace lens printed for the 1x512x7x7 -> 512 3x3 workload
+    assert [ct.ct_split_count(512, 4), ct.ct_split_count(7, 4), ct.ct_split_count(512, 3),
+            ct.ct_split_count(3, 3)] == [220, 4, 55, 3]
+    assert ct.ct_split_count(0, 3) < 0 and ct.ct_split_count(8, 9) < 0
+
+
+# ------------------------------------------------------------ tile-config space
+def _dt(w):
+    return {wl.F32: ct.CT_F32, wl.F16: ct.CT_F16, wl.BF16: ct.CT_BF16}[w.dtype]
+
+
+def _args(w):
+    return w.shape_args() + (_dt(w), w.epilogue)
+
+
+@pytest.mark.parametrize("name", list(wl.CONV_WORKLOADS))
+def test_space_is_split_times_variants(name):
+    w = wl.CONV_WORKLOADS[name]
+    n_var = sum(1 for v in ct.variants() if v["kind"] == 1 and v["dtype"] == _dt(w))
+    size = ct.ct_conv2d_space_size(*_args(w))
+    assert size == len(O.ordered_factorizations(w.CI, 3)) * n_var
+    splits = O.ordered_factorizations(w.CI, 3)
+    seen_legal = 0
+    for idx in range(size):
+        st, cfg, legal = ct.ct_conv2d_space_entity(*_args(w), idx)
+        assert st == 0 and cfg.index == idx
+        # mixed radix, first knob (tile_ci) least significant
+        assert [cfg.split_k, cfg.stages, cfg.kc] == splits[idx % len(splits)]
+        seen_legal += legal
+    if n_var:
+        assert seen_legal > 0, "no legal tile config"
+    st, _, _ = ct.ct_conv2d_space_entity(*_args(w), size)
+    assert st == ct.CT_ERR_INVALID_ARG
+
+
+def test_legality_rejects_oversized_stage():
+    w = wl.CONV_WORKLOADS["resnet_final_c512_7x7_k3"]
+    by_name = {v["name"]: v for v in ct.variants()}
+    big = by_name["f32_m128n128_w2x2x1_r2x2"]
+    size = ct.ct_conv2d_space_size(*_args(w))
+    for idx in range(size):
+        st, cfg, legal = ct.ct_conv2d_space_entity(*_args(w), idx)
+        if cfg.variant == big["id"] and cfg.kc == 64:
+            # a 128-row W tile of 64 channels x 9 taps alone is 295 KB
+            assert legal == 0
+        if cfg.kc > 64:
+            assert legal == 0
+
+
+def test_query_default_without_gpu():
+    ct.ct_cache_clear()
+    for w in wl.CONV_WORKLOADS.values():
+        st, cfg, from_cache = ct.ct_conv2d_query(*_args(w))
+        assert st == 0 and from_cache == 0
+        info = ct.variants()[cfg.variant]
+        assert info["dtype"] == _dt(w)
+        if info["kind"] == 1:
+            st2, cfg2, legal = ct.ct_conv2d_space_entity(*_args(w), cfg.index)
+            assert legal == 1 and cfg2.variant == cfg.variant
+
+
+# ------------------------------------------------------------ cache file
+def test_cache_roundtrip_and_corrupt_lines(tmp_path):
+    w = wl.CONV_WORKLOADS["resnet_final_c512_7x7_k3"]
+    size = ct.ct_conv2d_space_size(*_args(w))
+    legal_idx = [i for i in range(size) if ct.ct_conv2d_space_entity(*_args(w), i)[2]]
+    st, cfg, _ = ct.ct_conv2d_space_entity(*_args(w), legal_idx[3])
+    vname = ct.variants()[cfg.variant]["name"]
+    rec = {"key": "x", "N": 1, "CI": 512, "H": 7, "W": 7, "CO": 512, "KH": 3, "KW": 3,
+           "stride": 1, "pad": 1, "dtype": 0, "epilogue": 0, "arch": "gfx950", "variant": vname,
+           "split_k": cfg.split_k, "stages": cfg.stages, "kc": cfg.kc, "index": 0, "us": 4.25,
+           "error_no": 0, "costs_us": [4.2, 4.3, 4.25], "all_cost": 0.5, "timestamp": 1.0}
+    p = tmp_path / "cache.jsonl"
+    bad_variant = dict(rec, variant="no_such_kernel")
+    failed = dict(rec, error_no=4)
+    p.write_text("not json\n" + json.dumps(bad_variant) + "\n{\"N\": 1,\n" +
+                 json.dumps(failed) + "\n" + json.dumps(rec) + "\n")
+    ct.ct_cache_clear()
+    assert ct.ct_cache_load(str(p)) == 0
+    assert ct.ct_cache_size() == 1
+    st, got, from_cache = ct.ct_conv2d_query(*_args(w))
+    assert st == 0 and from_cache == 1
+    assert (got.variant, got.split_k, got.stages, got.kc) == (cfg.variant, cfg.split_k,
+                                                              cfg.stages, cfg.kc)
+    assert got.index == legal_idx[3]
+    assert abs(got.us - 4.25) < 1e-6
+    # save appends; loading the saved file reproduces the same entry
+    p2 = tmp_path / "saved.jsonl"
+    assert ct.ct_cache_save(str(p2)) == 0
+    ct.ct_cache_clear()
+    assert ct.ct_cache_size() == 0
+    assert ct.ct_cache_load(str(p2)) == 0
+    st, got2, fc = ct.ct_conv2d_query(*_args(w))
+    assert fc == 1 and got2.index == got.index
+    ct.ct_cache_clear()
+    assert ct.ct_cache_load(str(tmp_path / "missing.jsonl")) == ct.CT_ERR_IO
+
+
+def test_workload_shapes():
+    ohs = [w.OH for w in wl.CONV_WORKLOADS.values()]
+    assert ohs == [14, 7, 112, 56, 28, 14, 7, 14, 14, 32]
+    assert wl.CONV_WORKLOADS[wl.HEADLINE].flops == 231211008
+    assert wl.CONV_WORKLOADS["f16_n128_c128to256_32x32_k3_epi"].flops == 77309411328
