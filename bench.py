@@ -113,10 +113,18 @@ def main():
     ct.check(st, "query")
     vdesc = ct.variants()[cfg.variant]
 
-    stream = torch.cuda.current_stream()
+    # one side stream for warm-up, capture and replay (the library keys its
+    # split workspace by stream, so warm-up on this stream allocates it)
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    xp, kp, yp, bp, vp = x.data_ptr(), k.data_ptr(), y.data_ptr(), b.data_ptr(), v.data_ptr()
+    lib = ct.library()
 
     def step():
-        st = ct.ct_conv2d_nchw_fwd(x, k, y, *args, b, v, 1e-5, stream.cuda_stream)
+        # the stream current at call time: inside graph capture it is the
+        # capture stream
+        st = lib.ct_conv2d_nchw_fwd(xp, kp, yp, *args, bp, vp, 1e-5,
+                                    torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise ct.ConvTileError(st, "fwd")
 
@@ -127,7 +135,7 @@ def main():
     graph = None
     if not a.eager:
         graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
+        with torch.cuda.graph(graph, stream=stream):
             for _ in range(a.steps):
                 step()
         torch.cuda.synchronize()

@@ -107,9 +107,11 @@ hipError_t launch_bcast_channel(const float* var, void* out, int N, int C, int H
     if ((swap ? C : row_blocks) > 65535) return hipErrorInvalidValue;
     dim3 grid = swap ? dim3(row_blocks, C) : dim3(C, row_blocks);
     if (out_dtype == DT_F16) {
+        (void)hipGetLastError();
         hipLaunchKernelGGL(bcast_channel_kernel<DT_F16>, grid, dim3(kBcastThreads), 0, stream, var,
                            static_cast<_Float16*>(out), N, C, HW, rows, swap);
     } else if (out_dtype == DT_F32) {
+        (void)hipGetLastError();
         hipLaunchKernelGGL(bcast_channel_kernel<DT_F32>, grid, dim3(kBcastThreads), 0, stream, var,
                            static_cast<float*>(out), N, C, HW, rows, swap);
     } else {
@@ -127,9 +129,11 @@ hipError_t launch_bcast_flat(const float* var, void* out, int N, int C, int HW, 
     if (blocks < 1) blocks = 1;
     const int vec_ok = (reinterpret_cast<uintptr_t>(out) % 16) == 0 ? 1 : 0;
     if (out_dtype == DT_F16) {
+        (void)hipGetLastError();
         hipLaunchKernelGGL(bcast_flat_kernel<DT_F16>, dim3((unsigned)blocks), dim3(kBcastThreads),
                            0, stream, var, static_cast<_Float16*>(out), total, C, HW, vec_ok);
     } else if (out_dtype == DT_F32) {
+        (void)hipGetLastError();
         hipLaunchKernelGGL(bcast_flat_kernel<DT_F32>, dim3((unsigned)blocks), dim3(kBcastThreads),
                            0, stream, var, static_cast<float*>(out), total, C, HW, vec_ok);
     } else {

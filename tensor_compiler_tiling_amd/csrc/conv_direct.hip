@@ -56,14 +56,17 @@ hipError_t launch_conv_direct(const ConvParams& p, int dtype, hipStream_t stream
     if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
     switch (dtype) {
         case DT_F32:
+            (void)hipGetLastError();
             hipLaunchKernelGGL(conv_direct_kernel<DT_F32>, dim3((unsigned)grid), dim3(block), 0,
                                stream, p);
             break;
         case DT_F16:
+            (void)hipGetLastError();
             hipLaunchKernelGGL(conv_direct_kernel<DT_F16>, dim3((unsigned)grid), dim3(block), 0,
                                stream, p);
             break;
         case DT_BF16:
+            (void)hipGetLastError();
             hipLaunchKernelGGL(conv_direct_kernel<DT_BF16>, dim3((unsigned)grid), dim3(block), 0,
                                stream, p);
             break;

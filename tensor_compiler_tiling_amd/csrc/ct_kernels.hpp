@@ -7,6 +7,26 @@
 
 namespace ct {
 
+// Division by a runtime constant d (1 <= d < 2^31) with a multiply-high and a
+// shift (Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): q = (umulhi(n, mul) + n) >> shift, exact for every
+// 32-bit n.
+struct FastDiv {
+    uint32_t d, mul, shift;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    const uint64_t m = ((1ull << 32) * ((1ull << l) - d)) / d + 1;
+    return FastDiv{d, (uint32_t)m, l};
+}
+
+// Arrival counters of the split reduction sit one per 128-byte line
+// (tickets[tile * kTicketStride]), so the workgroups of different tiles do
+// not contend for one cache line.
+constexpr int kTicketStride = 32;
+
 // Everything a convolution launch needs, resolved on the host.
 struct ConvParams {
     const void* x;
@@ -31,6 +51,9 @@ struct ConvParams {
     int Hp, Wp;     // padded input height / width (H + 2 pad, W + 2 pad)
     float* ws;      // S partial tiles per output tile (S > 1 only)
     unsigned* tickets;  // one arrival counter per output tile (S > 1 only)
+    const void* zero;   // >= 256 zero bytes: the source of every padded tap
+    FastDiv fd_wstr, fd_rwp, fd_wp, fd_hp;  // filled by the variant's launcher
+    FastDiv fd_ow, fd_t, fd_kw;
 };
 
 // Static description of one compiled implicit-GEMM instantiation.
@@ -41,14 +64,15 @@ struct IgemmVariant {
     int waves_m, waves_n, waves_k;
     int reps_m, reps_n;
     int kc_max;
-    // LDS bytes the variant needs for a stage of `kc` channels with a window
-    // of R rows by Wp columns and T taps.
-    int (*lds_bytes)(int kc, int R, int Wp, int T);
+    // LDS bytes the variant needs for this shape and tiling (p has the shape
+    // plus kc, stages, S and R filled in); > 163840 means "cannot run".
+    int (*lds_bytes)(const ConvParams& p);
     hipError_t (*launch)(const ConvParams& p, hipStream_t stream);
 };
 
 // Kernel-file registries.
 const IgemmVariant* igemm_f32_variants(int* count);
+const IgemmVariant* igemm_f32_sk_variants(int* count);
 const IgemmVariant* igemm_f16_variants(int* count);
 
 // Direct (one lane per output) reference kernel.

@@ -59,11 +59,16 @@ template <> struct MfmaF32<16> {
 };
 
 // LDS carve-up of one workgroup, in 4-byte words.  Shared by the host
-// (legality, launch size) and the kernel so the two cannot disagree.
+// (legality, launch size) and the kernel so the two cannot disagree.  The W
+// and window regions are whole 64-word chunks: each chunk is filled by one
+// direct-to-LDS load instruction of one wave.
 struct F32Layout {
     int ksp;       // stage reduction extent kc*T rounded up to the MFMA K
-    int wstr;      // W tile row stride (odd, spreads rows over banks)
-    int xs_off;    // window tile [kc][R][Wp]
+    int wstr;      // W tile row stride; = KPI mod 64 so a fragment read of
+                   // rows i and k-lanes q hits 64 distinct banks
+    int w_words;   // W region [tile_m][wstr], rounded up to 64
+    int xs_off;    // window region [kc][R][Wp]
+    int x_words;   // rounded up to 64
     int ktab_off;  // per-k window offset table [ksp]
     int epi_off;   // per-channel bias and rsqrt [2][tile_m]
     int words;
@@ -73,14 +78,28 @@ __host__ __device__ inline F32Layout f32_layout(int tile_m, int kpi, int kc, int
                                                 int red_words) {
     F32Layout L;
     L.ksp = round_up(kc * T, kpi);
-    L.wstr = L.ksp + 1;
-    L.xs_off = tile_m * L.wstr;
-    int stage = L.xs_off + kc * R * Wp;
+    L.wstr = round_up(L.ksp - kpi, 64) + kpi;
+    L.w_words = round_up(tile_m * L.wstr, 64);
+    L.xs_off = L.w_words;
+    L.x_words = round_up(kc * R * Wp, 64);
+    int stage = L.xs_off + L.x_words;
     int region = stage > red_words ? stage : red_words;
     L.ktab_off = region;
     L.epi_off = L.ktab_off + L.ksp;
     L.words = L.epi_off + 2 * tile_m;
     return L;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// One wave fills 64 consecutive LDS words; lane l's word comes from src.
+__device__ __forceinline__ void load_word_to_lds(const float* src, float* lds_chunk) {
+    __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)lds_chunk, 4, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (uint32_t)(((uint64_t)__umulhi(n, f.mul) + n) >> f.shift);
 }
 
 template <int MF, int WM, int WN, int WK, int RM, int RN>
@@ -100,6 +119,7 @@ __global__ __launch_bounds__(WM * WN * WK * 64) void igemm_f32_kernel(ConvParams
     using acc_t = typename Mf::acc_t;
     constexpr int M = Mf::M, N = Mf::N, KPI = Mf::KPI, NACC = Mf::NACC;
     constexpr int TILE_M = Cfg::TILE_M, TILE_N = Cfg::TILE_N, THREADS = Cfg::THREADS;
+    constexpr int NWAVES = THREADS / 64;
 
     extern __shared__ float lds[];
     __shared__ int s_last;
@@ -178,8 +198,8 @@ __global__ __launch_bounds__(WM * WN * WK * 64) void igemm_f32_kernel(ConvParams
 
     const float* __restrict__ xg = static_cast<const float*>(p.x);
     const float* __restrict__ wg = static_cast<const float*>(p.w);
+    const float* zero = static_cast<const float*>(p.zero);
     const int RWp = p.R * p.Wp;
-    const int stage_words_x = p.kc * RWp;
 
     for (int st = 0; st < p.stages; ++st) {
         const int c0 = (split * p.stages + st) * p.kc;
@@ -187,33 +207,39 @@ __global__ __launch_bounds__(WM * WN * WK * 64) void igemm_f32_kernel(ConvParams
         const int cvalid = min(p.kc, p.CI - c0);
         const int kvalid = cvalid * p.T;
         __syncthreads();  // previous stage fully consumed
+        // Every load of the stage is issued before any is waited for: the
+        // loads write LDS directly, so nothing waits on a register.
         // W tile: rows co0.., columns c0*T .. c0*T + ksp (zero past kvalid)
-        for (int i = tid; i < TILE_M * L.ksp; i += THREADS) {
-            const int m = i / L.ksp;
-            const int kk = i - m * L.ksp;
-            const int co = co0 + m;
-            float v = 0.0f;
-            if (co < p.CO && kk < kvalid) v = wg[(long long)co * p.K + (long long)c0 * p.T + kk];
-            Ws[m * L.wstr + kk] = v;
+        for (int ch = wave; ch < L.w_words / 64; ch += NWAVES) {
+            const uint32_t q = (uint32_t)(ch * 64 + lane);
+            const uint32_t m = fdiv(q, p.fd_wstr);
+            const int kk = (int)(q - m * (uint32_t)L.wstr);
+            const int co = co0 + (int)m;
+            const float* src = zero;
+            if ((int)m < TILE_M && co < p.CO && kk < kvalid)
+                src = wg + (long long)co * p.K + (long long)c0 * p.T + kk;
+            load_word_to_lds(src, Ws + ch * 64);
         }
         // padded-input window: channels c0.., virtual rows vr_first..
-        for (int i = tid; i < stage_words_x; i += THREADS) {
-            const int c = i / RWp;
-            const int rem = i - c * RWp;
-            const int r = rem / p.Wp;
-            const int col = rem - r * p.Wp;
-            float v = 0.0f;
-            if (c < cvalid) {
+        for (int ch = wave; ch < L.x_words / 64; ch += NWAVES) {
+            const uint32_t i = (uint32_t)(ch * 64 + lane);
+            const uint32_t c = fdiv(i, p.fd_rwp);
+            const uint32_t rem = i - c * (uint32_t)RWp;
+            const uint32_t r = fdiv(rem, p.fd_wp);
+            const int col = (int)(rem - r * (uint32_t)p.Wp);
+            const float* src = zero;
+            if ((int)c < cvalid) {
                 const long long vr = vr_first + r;
-                const long long n = vr / p.Hp;
+                const long long n = fdiv((uint32_t)vr, p.fd_hp);
                 const int iy = (int)(vr - n * p.Hp) - p.pad;
                 const int ix = col - p.pad;
                 if (n < p.N && iy >= 0 && iy < p.H && ix >= 0 && ix < p.W)
-                    v = xg[((n * p.CI + c0 + c) * p.H + iy) * (long long)p.W + ix];
+                    src = xg + ((n * p.CI + c0 + c) * p.H + iy) * (long long)p.W + ix;
             }
-            Xs[i] = v;
+            load_word_to_lds(src, Xs + ch * 64);
         }
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's loads have landed
+        __syncthreads();                // and everybody else's
         const int nsteps = (kvalid + KPI - 1) / KPI;
         for (int j = wk; j < nsteps; j += WK) {
             const int k = j * KPI + Mf::k_idx(lane);
@@ -253,6 +279,12 @@ __global__ __launch_bounds__(WM * WN * WK * 64) void igemm_f32_kernel(ConvParams
     }
 
     // ---- split reduction across workgroups ---------------------------------
+    // Partials and tickets are accessed only with device-scope atomics.  On
+    // gfx950 a device-scope store is written through to the device's point
+    // of coherence and a device-scope load reads from it, so no cache-wide
+    // write-back or invalidate (what a device-scope fence costs) is needed:
+    // each wave waits for its stores to complete before the workgroup
+    // barrier, and the ticket is taken after the barrier.
     if (p.S > 1) {
         const long long tile_words = (long long)TILE_M * TILE_N;
         float* part = p.ws + ((long long)tile * p.S) * tile_words;
@@ -262,29 +294,70 @@ __global__ __launch_bounds__(WM * WN * WK * 64) void igemm_f32_kernel(ConvParams
             for (int rm = 0; rm < RM; ++rm)
                 for (int rn = 0; rn < RN; ++rn)
                     for (int r = 0; r < NACC; ++r)
-                        mine[(base + (rm * RN + rn) * NACC + r) * 64 + lane] = acc[rm][rn][r];
+                        __hip_atomic_store(&mine[(base + (rm * RN + rn) * NACC + r) * 64 + lane],
+                                           acc[rm][rn][r], __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
         }
-        __threadfence();
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
         __syncthreads();
         if (tid == 0) {
-            const unsigned old = atomicAdd(&p.tickets[tile], 1u);
+            const unsigned old = __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
             s_last = (old == (unsigned)(p.S - 1)) ? 1 : 0;
         }
         __syncthreads();
         if (!s_last) return;
-        __threadfence();
-        if (wk == 0) {
-            for (int rm = 0; rm < RM; ++rm)
-                for (int rn = 0; rn < RN; ++rn)
-                    for (int r = 0; r < NACC; ++r) {
-                        const int o = (base + (rm * RN + rn) * NACC + r) * 64 + lane;
-                        float sum = (split == 0) ? acc[rm][rn][r] : part[o];
-                        for (int s2 = 1; s2 < p.S; ++s2)
-                            sum += (s2 == split) ? acc[rm][rn][r] : part[(long long)s2 * tile_words + o];
-                        acc[rm][rn][r] = sum;
+        // Last to arrive: every thread of the workgroup reduces a share of
+        // the tile, with its loads issued in batches of OB outputs x SB
+        // splits before any is consumed.  Summation order is 0..S-1.
+        constexpr int OB = 4, SB = 8;
+        constexpr int TILE_WORDS = TILE_M * TILE_N;
+        for (int o0 = tid; o0 < TILE_WORDS; o0 += THREADS * OB) {
+            float sum[OB];
+            for (int u = 0; u < OB; ++u) sum[u] = 0.0f;
+            for (int s0 = 0; s0 < p.S; s0 += SB) {
+                float v[OB][SB];
+#pragma unroll
+                for (int u = 0; u < OB; ++u)
+#pragma unroll
+                    for (int j = 0; j < SB; ++j) {
+                        const int o = o0 + u * THREADS;
+                        v[u][j] = 0.0f;
+                        if (o < TILE_WORDS && s0 + j < p.S)
+                            v[u][j] = __hip_atomic_load(&part[(long long)(s0 + j) * tile_words + o],
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
+#pragma unroll
+                for (int u = 0; u < OB; ++u)
+#pragma unroll
+                    for (int j = 0; j < SB; ++j)
+                        if (s0 + j < p.S) sum[u] = (s0 + j == 0) ? v[u][j] : sum[u] + v[u][j];
+            }
+#pragma unroll
+            for (int u = 0; u < OB; ++u) {
+                const int o = o0 + u * THREADS;
+                if (o >= TILE_WORDS) continue;
+                // o = ((slot * RM + rm) * RN + rn) * NACC + r) * 64 + lane
+                const int ln = o & 63;
+                int t = o >> 6;
+                const int r = t % NACC;
+                t /= NACC;
+                const int rn = t % RN;
+                t /= RN;
+                const int rm = t % RM;
+                const int slot = t / RM;
+                const int row = ((slot % WM) * RM + rm) * M + Mf::c_row(r, ln);
+                const int co = co0 + row;
+                const long long pc = p0 + (long long)((slot / WM) * RN + rn) * N + Mf::ab_idx(ln);
+                if (co >= p.CO || pc >= p.P) continue;
+                const long long n = pc / p.OHW;
+                const long long rem = pc - n * p.OHW;
+                p.y[(n * p.CO + co) * p.OHW + rem] =
+                    apply_epilogue(p.epilogue, sum[u], e_bias[row], e_rs[row]);
+            }
         }
-        if (tid == 0) p.tickets[tile] = 0u;
+        if (tid == 0) __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
     }
 
     // ---- epilogue and store ------------------------------------------------
@@ -305,26 +378,37 @@ __global__ __launch_bounds__(WM * WN * WK * 64) void igemm_f32_kernel(ConvParams
 }
 
 template <int MF, int WM, int WN, int WK, int RM, int RN>
-int f32_lds_bytes(int kc, int R, int Wp, int T) {
+int f32_lds_bytes(const ConvParams& p) {
     using Cfg = F32Cfg<MF, WM, WN, WK, RM, RN>;
-    return 4 * f32_layout(Cfg::TILE_M, MfmaF32<MF>::KPI, kc, T, R, Wp, Cfg::RED_WORDS).words;
+    return 4 * f32_layout(Cfg::TILE_M, MfmaF32<MF>::KPI, p.kc, p.T, p.R, p.Wp, Cfg::RED_WORDS).words;
 }
 
 template <int MF, int WM, int WN, int WK, int RM, int RN>
 hipError_t f32_launch(const ConvParams& p, hipStream_t stream) {
     using Cfg = F32Cfg<MF, WM, WN, WK, RM, RN>;
-    const int bytes = f32_lds_bytes<MF, WM, WN, WK, RM, RN>(p.kc, p.R, p.Wp, p.T);
+    const int bytes = f32_lds_bytes<MF, WM, WN, WK, RM, RN>(p);
     auto kern = igemm_f32_kernel<MF, WM, WN, WK, RM, RN>;
-    // raise the dynamic-LDS limit once per instantiation (process-wide)
-    static std::atomic<int> lds_limit{0};
+    const F32Layout L = f32_layout(Cfg::TILE_M, MfmaF32<MF>::KPI, p.kc, p.T, p.R, p.Wp,
+                                   Cfg::RED_WORDS);
+    ConvParams q = p;
+    q.fd_wstr = make_fastdiv((uint32_t)L.wstr);
+    q.fd_rwp = make_fastdiv((uint32_t)(p.R * p.Wp));
+    q.fd_wp = make_fastdiv((uint32_t)p.Wp);
+    q.fd_hp = make_fastdiv((uint32_t)p.Hp);
+    // raise the dynamic-LDS limit (64 KiB by default) once per instantiation
+    static std::atomic<int> lds_limit{65536};
     if (bytes > lds_limit.load(std::memory_order_relaxed)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 163840);
-        if (e != hipSuccess) return e;
-        lds_limit.store(163840, std::memory_order_relaxed);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return e;
+        }
+        lds_limit.store(bytes, std::memory_order_relaxed);
     }
+    (void)hipGetLastError();  // report only this launch's error
     const long long grid = (long long)p.tiles_m * p.tiles_n * p.S;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::THREADS), bytes, stream, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(Cfg::THREADS), bytes, stream, q);
     return hipGetLastError();
 }
 

@@ -147,8 +147,9 @@ const std::vector<Variant>& variants() {
             d.ig = nullptr;
             out.push_back(d);
         }
-        int n32 = 0, n16 = 0;
+        int n32 = 0, n16 = 0, nsk = 0;
         const IgemmVariant* t32 = igemm_f32_variants(&n32);
+        const IgemmVariant* tsk = igemm_f32_sk_variants(&nsk);
         const IgemmVariant* t16 = igemm_f16_variants(&n16);
         auto add = [&](const IgemmVariant* t, int n) {
             for (int i = 0; i < n; ++i) {
@@ -173,6 +174,7 @@ const std::vector<Variant>& variants() {
             }
         };
         add(t32, n32);
+        add(tsk, nsk);
         add(t16, n16);
         return out;
     }();
@@ -338,11 +340,19 @@ bool legal(const Shape& s, const ct_tile_config& c, Resolved* out, std::string* 
     if ((long long)(c.split_k - 1) * per_split >= s.CI) return no("an empty split");
     if ((long long)c.split_k * per_split < s.CI) return no("splits do not cover CI");
     if (v.desc.threads > kMaxThreads) return no("workgroup too large");
+    // virtual padded rows are addressed with 32-bit arithmetic
+    if ((long long)s.N * (s.H + 2LL * s.pad) >= (1LL << 31)) return no("too many padded rows");
     const int R = window_rows(s, v.desc.tile_n);
     const long long Wp = (long long)s.W + 2 * s.pad;
     if ((long long)c.kc * R * Wp > (1LL << 28)) return no("window too large");
-    const int lds = v.ig->lds_bytes(c.kc, R, (int)Wp, s.T);
-    if (lds > kMaxLds || lds <= 0) return no("LDS above 160 KiB");
+    ConvParams lp{};
+    lp.N = s.N; lp.CI = s.CI; lp.H = s.H; lp.W = s.W; lp.CO = s.CO; lp.KH = s.KH; lp.KW = s.KW;
+    lp.stride = s.stride; lp.pad = s.pad; lp.OH = s.OH; lp.OW = s.OW; lp.T = s.T; lp.K = s.K;
+    lp.P = s.P; lp.OHW = s.OH * s.OW; lp.Hp = s.H + 2 * s.pad; lp.Wp = (int)Wp;
+    lp.kc = c.kc; lp.stages = c.stages; lp.S = c.split_k; lp.R = R;
+    const int lds = v.ig->lds_bytes(lp);
+    // 64 bytes left for the kernels' static LDS
+    if (lds + 64 > kMaxLds || lds <= 0) return no("LDS above 160 KiB");
     const long long tiles_m = (s.CO + v.desc.tile_m - 1) / v.desc.tile_m;
     const long long tiles_n = (s.P + v.desc.tile_n - 1) / v.desc.tile_n;
     const long long grid = tiles_m * tiles_n * c.split_k;
@@ -527,6 +537,13 @@ int get_workspace(hipStream_t stream, long long ws_bytes, long long n_tickets, W
     std::lock_guard<std::mutex> lk(g_ws_mu);
     Workspace& w = g_ws[{dev, stream}];
     if (w.ws_bytes < ws_bytes || w.n_tickets < n_tickets) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        e = hipStreamIsCapturing(stream, &cs);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+        if (cs != hipStreamCaptureStatusNone)
+            return fail(CT_ERR_UNSUPPORTED,
+                        "the split workspace of this stream must grow, which cannot happen during "
+                        "stream capture: run the same convolution once on the stream first");
         // in-flight launches on this stream may still use the old buffers
         e = hipStreamSynchronize(stream);
         if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
@@ -556,6 +573,32 @@ int get_workspace(hipStream_t stream, long long ws_bytes, long long n_tickets, W
         w.n_tickets = n;
     }
     *out = w;
+    return CT_OK;
+}
+
+// One zeroed 256-byte block per device: the source address of every padded
+// tap in the direct-to-LDS loads.
+std::mutex g_zero_mu;
+std::map<int, void*> g_zero;
+
+int zero_page(const void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_zero_mu);
+    auto it = g_zero.find(dev);
+    if (it != g_zero.end()) {
+        *out = it->second;
+        return CT_OK;
+    }
+    void* z = nullptr;
+    e = hipMalloc(&z, 256);
+    if (e != hipSuccess) return fail(CT_ERR_NO_MEMORY, "zero page: %s", hipGetErrorString(e));
+    e = hipMemset(z, 0, 256);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return hip_fail(e, "zero page");
+    g_zero[dev] = z;
+    *out = z;
     return CT_OK;
 }
 
@@ -594,9 +637,11 @@ int launch_tiled(const Shape& s, const ct_tile_config& c, const void* x, const v
     p.tiles_m = r.tiles_m;
     p.tiles_n = r.tiles_n;
     p.R = r.R;
+    int zst = zero_page(&p.zero);
+    if (zst != CT_OK) return zst;
     if (c.split_k > 1) {
         Workspace ws;
-        int st = get_workspace(stream, r.ws_bytes, (long long)r.tiles_m * r.tiles_n, &ws);
+        int st = get_workspace(stream, r.ws_bytes, (long long)r.tiles_m * r.tiles_n * kTicketStride, &ws);
         if (st != CT_OK) return st;
         p.ws = ws.ws;
         p.tickets = ws.tickets;

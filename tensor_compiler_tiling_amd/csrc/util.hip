@@ -59,14 +59,17 @@ hipError_t launch_fill_uniform(void* dst, long long n, int dtype, float lo, floa
     if (blocks < 1) blocks = 1;
     switch (dtype) {
         case DT_F32:
+            (void)hipGetLastError();
             hipLaunchKernelGGL(fill_uniform_kernel<DT_F32>, dim3((unsigned)blocks), dim3(256), 0,
                                stream, dst, n, lo, hi, seed);
             break;
         case DT_F16:
+            (void)hipGetLastError();
             hipLaunchKernelGGL(fill_uniform_kernel<DT_F16>, dim3((unsigned)blocks), dim3(256), 0,
                                stream, dst, n, lo, hi, seed);
             break;
         case DT_BF16:
+            (void)hipGetLastError();
             hipLaunchKernelGGL(fill_uniform_kernel<DT_BF16>, dim3((unsigned)blocks), dim3(256), 0,
                                stream, dst, n, lo, hi, seed);
             break;
@@ -81,6 +84,7 @@ hipError_t launch_compare(const float* a, const float* b, long long n, float ato
     long long blocks = (n + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
+    (void)hipGetLastError();
     hipLaunchKernelGGL(compare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a, b, n, atol,
                        rtol, bad_count);
     return hipGetLastError();
