@@ -8,15 +8,20 @@ fp32 layer (the final ResNet layer of the TVM tutorial's tuning example),
 with seeded synthetic inputs already resident in HBM.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
-                    [--tune] [--no-cpu-baseline]
+                    [--tune] [--cache PATH | --no-cache] [--no-cpu-baseline]
+                    [--calibrate-copy]
 
-K steps are captured in one HIP graph and replayed (default) or launched
-eagerly (--eager); HIP events on the launch stream bracket the K steps.
+The tile config comes from the tuning log shipped with the package (the
+search's recorded winners, loaded with ct_cache_load) unless --no-cache or
+--tune is given.  K steps are captured in one HIP graph and replayed
+(default) or launched eagerly (--eager); HIP events on the launch stream
+bracket the K steps.
 Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +34,71 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}  # dense matrix peaks, MI355X
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "tensor_compiler_tiling_amd", "csrc")
+DEFAULT_CACHE = os.path.join(ROOT, "tensor_compiler_tiling_amd", "tuned", "gfx950.jsonl")
+TRAFFIC_LOG = os.path.join(ROOT, "profiles", "traffic.json")
+_SHARED_SRC = ["ct_kernels.hpp", "ct_device.hpp", "igemm_common.hpp"]
+
+
+def kernel_sources(kernel: str):
+    """The source files a kernel (variant name, or "broadcast") is built from."""
+    if kernel == "broadcast":
+        main = "broadcast.hip"
+    elif kernel.startswith("f32sk_"):
+        main = "igemm_f32_sk.hip"
+    elif kernel.startswith("f32_"):
+        main = "igemm_f32.hip"
+    elif kernel.startswith(("f16_", "bf16_")):
+        main = "igemm_f16.hip"
+    else:
+        main = "conv_direct.hip"
+    return [main] + _SHARED_SRC
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in kernel_sources(kernel):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str, cfg: dict):
+    """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+    recorded for this workload, or None when no record matches the kernel
+    source and tile config as they are now."""
+    try:
+        with open(TRAFFIC_LOG) as f:
+            recs = json.load(f)
+    except (OSError, ValueError):
+        return None
+    digest = source_digest(kernel)
+    for r in recs:
+        if (r.get("workload") == workload and r.get("kernel") == kernel
+                and r.get("source_sha256") == digest and r.get("tile", {}) == cfg):
+            return r.get("traffic_bytes_per_launch")
+    return None
+
+
+def calibrate_copy(mib: int = 1024, reps: int = 3) -> None:
+    """Plain device-to-device copies of a known size: the reference dispatches
+    that scale the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = mib * 2 ** 20 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def host_threads() -> int:
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    return len(os.sched_getaffinity(0))
 
 
 def _parse():
@@ -43,7 +113,11 @@ def _parse():
     ap.add_argument("--tune-ms", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--cache", default=None, help="tile-config cache (JSON lines) to load first")
+    ap.add_argument("--cache", default=DEFAULT_CACHE,
+                    help="tuning log (JSON lines) to load before dispatch")
+    ap.add_argument("--no-cache", action="store_true", help="do not load a tuning log")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run 1 GiB copies (reference dispatches for the HBM counters)")
     return ap.parse_args()
 
 
@@ -62,19 +136,39 @@ def cpu_baseline(w, seconds: float) -> dict:
     inp = wl.conv_inputs(w)
     x = inp["x"].astype(np.float64)
     k = inp["w"].astype(np.float64)
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = host_threads()
     reps = 0
     t0 = time.perf_counter()
     while True:
         O.conv2d_nchw(x, k, w.stride, w.pad)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
+        if el >= seconds:
             break
     tflops = w.flops * reps / el / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{reps} full passes of the fp64 seven-loop oracle on {w.name} "
-                      f"({el:.1f} s)"}
+    return {"value": round(tflops, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} full passes of the fp64 seven-loop oracle (OpenMP over n, f) "
+                      f"on {w.name} in {el:.1f} s"}
+
+
+def cpu_baseline_broadcast(bw, seconds: float) -> dict:
+    """The fp64 oracle broadcast on this host, repeated for about `seconds`;
+    reported as bytes of the output dtype written per second."""
+    from oracle import oracle as O
+    from tensor_compiler_tiling_amd import workloads as wl
+    var = wl.broadcast_var(bw)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.broadcast_exp(var, bw.N, bw.H, bw.W)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(bw.bytes_written() * reps / el / 1e9, 3), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full [1,{bw.C},1,1]->[{bw.N},{bw.C},{bw.H},{bw.W}] fp64 "
+                      f"oracle passes in {el:.1f} s, counted at {bw.out_dtype} output bytes"}
 
 
 def bench_broadcast(a, name: str) -> dict:
@@ -123,7 +217,8 @@ def bench_broadcast(a, name: str) -> dict:
         ms = e0.elapsed_time(e1) / a.steps
         res[label] = {"ms_per_step": round(ms, 6), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
     gbs = res["channel"]["GB/s"]
-    return {
+    traffic = measured_traffic(name, "broadcast", {"mode": "channel"})
+    out = {
         "metric": "per-channel broadcast [1,C,1,1]->[N,C,H,W] of exp(var[c]), HBM GB/s",
         "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": res["channel"]["ms_per_step"], "higher_is_better": True,
@@ -133,10 +228,13 @@ def bench_broadcast(a, name: str) -> dict:
                    "bytes_written_per_step": nbytes, "rotating_buffers": nbuf,
                    "launch": "hip_graph"},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic},
         "flat_form": res["flat"],
         "speedup_channel_vs_flat": round(res["flat"]["ms_per_step"] / res["channel"]["ms_per_step"], 3),
     }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_broadcast(bw, a.cpu_seconds)
+    return out
 
 
 def main():
@@ -149,6 +247,9 @@ def main():
     import torch
     from tensor_compiler_tiling_amd import convtile as ct
     from tensor_compiler_tiling_amd import workloads as wl
+
+    if a.calibrate_copy:
+        calibrate_copy()
 
     name = a.workload or wl.HEADLINE
     if name in wl.BROADCAST_WORKLOADS:
@@ -167,8 +268,10 @@ def main():
     dt = ct.dtype_code(tdt)
     args = w.shape_args() + (dt, w.epilogue)
 
-    if a.cache and os.path.exists(a.cache):
+    cache_loaded = None
+    if not a.no_cache and not a.tune and a.cache and os.path.exists(a.cache):
         ct.check(ct.ct_cache_load(a.cache), "cache load")
+        cache_loaded = os.path.relpath(a.cache, ROOT)
     tune_info = None
     if a.tune:
         t0 = time.perf_counter()
@@ -257,10 +360,14 @@ def main():
                    "epilogue": w.epilogue, "flops_per_step": w.flops,
                    "launch": "hip_graph" if graph is not None else "eager",
                    "kernel": vdesc["name"], "split_k": cfg.split_k, "stages": cfg.stages,
-                   "kc": cfg.kc, "config_index": cfg.index, "from_cache": bool(from_cache)},
+                   "kc": cfg.kc, "config_index": cfg.index, "from_cache": bool(from_cache),
+                   "tuning_log": cache_loaded},
         "pct_of_peak": round(100.0 * tflops / peak, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4), "traffic": None},
+                     "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
+                     "traffic": measured_traffic(name, vdesc["name"],
+                                                 {"split_k": cfg.split_k, "stages": cfg.stages,
+                                                  "kc": cfg.kc})},
         "eager_ms_per_step": round(eager_ms, 6) if eager_ms else None,
         "wall_s": round(wall, 4),
     }

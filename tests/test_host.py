@@ -192,3 +192,28 @@ def test_workload_shapes():
     assert ohs == [14, 7, 112, 56, 28, 14, 7, 14, 14, 32]
     assert wl.CONV_WORKLOADS[wl.HEADLINE].flops == 231211008
     assert wl.CONV_WORKLOADS["f16_n128_c128to256_32x32_k3_epi"].flops == 77309411328
+
+
+def test_shipped_tuning_log_is_legal():
+    """Every record of the package's gfx950 tuning log parses, names a compiled
+    variant and is legal for its shape (the loader drops anything else)."""
+    log = os.path.join(ROOT, "tensor_compiler_tiling_amd", "tuned", "gfx950.jsonl")
+    lines = [l for l in open(log).read().splitlines() if l.strip()]
+    keys = {json.loads(l)["key"] for l in lines}
+    ct.ct_cache_clear()
+    try:
+        assert ct.ct_cache_load(log) == 0
+        assert ct.ct_cache_size() == len(keys)
+        for name, w in wl.CONV_WORKLOADS.items():
+            st, cfg, from_cache = ct.ct_conv2d_query(*_args(w))
+            assert st == 0 and from_cache == 1, name
+    finally:
+        ct.ct_cache_clear()
+
+
+def test_traffic_records_point_at_summaries():
+    recs = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    for r in recs:
+        assert os.path.exists(os.path.join(ROOT, r["summary"])), r["summary"]
+        assert r["traffic_bytes_per_launch"] > 0
+        assert len(r["source_sha256"]) == 64
