@@ -54,6 +54,7 @@ struct ConvParams {
     const void* zero;   // >= 256 zero bytes: the source of every padded tap
     FastDiv fd_wstr, fd_rwp, fd_wp, fd_hp;  // filled by the variant's launcher
     FastDiv fd_ow, fd_t, fd_kw;
+    FastDiv fd_w, fd_hw;                    // W, H*W (register-staged windows)
 };
 
 // Static description of one compiled implicit-GEMM instantiation.
@@ -73,6 +74,7 @@ struct IgemmVariant {
 // Kernel-file registries.
 const IgemmVariant* igemm_f32_variants(int* count);
 const IgemmVariant* igemm_f32_sk_variants(int* count);
+const IgemmVariant* igemm_f32_sk16_variants(int* count);
 const IgemmVariant* igemm_f16_variants(int* count);
 
 // Direct (one lane per output) reference kernel.

@@ -28,9 +28,26 @@
 // past the last image are written as zeros, so padding is applied inline.
 #pragma once
 
+#include <cstddef>
+
 #include "ct_kernels.hpp"
 
 namespace ct {
+
+// Kernel arguments arrive in a buffer no cache holds yet.  Left alone, the
+// compiler loads the fields of ConvParams in several batches where they are
+// first needed, and each batch that touches a new 64-byte line is a full
+// memory round trip (about a microsecond).  Naming one field of every line at
+// kernel entry makes the first batch bring in all five lines together; later
+// loads of any field then hit the scalar cache.
+static_assert(sizeof(ConvParams) <= 320, "ConvParams spans more than five 64-byte lines");
+static_assert(offsetof(ConvParams, x) < 64 && offsetof(ConvParams, KH) / 64 == 1 &&
+                  offsetof(ConvParams, tiles_n) / 64 == 2 && offsetof(ConvParams, fd_wp) / 64 == 3 &&
+                  offsetof(ConvParams, fd_hw) / 64 == 4,
+              "one touched field per 64-byte line of ConvParams");
+__device__ __forceinline__ void fetch_kernargs(const ConvParams& p) {
+    asm volatile("" ::"s"(p.x), "s"(p.KH), "s"(p.tiles_n), "s"(p.fd_wp.d), "s"(p.fd_hw.d));
+}
 
 // Round up to a multiple.
 __host__ __device__ inline int round_up(int v, int m) { return (v + m - 1) / m * m; }

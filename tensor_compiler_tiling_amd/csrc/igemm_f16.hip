@@ -92,6 +92,7 @@ struct HCfg {
 // padded-window pixel (8 loads of 2 bytes, zero outside the image).
 template <int DT, int WM, int WN, int RM, int RN, int WTM, int XTM>
 __global__ __launch_bounds__(WM * WN * 64) void igemm_h_kernel(ConvParams p) {
+    fetch_kernargs(p);
     using Cfg = HCfg<DT, WM, WN, RM, RN, WTM, XTM>;
     constexpr int TILE_M = Cfg::TILE_M, TILE_N = Cfg::TILE_N, THREADS = Cfg::THREADS;
     extern __shared__ __align__(16) uint16_t hs[];

@@ -114,6 +114,7 @@ struct F32Cfg {
 
 template <int MF, int WM, int WN, int WK, int RM, int RN>
 __global__ __launch_bounds__(WM * WN * WK * 64) void igemm_f32_kernel(ConvParams p) {
+    fetch_kernargs(p);
     using Cfg = F32Cfg<MF, WM, WN, WK, RM, RN>;
     using Mf = typename Cfg::Mf;
     using acc_t = typename Mf::acc_t;

@@ -84,6 +84,7 @@ constexpr int kCoherent = 16;          // cache policy: device-coherent (sc1)
 //   fd_t = KH*KW, fd_kw = KW.
 template <int KL>
 __global__ __launch_bounds__(kSkThreads) void igemm_f32_sk_kernel(ConvParams p) {
+    fetch_kernargs(p);
     constexpr int KS = 8 * KL;
     constexpr int KT = KL / 4;
     static_assert(KL % 4 == 0, "KL must be a multiple of 4");

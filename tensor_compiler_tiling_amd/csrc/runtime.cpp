@@ -147,9 +147,10 @@ const std::vector<Variant>& variants() {
             d.ig = nullptr;
             out.push_back(d);
         }
-        int n32 = 0, n16 = 0, nsk = 0;
+        int n32 = 0, n16 = 0, nsk = 0, nsk16 = 0;
         const IgemmVariant* t32 = igemm_f32_variants(&n32);
         const IgemmVariant* tsk = igemm_f32_sk_variants(&nsk);
+        const IgemmVariant* tsk16 = igemm_f32_sk16_variants(&nsk16);
         const IgemmVariant* t16 = igemm_f16_variants(&n16);
         auto add = [&](const IgemmVariant* t, int n) {
             for (int i = 0; i < n; ++i) {
@@ -175,6 +176,7 @@ const std::vector<Variant>& variants() {
         };
         add(t32, n32);
         add(tsk, nsk);
+        add(tsk16, nsk16);
         add(t16, n16);
         return out;
     }();

@@ -134,8 +134,12 @@ def test_legality_rejects_oversized_stage():
         if cfg.variant == big["id"] and cfg.kc == 64:
             # a 128-row W tile of 64 channels x 9 taps alone is 295 KB
             assert legal == 0
-        if cfg.kc > 64:
-            assert legal == 0
+        if legal:
+            v = ct.variants()[cfg.variant]
+            assert cfg.kc <= v["kc_max"]
+            if v["name"].startswith(("f32sk_", "f32sk16_")):
+                # the split-K kernels hold a stage's kc * KH * KW k values in lanes
+                assert cfg.kc * 9 <= v["kc_max"]
 
 
 def test_query_default_without_gpu():
