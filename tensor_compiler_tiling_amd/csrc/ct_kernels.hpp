@@ -55,6 +55,7 @@ struct ConvParams {
     FastDiv fd_wstr, fd_rwp, fd_wp, fd_hp;  // filled by the variant's launcher
     FastDiv fd_ow, fd_t, fd_kw;
     FastDiv fd_w, fd_hw;                    // W, H*W (register-staged windows)
+    void* aux;          // variant-specific scratch (a reordered filter copy), or null
 };
 
 // Static description of one compiled implicit-GEMM instantiation.
@@ -69,6 +70,8 @@ struct IgemmVariant {
     // plus kc, stages, S and R filled in); > 163840 means "cannot run".
     int (*lds_bytes)(const ConvParams& p);
     hipError_t (*launch)(const ConvParams& p, hipStream_t stream);
+    // bytes of ConvParams::aux the launch needs (null: none)
+    long long (*aux_bytes)(const ConvParams& p);
 };
 
 // Kernel-file registries.
@@ -76,6 +79,7 @@ const IgemmVariant* igemm_f32_variants(int* count);
 const IgemmVariant* igemm_f32_sk_variants(int* count);
 const IgemmVariant* igemm_f32_sk16_variants(int* count);
 const IgemmVariant* igemm_f16_variants(int* count);
+const IgemmVariant* igemm_f16v2_variants(int* count);
 
 // Direct (one lane per output) reference kernel.
 hipError_t launch_conv_direct(const ConvParams& p, int dtype, hipStream_t stream);

@@ -1,0 +1,535 @@
+// fp16 / bf16 implicit-GEMM convolution for 3x3 filters, second form
+// (v_mfma_f32_32x32x16_f16 / _bf16, fp32 accumulation and output, as the
+// TVM tutorial "Tuning High Performance Convolution on NVIDIA GPUs", Step 1,
+// declares the output).
+//
+// The half-precision instruction takes 8 consecutive reduction values per
+// lane.  The reduction of a stage (KC channels x 9 taps) is ordered in groups
+// of 8 channels at one tap, g = tap * (KC/8) + channel/8, and both operands
+// sit channel-fastest in LDS, so a fragment is one 16-byte LDS read:
+//   filter tile  [m][g][8]           window  [pixel][channel]
+// What differs from the first form is where the reordering happens:
+//  - the filter is reordered once per call by a small kernel into a
+//    stage-major copy [CO'][CI'/KC][9][KC] (zero-padded to CO' = multiple of
+//    256 and CI' = multiple of KC), so one stage of one filter row is 9*KC
+//    contiguous halves and staging the filter tile is a stream of 16-byte
+//    copies with no arithmetic;
+//  - the window is staged with vector loads of PX consecutive pixels of one
+//    channel (PX = 8, 4, 2 or 1, the largest the row width and alignment
+//    allow), 8 channels per task, transposed in registers into PX 16-byte
+//    pixel records;
+//  - LDS holds two copies of (filter tile, window): the next stage's global
+//    loads are issued before the current stage's matrix steps and written to
+//    the other copy after them, with one barrier per stage;
+//  - a stage's 9*KC/16 matrix steps are unrolled, each reading the next
+//    step's fragments before issuing its own instructions.
+// The window's padding is zeroed once at kernel start and never written
+// again (only in-image pixels are staged).
+#include "ct_device.hpp"
+#include "igemm_common.hpp"
+
+#include <atomic>
+
+namespace ct {
+
+namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
+typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
+
+constexpr int kPackCO = 256;  // reordered filter rows: a multiple of this
+
+template <int DT> struct HMma2;
+template <> struct HMma2<DT_F16> {
+    static __device__ __forceinline__ floatx16 mma(uint4v a, uint4v b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                                     __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+    }
+};
+template <> struct HMma2<DT_BF16> {
+    static __device__ __forceinline__ floatx16 mma(uint4v a, uint4v b, floatx16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                      __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+// w [CO][CI][T] -> wp [COp][CIp/KC][T][KC], zeros outside CO x CI.
+__global__ __launch_bounds__(256) void h2_prepack_kernel(const uint16_t* __restrict__ w,
+                                                         uint16_t* __restrict__ wp, int CO, int CI,
+                                                         int T, int KC, int COp, int CIp) {
+    const long long total = (long long)COp * CIp * T;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
+         i += (long long)gridDim.x * 256) {
+        const int c = (int)(i % KC);
+        const long long r1 = i / KC;
+        const int t = (int)(r1 % T);
+        const long long r2 = r1 / T;
+        const int s = (int)(r2 % (CIp / KC));
+        const int co = (int)(r2 / (CIp / KC));
+        const int ci = s * KC + c;
+        wp[i] = (co < CO && ci < CI) ? w[((long long)co * CI + ci) * T + t] : (uint16_t)0;
+    }
+}
+
+template <int WM, int WN, int RM, int RN, int KC, int T>
+struct H2 {
+    static constexpr int TM = WM * RM * 32;
+    static constexpr int TN = WN * RN * 32;
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int CG = KC / 8;          // channel groups per stage
+    static constexpr int G = T * CG;           // groups per stage
+    static constexpr int NSTEP = G / 2;        // instruction steps per stage
+    static constexpr int WST = (G + 1) * 8;    // halves per filter row in LDS (odd x 16 B)
+    static constexpr int KCS = (CG + 1) * 8;   // halves per window pixel (odd x 16 B)
+    static constexpr int WCH = TM * G;         // 16-byte filter chunks per stage
+    static constexpr int WPT = (WCH + NT - 1) / NT;
+    static constexpr int XPT = NT >= 512 ? 1 : 2;  // window tasks per thread
+    static constexpr int WB = TM * WST;        // halves per filter copy
+    static_assert(G % 2 == 0, "a step takes two groups");
+};
+
+__host__ __device__ inline int h2_xb(int R, int Wp, int kcs) { return round_up(R * Wp * kcs, 8); }
+
+// Vector of PX halves.
+template <int PX> struct PxVec;
+template <> struct PxVec<8> { typedef uint4v T; };
+template <> struct PxVec<4> { typedef uint2v T; };
+template <> struct PxVec<2> { typedef uint32_t T; };
+template <> struct PxVec<1> { typedef uint16_t T; };
+
+template <int PX>
+__device__ __forceinline__ uint16_t px_half(const typename PxVec<PX>::T& v, int u) {
+    if constexpr (PX == 8) {
+        const uint32_t d = v[u >> 1];
+        return (u & 1) ? (uint16_t)(d >> 16) : (uint16_t)(d & 0xffffu);
+    } else if constexpr (PX == 4) {
+        const uint32_t d = v[u >> 1];
+        return (u & 1) ? (uint16_t)(d >> 16) : (uint16_t)(d & 0xffffu);
+    } else if constexpr (PX == 2) {
+        return (u & 1) ? (uint16_t)(v >> 16) : (uint16_t)(v & 0xffffu);
+    } else {
+        return v;
+    }
+}
+
+__device__ __forceinline__ uint32_t pack2h(uint16_t lo, uint16_t hi) {
+    return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// Divisors: fd_kw = KW.
+template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
+__global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
+    fetch_kernargs(p);
+    using C = H2<WM, WN, RM, RN, KC, T>;
+    constexpr int TM = C::TM, TN = C::TN, NT = C::NT, CG = C::CG, G = C::G;
+    constexpr int NSTEP = C::NSTEP, WST = C::WST, KCS = C::KCS, WPT = C::WPT, XPT = C::XPT;
+    extern __shared__ __align__(16) uint16_t hs[];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave % WM;
+    const int wn = wave / WM;
+    const int lj = lane & 31;
+    const int lh = lane >> 5;
+
+    const int RWp = p.R * p.Wp;
+    const int XB = h2_xb(p.R, p.Wp, KCS);
+    uint16_t* Wsb = hs;                // [2][TM][WST]
+    uint16_t* Xsb = hs + 2 * C::WB;    // [2][R*Wp][KCS]
+    float* e_bias = reinterpret_cast<float*>(hs + 2 * C::WB + 2 * XB);
+    float* e_rs = e_bias + TM;
+
+    // workgroup -> (split, tile); when the column tiles come in multiples of
+    // 8, the row tiles of one column tile (readers of the same window) share
+    // blockIdx % 8, i.e. one XCD under round-robin placement
+    const int tiles = p.tiles_m * p.tiles_n;
+    const int split = blockIdx.x / tiles;
+    const int b = blockIdx.x - split * tiles;
+    int tm, tn;
+    if ((p.tiles_n & 7) == 0) {
+        tm = (b >> 3) % p.tiles_m;
+        tn = (b / (8 * p.tiles_m)) * 8 + (b & 7);
+    } else {
+        tm = b % p.tiles_m;
+        tn = b / p.tiles_m;
+    }
+    const int tile = tm + tn * p.tiles_m;
+    const int co0 = tm * TM;
+    const long long p0 = (long long)tn * TN;
+    const long long n_first = p0 / p.OHW;
+    const int oy_first = (int)((p0 % p.OHW) / p.OW);
+    const long long vr_first = n_first * p.Hp + (long long)oy_first * p.stride;
+    const long long HW = (long long)p.H * p.W;
+
+    const uint16_t* __restrict__ xg = static_cast<const uint16_t*>(p.x);
+    const uint16_t* __restrict__ wpk = static_cast<const uint16_t*>(p.aux);
+    const int CIp = round_up(p.CI, KC);
+    const int NS = CIp / KC;  // stages of the whole reduction in the reordered filter
+
+    // ---- per-lane B columns --------------------------------------------------
+    int pbase[RN];       // window pixel of the column's (0,0) tap
+    long long yoff[RN];  // y offset of (n, 0, oy, ox); -1 past P
+#pragma unroll
+    for (int rn = 0; rn < RN; ++rn) {
+        const long long pc = p0 + (long long)(wn * RN + rn) * 32 + lj;
+        pbase[rn] = 0;
+        yoff[rn] = -1;
+        if (pc < p.P) {
+            const long long n = pc / p.OHW;
+            const int rem = (int)(pc - n * p.OHW);
+            const int oy = rem / p.OW;
+            const int ox = rem - oy * p.OW;
+            pbase[rn] = (int)(n * p.Hp + (long long)oy * p.stride - vr_first) * p.Wp + ox * p.stride;
+            yoff[rn] = n * (long long)p.CO * p.OHW + rem;
+        }
+    }
+    // window offset of this lane's group 2s + lh at every step
+    int koff[NSTEP];
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+        const int g = 2 * s + lh;
+        const int t = g / CG;
+        const int cg = g - t * CG;
+        const int ky = (int)(((uint64_t)__umulhi((uint32_t)t, p.fd_kw.mul) + (uint32_t)t) >> p.fd_kw.shift);
+        const int kx = t - ky * p.KW;
+        koff[s] = (ky * p.Wp + kx) * KCS + cg * 8;
+    }
+
+    // ---- epilogue tables; zero both windows ----------------------------------
+    for (int m = tid; m < TM; m += NT) {
+        const int co = co0 + m;
+        float bb = 0.0f, r = 1.0f;
+        if (co < p.CO) {
+            if (p.epilogue != EPI_NONE) bb = p.bias[co];
+            if (p.epilogue == EPI_EXP_BIAS_RSQRT) r = dev_rsqrt(p.var[co] + p.eps);
+        }
+        e_bias[m] = bb;
+        e_rs[m] = r;
+    }
+    {
+        uint4v* xz = reinterpret_cast<uint4v*>(Xsb);
+        for (int i = tid; i < XB / 4; i += NT) xz[i] = uint4v{0u, 0u, 0u, 0u};  // 2*XB halves
+    }
+
+    // ---- staging tasks (fixed for the kernel) ----------------------------------
+    // filter chunk q = (m, g): 16 bytes of row co0+m, group g of a stage
+    int wsrc[WPT];  // halves, without the stage term; -1: no chunk
+    int wdst[WPT];
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+        const int q = tid + j * NT;
+        wsrc[j] = -1;
+        wdst[j] = 0;
+        if (q < C::WCH) {
+            const int m = q / G;
+            const int g = q - m * G;
+            wsrc[j] = (co0 + m) * NS * (T * KC) + g * 8;
+            wdst[j] = m * WST + g * 8;
+        }
+    }
+    // window task q = (cg, window row r, run u): 8 channels x PX pixels
+    const int nrun = p.W / PX;
+    const int n_xt = CG * p.R * nrun;
+    long long xsrc[XPT];  // halves, channel cg*8 without the stage term; -1: none
+    int xdst[XPT];
+    int xch[XPT];         // channel of the task's first lane within a stage
+#pragma unroll
+    for (int j = 0; j < XPT; ++j) {
+        const int q = tid + j * NT;
+        xsrc[j] = -1;
+        xdst[j] = 0;
+        xch[j] = 0;
+        if (q < n_xt) {
+            const int cg = q / (p.R * nrun);
+            const int rem = q - cg * (p.R * nrun);
+            const int r = rem / nrun;
+            const int u = rem - r * nrun;
+            const long long vr = vr_first + r;
+            const long long n = vr / p.Hp;
+            const int iy = (int)(vr - n * p.Hp) - p.pad;
+            if (n < p.N && iy >= 0 && iy < p.H) {
+                xsrc[j] = ((n * p.CI + cg * 8) * p.H + iy) * (long long)p.W + u * PX;
+                xdst[j] = (r * p.Wp + p.pad + u * PX) * KCS + cg * 8;
+                xch[j] = cg * 8;
+            }
+        }
+    }
+
+    using XV = typename PxVec<PX>::T;
+    uint4v wreg[WPT];
+    XV xreg[XPT][8];
+    auto load_stage = [&](int s_abs, int c0) {
+#pragma unroll
+        for (int j = 0; j < WPT; ++j)
+            if (wsrc[j] >= 0)
+                wreg[j] = *reinterpret_cast<const uint4v*>(wpk + wsrc[j] + s_abs * (T * KC));
+#pragma unroll
+        for (int j = 0; j < XPT; ++j) {
+            if (xsrc[j] < 0) continue;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int c = c0 + xch[j] + i;
+                xreg[j][i] = c < p.CI ? *reinterpret_cast<const XV*>(xg + xsrc[j] + (long long)(c0 + i) * HW)
+                                      : XV{};
+            }
+        }
+    };
+    auto store_stage = [&](int buf) {
+        uint16_t* Wb = Wsb + buf * C::WB;
+        uint16_t* Xb = Xsb + buf * XB;
+#pragma unroll
+        for (int j = 0; j < WPT; ++j)
+            if (wsrc[j] >= 0) *reinterpret_cast<uint4v*>(Wb + wdst[j]) = wreg[j];
+#pragma unroll
+        for (int j = 0; j < XPT; ++j) {
+            if (xsrc[j] < 0) continue;
+#pragma unroll
+            for (int u = 0; u < PX; ++u) {
+                uint4v o;
+                o.x = pack2h(px_half<PX>(xreg[j][0], u), px_half<PX>(xreg[j][1], u));
+                o.y = pack2h(px_half<PX>(xreg[j][2], u), px_half<PX>(xreg[j][3], u));
+                o.z = pack2h(px_half<PX>(xreg[j][4], u), px_half<PX>(xreg[j][5], u));
+                o.w = pack2h(px_half<PX>(xreg[j][6], u), px_half<PX>(xreg[j][7], u));
+                *reinterpret_cast<uint4v*>(Xb + xdst[j] + u * KCS) = o;
+            }
+        }
+    };
+
+    floatx16 acc[RM][RN];
+#pragma unroll
+    for (int rm = 0; rm < RM; ++rm)
+#pragma unroll
+        for (int rn = 0; rn < RN; ++rn)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[rm][rn][r] = 0.0f;
+
+    auto mfma_stage = [&](int buf) {
+        const uint16_t* Wb = Wsb + buf * C::WB;
+        const uint16_t* Xb = Xsb + buf * XB;
+        uint4v a[2][RM], bf[2][RN];
+        auto frag = [&](int s, uint4v (&ar)[RM], uint4v (&br)[RN]) {
+#pragma unroll
+            for (int rm = 0; rm < RM; ++rm)
+                ar[rm] = *reinterpret_cast<const uint4v*>(Wb + ((wm * RM + rm) * 32 + lj) * WST +
+                                                          (2 * s + lh) * 8);
+#pragma unroll
+            for (int rn = 0; rn < RN; ++rn)
+                br[rn] = *reinterpret_cast<const uint4v*>(Xb + pbase[rn] * KCS + koff[s]);
+        };
+        frag(0, a[0], bf[0]);
+#pragma unroll
+        for (int s = 0; s < NSTEP; ++s) {
+            if (s + 1 < NSTEP) frag(s + 1, a[(s + 1) & 1], bf[(s + 1) & 1]);
+            // the next step's reads stay ahead of this step's instructions
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rm = 0; rm < RM; ++rm)
+#pragma unroll
+                for (int rn = 0; rn < RN; ++rn)
+                    acc[rm][rn] = HMma2<DT>::mma(a[s & 1][rm], bf[s & 1][rn], acc[rm][rn]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- stages of this split: load ahead, multiply, store ahead, one barrier
+    const int s_first = split * p.stages;
+    int nst = p.stages;
+    if (s_first + nst > NS) nst = NS - s_first;
+    __syncthreads();  // windows zeroed before any stage writes into them
+    if (nst > 0) {
+        load_stage(s_first, s_first * KC);
+        store_stage(0);
+    }
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+        const bool more = st + 1 < nst;
+        if (more) load_stage(s_first + st + 1, (s_first + st + 1) * KC);
+        // keep the loads here, ahead of the matrix steps: left free, the
+        // compiler sinks them to their LDS writes and the latency is exposed
+        asm volatile("" ::: "memory");
+        mfma_stage(st & 1);
+        if (more) store_stage((st + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- split reduction across workgroups (device-scope atomics) -------------
+    const int wslot = wm + wn * WM;
+    if (p.S > 1) {
+        const long long tile_words = (long long)TM * TN;
+        float* part = p.ws + ((long long)tile * p.S) * tile_words;
+        const int base = wslot * RM * RN * 16;
+        float* mine = part + (long long)split * tile_words;
+#pragma unroll
+        for (int rm = 0; rm < RM; ++rm)
+#pragma unroll
+            for (int rn = 0; rn < RN; ++rn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    __hip_atomic_store(&mine[(base + (rm * RN + rn) * 16 + r) * 64 + lane], acc[rm][rn][r],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            const unsigned old = __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (old == (unsigned)(p.S - 1)) ? 1 : 0;
+        }
+        __syncthreads();
+        if (!s_last) return;
+#pragma unroll
+        for (int rm = 0; rm < RM; ++rm)
+#pragma unroll
+            for (int rn = 0; rn < RN; ++rn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int o = (base + (rm * RN + rn) * 16 + r) * 64 + lane;
+                    float sum = 0.0f;
+                    for (int s2 = 0; s2 < p.S; ++s2) {
+                        const float v = (s2 == split)
+                                            ? acc[rm][rn][r]
+                                            : __hip_atomic_load(&part[(long long)s2 * tile_words + o],
+                                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        sum = (s2 == 0) ? v : sum + v;
+                    }
+                    acc[rm][rn][r] = sum;
+                }
+        if (tid == 0)
+            __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+
+    // ---- epilogue and store (C: row 8*(r/4) + 4*(lane/32) + r%4, col lane%32)
+#pragma unroll
+    for (int rm = 0; rm < RM; ++rm) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = (wm * RM + rm) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const int co = co0 + row;
+            if (co >= p.CO) continue;
+            const float eb = e_bias[row], er = e_rs[row];
+#pragma unroll
+            for (int rn = 0; rn < RN; ++rn) {
+                if (yoff[rn] < 0) continue;
+                p.y[yoff[rn] + (long long)co * p.OHW] = apply_epilogue(p.epilogue, acc[rm][rn][r], eb, er);
+            }
+        }
+    }
+}
+
+// Pixels per window task for this shape: the widest vector that divides W.
+inline int h2_px_for_shape(int W) {
+    if (W % 8 == 0) return 8;
+    if (W % 4 == 0) return 4;
+    if (W % 2 == 0) return 2;
+    return 1;
+}
+
+template <int WM, int WN, int RM, int RN, int KC, int T>
+int h2_bytes_for(const ConvParams& p, int px) {
+    using C = H2<WM, WN, RM, RN, KC, T>;
+    if (p.T != T || p.kc != KC) return 1 << 30;
+    if (p.P >= (1LL << 31) || (long long)p.N * p.Hp >= (1LL << 31)) return 1 << 30;
+    const long long CIp = round_up(p.CI, KC);
+    const long long COp = round_up(p.CO, kPackCO);
+    // reordered filter offsets are 32-bit
+    if (COp * CIp * T >= (1LL << 31)) return 1 << 30;
+    // the window tasks must fit the per-thread slots
+    if ((long long)C::CG * p.R * (p.W / px) > (long long)C::XPT * C::NT) return 1 << 30;
+    if ((long long)p.R * p.Wp * C::KCS >= (1LL << 28)) return 1 << 30;
+    return 2 * (2 * C::WB + 2 * h2_xb(p.R, p.Wp, C::KCS) + 4 * C::TM);
+}
+
+template <int WM, int WN, int RM, int RN, int KC, int T>
+int h2_lds_bytes(const ConvParams& p) {
+    return h2_bytes_for<WM, WN, RM, RN, KC, T>(p, h2_px_for_shape(p.W));
+}
+
+template <int WM, int WN, int RM, int RN, int KC, int T>
+long long h2_aux_bytes(const ConvParams& p) {
+    return 2LL * round_up(p.CO, kPackCO) * round_up(p.CI, KC) * T;
+}
+
+template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
+hipError_t h2_launch_px(const ConvParams& q, int bytes, hipStream_t stream) {
+    using C = H2<WM, WN, RM, RN, KC, T>;
+    auto kern = igemm_h2_kernel<DT, WM, WN, RM, RN, KC, T, PX>;
+    static std::atomic<int> lds_limit{65536};
+    if (bytes > lds_limit.load(std::memory_order_relaxed)) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return e;
+        }
+        lds_limit.store(bytes, std::memory_order_relaxed);
+    }
+    const long long grid = (long long)q.tiles_m * q.tiles_n * q.S;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), bytes, stream, q);
+    return hipGetLastError();
+}
+
+template <int DT, int WM, int WN, int RM, int RN, int KC, int T>
+hipError_t h2_launch(const ConvParams& p, hipStream_t stream) {
+    if (!p.aux) return hipErrorInvalidValue;
+    // the widest window vector the shape and the pointer's alignment allow
+    // (every run starts at a multiple of PX pixels of a row)
+    int px = h2_px_for_shape(p.W);
+    const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x);
+    while (px > 1 && (xa % (2u * px) != 0 || (p.H * (long long)p.W) % px != 0)) px >>= 1;
+    const int bytes = h2_bytes_for<WM, WN, RM, RN, KC, T>(p, px);
+    if (bytes > 163840 - 64) return hipErrorInvalidValue;
+
+    // reorder the filter into the stage-major copy
+    const int COp = round_up(p.CO, kPackCO);
+    const int CIp = round_up(p.CI, KC);
+    const long long total = (long long)COp * CIp * T;
+    long long blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(h2_prepack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(p.w), static_cast<uint16_t*>(p.aux), p.CO, p.CI,
+                       T, KC, COp, CIp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    ConvParams q = p;
+    q.fd_kw = make_fastdiv((uint32_t)p.KW);
+    switch (px) {
+        case 8: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 8>(q, bytes, stream);
+        case 4: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 4>(q, bytes, stream);
+        case 2: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 2>(q, bytes, stream);
+        default: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 1>(q, bytes, stream);
+    }
+}
+
+// descriptor: 32x32x16 instruction, waves WM x WN x 1, reps RM x RN; kc fixed
+// at KC (kc_max = KC), 3x3 filters only
+#define CT_H2_VARIANT(NAME, DT, WM, WN, RM, RN, KC)                                              \
+    {NAME, DT, 32, 32, 16, WM, WN, 1, RM, RN, KC, &h2_lds_bytes<WM, WN, RM, RN, KC, 9>,          \
+     &h2_launch<DT, WM, WN, RM, RN, KC, 9>, &h2_aux_bytes<WM, WN, RM, RN, KC, 9>}
+
+const IgemmVariant kH2Variants[] = {
+    CT_H2_VARIANT("h2f16_m128n256_w2x4_r2x2_kc16", DT_F16, 2, 4, 2, 2, 16),
+    CT_H2_VARIANT("h2f16_m128n128_w2x2_r2x2_kc16", DT_F16, 2, 2, 2, 2, 16),
+    CT_H2_VARIANT("h2f16_m128n256_w2x2_r2x4_kc16", DT_F16, 2, 2, 2, 4, 16),
+    CT_H2_VARIANT("h2f16_m64n256_w1x4_r2x2_kc32", DT_F16, 1, 4, 2, 2, 32),
+    CT_H2_VARIANT("h2f16_m64n256_w1x4_r2x2_kc16", DT_F16, 1, 4, 2, 2, 16),
+    CT_H2_VARIANT("h2f16_m64n128_w1x2_r2x2_kc16", DT_F16, 1, 2, 2, 2, 16),
+    CT_H2_VARIANT("h2bf16_m128n256_w2x4_r2x2_kc16", DT_BF16, 2, 4, 2, 2, 16),
+    CT_H2_VARIANT("h2bf16_m128n128_w2x2_r2x2_kc16", DT_BF16, 2, 2, 2, 2, 16),
+};
+
+}  // namespace
+
+const IgemmVariant* igemm_f16v2_variants(int* count) {
+    *count = (int)(sizeof(kH2Variants) / sizeof(kH2Variants[0]));
+    return kH2Variants;
+}
+
+}  // namespace ct

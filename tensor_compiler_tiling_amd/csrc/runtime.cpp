@@ -147,11 +147,12 @@ const std::vector<Variant>& variants() {
             d.ig = nullptr;
             out.push_back(d);
         }
-        int n32 = 0, n16 = 0, nsk = 0, nsk16 = 0;
+        int n32 = 0, n16 = 0, nsk = 0, nsk16 = 0, nh2 = 0;
         const IgemmVariant* t32 = igemm_f32_variants(&n32);
         const IgemmVariant* tsk = igemm_f32_sk_variants(&nsk);
         const IgemmVariant* tsk16 = igemm_f32_sk16_variants(&nsk16);
         const IgemmVariant* t16 = igemm_f16_variants(&n16);
+        const IgemmVariant* th2 = igemm_f16v2_variants(&nh2);
         auto add = [&](const IgemmVariant* t, int n) {
             for (int i = 0; i < n; ++i) {
                 Variant v{};
@@ -178,6 +179,7 @@ const std::vector<Variant>& variants() {
         add(tsk, nsk);
         add(tsk16, nsk16);
         add(t16, n16);
+        add(th2, nh2);
         return out;
     }();
     return v;
@@ -321,7 +323,7 @@ int window_rows(const Shape& s, int tile_n) {
 struct Resolved {
     const Variant* v;
     int tiles_m, tiles_n, R, lds;
-    long long grid, ws_bytes;
+    long long grid, ws_bytes, aux_bytes;
 };
 
 // Legality of a tile config for a shape; never launches anything.
@@ -361,6 +363,8 @@ bool legal(const Shape& s, const ct_tile_config& c, Resolved* out, std::string* 
     if (tiles_m * tiles_n > (1LL << 30) || grid > 0x7fffffffLL) return no("grid too large");
     const long long ws = c.split_k > 1 ? grid * v.desc.tile_m * v.desc.tile_n * 4LL : 0;
     if (ws > kMaxWorkspace) return no("split workspace too large");
+    const long long aux = v.ig->aux_bytes ? v.ig->aux_bytes(lp) : 0;
+    if (aux > kMaxWorkspace) return no("reordered filter too large");
     if (out) {
         out->v = &v;
         out->tiles_m = (int)tiles_m;
@@ -369,6 +373,7 @@ bool legal(const Shape& s, const ct_tile_config& c, Resolved* out, std::string* 
         out->lds = lds;
         out->grid = grid;
         out->ws_bytes = ws;
+        out->aux_bytes = aux;
     }
     return true;
 }
@@ -527,24 +532,27 @@ struct Workspace {
     long long ws_bytes = 0;
     unsigned* tickets = nullptr;
     long long n_tickets = 0;
+    void* aux = nullptr;  // a variant's own scratch (the reordered filter)
+    long long aux_bytes = 0;
 };
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int get_workspace(hipStream_t stream, long long ws_bytes, long long n_tickets, Workspace* out) {
+int get_workspace(hipStream_t stream, long long ws_bytes, long long n_tickets, long long aux_bytes,
+                  Workspace* out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lk(g_ws_mu);
     Workspace& w = g_ws[{dev, stream}];
-    if (w.ws_bytes < ws_bytes || w.n_tickets < n_tickets) {
+    if (w.ws_bytes < ws_bytes || w.n_tickets < n_tickets || w.aux_bytes < aux_bytes) {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         e = hipStreamIsCapturing(stream, &cs);
         if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
         if (cs != hipStreamCaptureStatusNone)
             return fail(CT_ERR_UNSUPPORTED,
-                        "the split workspace of this stream must grow, which cannot happen during "
+                        "the workspace of this stream must grow, which cannot happen during "
                         "stream capture: run the same convolution once on the stream first");
         // in-flight launches on this stream may still use the old buffers
         e = hipStreamSynchronize(stream);
@@ -573,6 +581,16 @@ int get_workspace(hipStream_t stream, long long ws_bytes, long long n_tickets, W
         e = hipDeviceSynchronize();
         if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
         w.n_tickets = n;
+    }
+    if (w.aux_bytes < aux_bytes) {
+        if (w.aux) (void)hipFree(w.aux);
+        w.aux = nullptr;
+        w.aux_bytes = 0;
+        const long long b = std::max<long long>(aux_bytes, 1 << 20);
+        e = hipMalloc(&w.aux, (size_t)b);
+        if (e != hipSuccess) return fail(CT_ERR_NO_MEMORY, "filter scratch of %lld bytes: %s", b,
+                                         hipGetErrorString(e));
+        w.aux_bytes = b;
     }
     *out = w;
     return CT_OK;
@@ -641,12 +659,16 @@ int launch_tiled(const Shape& s, const ct_tile_config& c, const void* x, const v
     p.R = r.R;
     int zst = zero_page(&p.zero);
     if (zst != CT_OK) return zst;
-    if (c.split_k > 1) {
+    if (c.split_k > 1 || r.aux_bytes > 0) {
         Workspace ws;
-        int st = get_workspace(stream, r.ws_bytes, (long long)r.tiles_m * r.tiles_n * kTicketStride, &ws);
+        const long long nt = c.split_k > 1 ? (long long)r.tiles_m * r.tiles_n * kTicketStride : 0;
+        int st = get_workspace(stream, r.ws_bytes, nt, r.aux_bytes, &ws);
         if (st != CT_OK) return st;
-        p.ws = ws.ws;
-        p.tickets = ws.tickets;
+        if (c.split_k > 1) {
+            p.ws = ws.ws;
+            p.tickets = ws.tickets;
+        }
+        p.aux = ws.aux;
     }
     hipError_t e = r.v->ig->launch(p, stream);
     if (e != hipSuccess) return hip_fail(e, r.v->desc.name);
@@ -898,6 +920,7 @@ int ct_release(void) {
         (void)hipStreamSynchronize(kv.first.second);
         if (kv.second.ws) (void)hipFree(kv.second.ws);
         if (kv.second.tickets) (void)hipFree(kv.second.tickets);
+        if (kv.second.aux) (void)hipFree(kv.second.aux);
         (void)hipSetDevice(dev);
     }
     g_ws.clear();

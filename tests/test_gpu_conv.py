@@ -186,9 +186,23 @@ def test_epilogue_closed_form_zero_weights():
     assert np.all(got == got[:, :, :1, :1])
 
 
+HALF_SMALL = [
+    # N, CI, H, W, CO, KH, KW, stride, pad: odd width (1-pixel window runs),
+    # a partial channel stage and windows that cross images
+    ("half_small", 130, 3, 24, 11, 9, 40, 3, 3, 1, 1),
+    # width 16: 8-pixel runs; 32 channels: whole stages
+    ("half_w16", 131, 2, 32, 16, 16, 48, 3, 3, 1, 1),
+    # width 14: 2-pixel runs, 40 channels (a partial stage), 70 filters
+    ("half_w14", 132, 2, 40, 10, 14, 70, 3, 3, 1, 1),
+    # width 12, stride 2: 4-pixel runs
+    ("half_w12_s2", 133, 1, 16, 12, 12, 32, 3, 3, 2, 1),
+]
+
+
+@pytest.mark.parametrize("shape", HALF_SMALL, ids=lambda t: t[0])
 @pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
-def test_half_precision_small(dtype):
-    w = wl.ConvWorkload("half_small", 130, 3, 24, 11, 9, 40, 3, 3, 1, 1, dtype)
+def test_half_precision_small(dtype, shape):
+    w = wl.ConvWorkload(*shape, dtype)
     inp = wl.conv_inputs(w)
     y, a = oracle_full(w, inp)
     assert_conv_close(run(w, inp), y, a, dtype, f"{dtype} default")
@@ -197,8 +211,11 @@ def test_half_precision_small(dtype):
         assert_conv_close(run(w, inp, config=cfg), y, a, dtype,
                           f"{dtype} {ct.variants()[cfg.variant]['name']} S={cfg.split_k}")
     ints = wl.small_int_inputs(w)
-    yi, _ = O.conv2d_nchw(ints["x"].astype(np.float64), ints["w"].astype(np.float64), 1, 1)
+    yi, _ = O.conv2d_nchw(ints["x"].astype(np.float64), ints["w"].astype(np.float64), w.stride,
+                          w.pad)
     assert np.array_equal(run(w, ints), yi)
+    for cfg in legal_configs(w):
+        assert np.array_equal(run(w, ints, config=cfg), yi), ct.variants()[cfg.variant]["name"]
 
 
 @pytest.mark.parametrize("name", ["f16_n64_c256_14x14_k3", "f16_n128_c128to256_32x32_k3_epi"])
@@ -229,3 +246,28 @@ def test_half_precision_full_size_sampled(name):
         rel = float((np.abs(f - ref) / ref).max())
         say(f"  fused sampled max rel err = {rel:.3e}")
         assert rel <= 1e-2 * S + 1e-5
+
+
+@pytest.mark.parametrize("name", ["f16_n64_c256_14x14_k3", "f16_n128_c128to256_32x32_k3_epi"])
+def test_half_precision_full_size_every_variant(name):
+    """Full-size half-precision workloads through every variant (one split
+    factor each: the smallest legal one), on sampled outputs."""
+    w = wl.CONV_WORKLOADS[name]
+    inp = wl.conv_inputs(w)
+    idx = sample_points((w.N, w.CO, w.OH, w.OW), 2000, 6)
+    yp, ap = O.conv2d_points(inp["x"].astype(np.float64), inp["w"].astype(np.float64), w.stride,
+                             w.pad, idx)
+    S = float(ap.max())
+    chosen = {}
+    for cfg in legal_configs(w, epilogue=ct.CT_EPI_NONE):
+        v = cfg.variant
+        if v not in chosen or (cfg.split_k, cfg.stages) < (chosen[v].split_k, chosen[v].stages):
+            chosen[v] = cfg
+    say(f"[conv-f16-variants] {name}: {len(chosen)} variants")
+    assert chosen
+    for cfg in chosen.values():
+        got = run(w, inp, config=cfg, epilogue=ct.CT_EPI_NONE)
+        g = got[idx[:, 0], idx[:, 1], idx[:, 2], idx[:, 3]]
+        err = float(np.abs(g - yp).max())
+        assert np.all(np.isfinite(g)) and err <= 1e-2 * S, (ct.variants()[cfg.variant]["name"],
+                                                             cfg.split_k, cfg.stages, err)
