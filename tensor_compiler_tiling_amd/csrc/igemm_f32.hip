@@ -122,7 +122,7 @@ __global__ __launch_bounds__(WM * WN * WK * 64) void igemm_f32_kernel(ConvParams
     constexpr int TILE_M = Cfg::TILE_M, TILE_N = Cfg::TILE_N, THREADS = Cfg::THREADS;
     constexpr int NWAVES = THREADS / 64;
 
-    extern __shared__ float lds[];
+    extern __shared__ __align__(16) float lds[];  // 16-byte LDS accesses need a 16-byte aligned base
     __shared__ int s_last;
 
     const int tid = threadIdx.x;

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kSkThreads) void igemm_f32_sk_kernel(ConvParams p) 
     constexpr int KS = 8 * KL;
     constexpr int KT = KL / 4;
     static_assert(KL % 4 == 0, "KL must be a multiple of 4");
-    extern __shared__ float lds[];
+    extern __shared__ __align__(16) float lds[];  // 16-byte LDS accesses need a 16-byte aligned base
     __shared__ int s_last;
 
     const int tid = threadIdx.x;

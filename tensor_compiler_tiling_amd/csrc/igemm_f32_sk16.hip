@@ -13,9 +13,10 @@
 //
 // Workgroup: NW waves, tile 16 output channels x 64 pixels = four 16x16
 // blocks of v_mfma_f32_16x16x4_f32 per wave.  The waves split the stage's
-// reduction range: wave w owns k in [w*KPW, (w+1)*KPW), KPW = 16*KT, and at
+// reduction range: wave w owns k in [w*KPW, (w+1)*KPW), KPW = 4*KSTEP, and at
 // instruction step s the lane group g = lane/16 feeds
 //     k = w*KPW + 16*(s/4) + 4*g + s%4
+// (a last group of only 2 steps covers 8 values, g feeding 2g and 2g+1)
 // (any assignment of k to (step, lane group) is valid when A and B share
 // it), so a lane's A values for steps 4t..4t+3 are four consecutive floats
 // of its filter row: one 16-byte load from global memory per four steps.
@@ -93,14 +94,17 @@ __host__ __device__ inline Sk16Layout sk16_layout(int kc, int RWp, int KS, int N
 
 // Divisors in ConvParams: fd_wstr = OH*OW, fd_wp = Wp, fd_rwp = XCS,
 // fd_hp = Hp, fd_ow = OW, fd_t = KH*KW, fd_kw = KW, fd_w = W, fd_hw = H*W.
-template <int NW, int KT, bool STAGED>
+template <int NW, int KSTEP, bool STAGED>
 __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
     fetch_kernargs(p);
     constexpr int XE = 16;  // staged window words per thread
-    constexpr int KPW = 16 * KT;
+    static_assert(KSTEP % 2 == 0, "steps per wave come in pairs");
+    constexpr int KT = (KSTEP + 3) / 4;       // 4-step groups; the last may hold 2 steps
+    constexpr int LE = KSTEP - 4 * (KT - 1);  // steps of the last group: 2 or 4
+    constexpr int KPW = 4 * KSTEP;            // reduction values per wave
     constexpr int KS = NW * KPW;
     constexpr int NT = NW * 64;
-    extern __shared__ float lds[];
+    extern __shared__ __align__(16) float lds[];  // 16-byte LDS accesses need a 16-byte aligned base
     __shared__ int s_last;
 
     const int tid = threadIdx.x;
@@ -145,6 +149,8 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
 
     const int co_a = co0 + li;
     const int kw0 = wave * KPW + 4 * lg;  // k of step 0; step s adds 16*(s/4) + s%4
+    // a last group of 2 steps covers 8 values: lane group g takes 2g, 2g+1
+    const int kw_last = LE == 4 ? kw0 + 16 * (KT - 1) : wave * KPW + 16 * (KT - 1) + 2 * lg;
     const bool w_vec = ((p.K & 3) == 0) && ((reinterpret_cast<uintptr_t>(wg) & 15) == 0);
     const bool lane_offsets = xcs <= 64 * kChMax;
 
@@ -254,27 +260,38 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
             __builtin_amdgcn_sched_barrier(0);
         }
 
-        // (2) A: steps 4t..4t+3 = W[co_a][c0*T + kw0 + 16t + (0..3)]
+        // (2) A: steps 4t..4t+3 = W[co_a][c0*T + kw0 + 16t + (0..3)]; a last
+        // group of 2 steps = W[co_a][c0*T + kw_last + (0, 1)]
         floatx4 a4[KT];
         const float* wrow = wg + (long long)co_a * p.K + (long long)c0 * p.T + kw0;
         const bool row_ok = co_a < p.CO;
         // whole 16-byte groups only: every group is then all valid or all past
         // kvalid, and a group past it (or past CO) reads the zero block
         const bool vec_stage = STAGED || (w_vec && (((c0 * p.T) & 3) == 0) && ((kvalid & 3) == 0));
+        const float* wlast = wrow - kw0 + kw_last;
         if (vec_stage) {
 #pragma unroll
             for (int t = 0; t < KT; ++t) {
-                const int k = kw0 + 16 * t;
-                const float* src = (row_ok && k < kvalid) ? wrow + 16 * t : zero;
-                a4[t] = *reinterpret_cast<const floatx4*>(src);
+                if (t < KT - 1 || LE == 4) {
+                    const int k = kw0 + 16 * t;
+                    const float* src = (row_ok && k < kvalid) ? wrow + 16 * t : zero;
+                    a4[t] = *reinterpret_cast<const floatx4*>(src);
+                } else {
+                    const float* src = (row_ok && kw_last < kvalid) ? wlast : zero;
+                    const float2 v = *reinterpret_cast<const float2*>(src);
+                    a4[t] = floatx4{v.x, v.y, 0.0f, 0.0f};
+                }
             }
         } else if constexpr (!STAGED) {
 #pragma unroll
             for (int t = 0; t < KT; ++t)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int k = kw0 + 16 * t + e;
-                    a4[t][e] = (row_ok && k < kvalid) ? wrow[16 * t + e] : 0.0f;
+                    const bool last2 = t == KT - 1 && LE == 2;
+                    const int k = last2 ? kw_last + e : kw0 + 16 * t + e;
+                    a4[t][e] = (row_ok && k < kvalid && (!last2 || e < 2))
+                                   ? (last2 ? wlast[e] : wrow[16 * t + e])
+                                   : 0.0f;
                 }
         }
 
@@ -342,18 +359,28 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
         // past the data and the reads feed the instructions unmasked.
         int4 kt[KT];
 #pragma unroll
-        for (int t = 0; t < KT; ++t) kt[t] = *reinterpret_cast<const int4*>(ktab + kw0 + 16 * t);
+        for (int t = 0; t < KT; ++t) {
+            if (t < KT - 1 || LE == 4) {
+                kt[t] = *reinterpret_cast<const int4*>(ktab + kw0 + 16 * t);
+            } else {
+                const int2 v = *reinterpret_cast<const int2*>(ktab + kw_last);
+                kt[t] = int4{v.x, v.y, 0, 0};
+            }
+        }
         auto steps = [&](auto masked_tag) {
             constexpr bool MASKED = decltype(masked_tag)::value;
             float bcur[4][kNB], bnext[4][kNB];
             auto fetch = [&](int t, float (&b)[4][kNB]) {
+                const int ne = (t == KT - 1) ? LE : 4;
+                const int kb = (t == KT - 1) ? kw_last : kw0 + 16 * t;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
+                    if (e >= ne) break;
                     const int koff = e == 0 ? kt[t].x : e == 1 ? kt[t].y : e == 2 ? kt[t].z : kt[t].w;
 #pragma unroll
                     for (int nb = 0; nb < kNB; ++nb) {
                         const float v = Xs[pbase[nb] + koff];
-                        b[e][nb] = (!MASKED || kw0 + 16 * t + e < kvalid) ? v : 0.0f;
+                        b[e][nb] = (!MASKED || kb + e < kvalid) ? v : 0.0f;
                     }
                 }
             };
@@ -364,10 +391,12 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
                 // keep the next group's reads ahead of this group's instructions
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
+                for (int e = 0; e < 4; ++e) {
+                    if (e >= ((t == KT - 1) ? LE : 4)) break;
 #pragma unroll
                     for (int nb = 0; nb < kNB; ++nb)
                         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[t][e], bcur[e][nb], acc[nb], 0, 0, 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
                 if (t + 1 < KT) {
 #pragma unroll
@@ -468,9 +497,9 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
         __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int NW, int KT, bool STAGED>
+template <int NW, int KSTEP, bool STAGED>
 int sk16_lds_bytes(const ConvParams& p) {
-    constexpr int KS = NW * 16 * KT;
+    constexpr int KS = NW * 4 * KSTEP;
     if (p.kc * p.T > KS) return 1 << 30;  // the stage must fit the k lanes
     if (STAGED) {
         // one tile, one image, and its window reads every image row
@@ -486,7 +515,7 @@ int sk16_lds_bytes(const ConvParams& p) {
     return 4 * sk16_layout(p.kc, p.R * p.Wp, KS, NW).words;
 }
 
-template <int NW, int KT, bool STAGED>
+template <int NW, int KSTEP, bool STAGED>
 hipError_t sk16_launch(const ConvParams& p, hipStream_t stream) {
     if (STAGED) {
         const long long HW = (long long)p.H * p.W;
@@ -495,11 +524,11 @@ hipError_t sk16_launch(const ConvParams& p, hipStream_t stream) {
                              ((p.kc * HW) & 3) == 0 && ((p.CI * HW) & 3) == 0 &&
                              ((p.kc * p.T) & 3) == 0;
         // same tile config, same result: the direct-window form takes any layout
-        if (!aligned) return sk16_launch<NW, KT, false>(p, stream);
+        if (!aligned) return sk16_launch<NW, KSTEP, false>(p, stream);
     }
-    const int bytes = sk16_lds_bytes<NW, KT, STAGED>(p);
+    const int bytes = sk16_lds_bytes<NW, KSTEP, STAGED>(p);
     if (bytes > 163840 - 64) return hipErrorInvalidValue;
-    auto kern = igemm_f32_sk16_kernel<NW, KT, STAGED>;
+    auto kern = igemm_f32_sk16_kernel<NW, KSTEP, STAGED>;
     static std::atomic<int> lds_limit{65536};
     if (bytes > lds_limit.load(std::memory_order_relaxed)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -510,7 +539,7 @@ hipError_t sk16_launch(const ConvParams& p, hipStream_t stream) {
         }
         lds_limit.store(bytes, std::memory_order_relaxed);
     }
-    const Sk16Layout L = sk16_layout(p.kc, p.R * p.Wp, NW * 16 * KT, NW);
+    const Sk16Layout L = sk16_layout(p.kc, p.R * p.Wp, NW * 4 * KSTEP, NW);
     ConvParams q = p;
     q.fd_wstr = make_fastdiv((uint32_t)p.OHW);
     q.fd_wp = make_fastdiv((uint32_t)p.Wp);
@@ -523,23 +552,27 @@ hipError_t sk16_launch(const ConvParams& p, hipStream_t stream) {
     q.fd_hw = make_fastdiv((uint32_t)(p.H * p.W));
     const long long grid = (long long)p.tiles_m * p.tiles_n * p.S;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((igemm_f32_sk16_kernel<NW, KT, STAGED>), dim3((unsigned)grid), dim3(NW * 64),
+    hipLaunchKernelGGL((igemm_f32_sk16_kernel<NW, KSTEP, STAGED>), dim3((unsigned)grid), dim3(NW * 64),
                        bytes, stream, q);
     return hipGetLastError();
 }
 
-// descriptor: 16x16x4 instruction, waves 1 x 1 x NW (CO x P x K), reps 1 x 4
-#define CT_SK16_VARIANT(NAME, NW, KT, STAGED)                                              \
-    {NAME, DT_F32, 16, 16, 4, 1, 1, NW, 1, 4, NW * 16 * KT, &sk16_lds_bytes<NW, KT, STAGED>, \
-     &sk16_launch<NW, KT, STAGED>}
+// descriptor: 16x16x4 instruction, waves 1 x 1 x NW (CO x P x K), reps 1 x 4;
+// NW waves of KSTEP steps hold a stage of up to NW*4*KSTEP reduction values
+#define CT_SK16_VARIANT(NAME, NW, KSTEP, STAGED)                                                 \
+    {NAME, DT_F32, 16, 16, 4, 1, 1, NW, 1, 4, NW * 4 * KSTEP, &sk16_lds_bytes<NW, KSTEP, STAGED>, \
+     &sk16_launch<NW, KSTEP, STAGED>}
 
 const IgemmVariant kSk16Variants[] = {
-    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt9", 4, 9, false),
-    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt5", 4, 5, false),
-    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt3", 4, 3, false),
-    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt9", 4, 9, true),
-    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt5", 4, 5, true),
-    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt3", 4, 3, true),
+    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt9", 4, 36, false),
+    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt5", 4, 20, false),
+    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt3", 4, 12, false),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt9", 4, 36, true),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt5", 4, 20, true),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt3", 4, 12, true),
+    CT_SK16_VARIANT("f32sk16_m16n64_w8_s18", 8, 18, false),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w8_s18", 8, 18, true),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w8_s10", 8, 10, true),
 };
 
 }  // namespace
