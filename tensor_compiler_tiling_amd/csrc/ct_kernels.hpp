@@ -78,6 +78,7 @@ struct IgemmVariant {
 const IgemmVariant* igemm_f32_variants(int* count);
 const IgemmVariant* igemm_f32_sk_variants(int* count);
 const IgemmVariant* igemm_f32_sk16_variants(int* count);
+const IgemmVariant* igemm_f32_skc_variants(int* count);
 const IgemmVariant* igemm_f16_variants(int* count);
 const IgemmVariant* igemm_f16v2_variants(int* count);
 

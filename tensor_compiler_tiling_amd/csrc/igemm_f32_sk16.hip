@@ -154,6 +154,87 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
     const bool w_vec = ((p.K & 3) == 0) && ((reinterpret_cast<uintptr_t>(wg) & 15) == 0);
     const bool lane_offsets = xcs <= 64 * kChMax;
 
+    // ---- staged windows: the tile's image rows 0..H-1 of image 0 -----------
+    // (the host allows this form only for one tile per image whose window
+    // reads every image row, so a stage's data is kc*H*W contiguous floats)
+    const int wr0 = oy_first * p.stride;  // padded image row of window row 0
+    float xr[XE];
+    floatx4 a4[KT];
+    const bool row_ok = co_a < p.CO;
+    // Register loads of stage st: the window data (staged form: this thread's
+    // XE words, 16-byte groups in flat order) and then A, steps 4t..4t+3 =
+    // W[co_a][c0*T + kw0 + 16t + (0..3)] (a last group of 2 steps =
+    // W[co_a][c0*T + kw_last + (0, 1)]).  Issued before anything that waits,
+    // so the memory latency overlaps the set-up below.
+    auto issue_loads = [&](int st) {
+        const int c0 = (split * p.stages + st) * p.kc;
+        const int cvalid = min(p.kc, p.CI - c0);
+        const int kvalid = cvalid * p.T;
+        if constexpr (STAGED) {
+            // the launcher runs this form only with 16-byte aligned x and w and
+            // kc*H*W, CI*H*W, KH*KW*kc multiples of 4: every load below is a
+            // whole 16-byte group, issued unconditionally (past the end: the
+            // zero block)
+            const int E = cvalid * (int)HW;
+            const float* xblk = xg + (long long)c0 * HW;
+#pragma unroll
+            for (int j = 0; j < XE / 4; ++j) {
+                const int f = 4 * (j * NT + tid);
+                const float* src = f < E ? xblk + f : zero;
+                const floatx4 v = *reinterpret_cast<const floatx4*>(src);
+                xr[4 * j] = v[0];
+                xr[4 * j + 1] = v[1];
+                xr[4 * j + 2] = v[2];
+                xr[4 * j + 3] = v[3];
+            }
+            // window loads first in issue order: they retire first
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const float* wrow = wg + (long long)co_a * p.K + (long long)c0 * p.T + kw0;
+        // whole 16-byte groups only: every group is then all valid or all past
+        // kvalid, and a group past it (or past CO) reads the zero block
+        const bool vec_stage = STAGED || (w_vec && (((c0 * p.T) & 3) == 0) && ((kvalid & 3) == 0));
+        const float* wlast = wrow - kw0 + kw_last;
+        if (vec_stage) {
+#pragma unroll
+            for (int t = 0; t < KT; ++t) {
+                if (t < KT - 1 || LE == 4) {
+                    const int k = kw0 + 16 * t;
+                    const float* src = (row_ok && k < kvalid) ? wrow + 16 * t : zero;
+                    a4[t] = *reinterpret_cast<const floatx4*>(src);
+                } else {
+                    const float* src = (row_ok && kw_last < kvalid) ? wlast : zero;
+                    const float2 v = *reinterpret_cast<const float2*>(src);
+                    a4[t] = floatx4{v.x, v.y, 0.0f, 0.0f};
+                }
+            }
+        } else if constexpr (!STAGED) {
+#pragma unroll
+            for (int t = 0; t < KT; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool last2 = t == KT - 1 && LE == 2;
+                    const int k = last2 ? kw_last + e : kw0 + 16 * t + e;
+                    a4[t][e] = (row_ok && k < kvalid && (!last2 || e < 2))
+                                   ? (last2 ? wlast[e] : wrow[16 * t + e])
+                                   : 0.0f;
+                }
+        }
+    };
+    // k -> window offset of every k lane of a stage
+    auto build_ktab = [&]() {
+        for (int k = tid; k < KS; k += NT) {
+            const int c = (int)fdiv16((uint32_t)k, p.fd_t);
+            const int t = k - c * p.T;
+            const int ky = (int)fdiv16((uint32_t)t, p.fd_kw);
+            const int kx = t - ky * p.KW;
+            ktab[k] = (c < p.kc) ? c * xcs + ky * p.Wp + kx : 0;
+        }
+    };
+    // the first stage's register loads go out before any other set-up
+    if constexpr (STAGED) issue_loads(0);
+
+
     floatx4 acc[kNB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[nb] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -191,15 +272,13 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
         }
     }
 
-    // ---- staged windows: the tile's image rows 0..H-1 of image 0 -----------
-    // (the host allows this form only for one tile per image whose window
-    // reads every image row, so a stage's data is kc*H*W contiguous floats)
-    const int wr0 = oy_first * p.stride;  // padded image row of window row 0
     if constexpr (STAGED) {
-        // padding words are the same in every stage: zero the windows once
+        // padding words are the same in every stage: zero the windows once,
+        // and build the k table, while the first stage's loads are in flight
         floatx4* xz = reinterpret_cast<floatx4*>(Xs);
         for (int i = tid; i < L.x_words / 4; i += NT) xz[i] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-        __syncthreads();
+        build_ktab();
+        lds_barrier();
     }
     for (int st = 0; st < p.stages; ++st) {
         const int c0 = (split * p.stages + st) * p.kc;
@@ -207,31 +286,21 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
         const int cvalid = min(p.kc, p.CI - c0);
         const int kvalid = cvalid * p.T;
 
-        if (st > 0) lds_barrier();  // the previous stage's windows are consumed
+        if (st > 0) {
+            // the previous stage's registers are free: load this stage's, then
+            // wait until every wave is done reading the previous windows
+            if constexpr (STAGED) issue_loads(st);
+            lds_barrier();
+        }
+        if constexpr (!STAGED) issue_loads(st);
 
-        // (1) staged windows: this thread's XE data words into registers
-        const int E = cvalid * (int)HW;
-        const float* xblk = xg + (long long)c0 * HW;
-        float xr[XE];
-        // the launcher runs this form only with 16-byte aligned x and w and
-        // kc*H*W, CI*H*W, KH*KW*kc multiples of 4: every load below is a whole
-        // 16-byte group, issued unconditionally (past the end: the zero block)
-        auto x_load = [&](int f0) {
+        if constexpr (STAGED) {
+            // (3) window data into LDS from the registers loaded above (the
+            // host allows this form only when a stage's data fits NT*XE words)
+            const int E = cvalid * (int)HW;
 #pragma unroll
             for (int j = 0; j < XE / 4; ++j) {
-                const int f = f0 + 4 * (j * NT + tid);
-                const float* src = f < E ? xblk + f : zero;
-                const floatx4 v = *reinterpret_cast<const floatx4*>(src);
-                xr[4 * j] = v[0];
-                xr[4 * j + 1] = v[1];
-                xr[4 * j + 2] = v[2];
-                xr[4 * j + 3] = v[3];
-            }
-        };
-        auto x_store = [&](int f0) {
-#pragma unroll
-            for (int j = 0; j < XE / 4; ++j) {
-                const int f = f0 + 4 * (j * NT + tid);
+                const int f = 4 * (j * NT + tid);
                 if (f < E) {
                     // four consecutive words: step the column, wrapping rows
                     // and channels
@@ -253,52 +322,6 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
                     }
                 }
             }
-        };
-        if constexpr (STAGED) {
-            x_load(0);
-            // window loads first in issue order: they retire first
-            __builtin_amdgcn_sched_barrier(0);
-        }
-
-        // (2) A: steps 4t..4t+3 = W[co_a][c0*T + kw0 + 16t + (0..3)]; a last
-        // group of 2 steps = W[co_a][c0*T + kw_last + (0, 1)]
-        floatx4 a4[KT];
-        const float* wrow = wg + (long long)co_a * p.K + (long long)c0 * p.T + kw0;
-        const bool row_ok = co_a < p.CO;
-        // whole 16-byte groups only: every group is then all valid or all past
-        // kvalid, and a group past it (or past CO) reads the zero block
-        const bool vec_stage = STAGED || (w_vec && (((c0 * p.T) & 3) == 0) && ((kvalid & 3) == 0));
-        const float* wlast = wrow - kw0 + kw_last;
-        if (vec_stage) {
-#pragma unroll
-            for (int t = 0; t < KT; ++t) {
-                if (t < KT - 1 || LE == 4) {
-                    const int k = kw0 + 16 * t;
-                    const float* src = (row_ok && k < kvalid) ? wrow + 16 * t : zero;
-                    a4[t] = *reinterpret_cast<const floatx4*>(src);
-                } else {
-                    const float* src = (row_ok && kw_last < kvalid) ? wlast : zero;
-                    const float2 v = *reinterpret_cast<const float2*>(src);
-                    a4[t] = floatx4{v.x, v.y, 0.0f, 0.0f};
-                }
-            }
-        } else if constexpr (!STAGED) {
-#pragma unroll
-            for (int t = 0; t < KT; ++t)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool last2 = t == KT - 1 && LE == 2;
-                    const int k = last2 ? kw_last + e : kw0 + 16 * t + e;
-                    a4[t][e] = (row_ok && k < kvalid && (!last2 || e < 2))
-                                   ? (last2 ? wlast[e] : wrow[16 * t + e])
-                                   : 0.0f;
-                }
-        }
-
-        if constexpr (STAGED) {
-            // (3) window data into LDS from the registers loaded above (the
-            // host allows this form only when a stage's data fits NT*XE words)
-            x_store(0);
         } else {
             // (3) zero-padded windows of channels c0 .. c0+cvalid, straight to LDS
             if (lane_offsets) {
@@ -332,16 +355,8 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
                     __builtin_amdgcn_global_load_lds((glb_void_t*)src, (lds_void_t*)(Xs + ch * 64), 4, 0, 0);
                 }
             }
-        }
-        // (4) k -> window offset, once, while the loads are in flight
-        if (st == 0) {
-            for (int k = tid; k < KS; k += NT) {
-                const int c = (int)fdiv16((uint32_t)k, p.fd_t);
-                const int t = k - c * p.T;
-                const int ky = (int)fdiv16((uint32_t)t, p.fd_kw);
-                const int kx = t - ky * p.KW;
-                ktab[k] = (c < p.kc) ? c * xcs + ky * p.Wp + kx : 0;
-            }
+            // (4) k -> window offset, once, while the loads are in flight
+            if (st == 0) build_ktab();
         }
         // the windows and the k table are complete and visible to every wave;
         // direct-to-LDS loads are waited for here, register loads by the

@@ -136,6 +136,71 @@ def test_ones_count_valid_taps():
     assert np.array_equal(got[0], np.broadcast_to(512 * exp, (512, 7, 7)))
 
 
+# Layers with the compiled geometries of the 49-pixel split-K kernels
+# ("f32skc*": 7x7 stride 1 and 14x14 stride 2, 3x3, pad 1), at output-channel
+# counts that leave a partial 16-row tile.
+SKC_LAYERS = [
+    wl.ConvWorkload("skc_7x7_ci64_co40", 111, 1, 64, 7, 7, 40, 3, 3, 1, 1),
+    wl.ConvWorkload("skc_14x14s2_ci64_co24", 112, 1, 64, 14, 14, 24, 3, 3, 2, 1),
+]
+
+
+def _skc_configs(w):
+    return [c for c in legal_configs(w) if ct.variants()[c.variant]["name"].startswith("f32skc")]
+
+
+@pytest.mark.parametrize("misaligned", [False, True], ids=["aligned", "x_offset_4B"])
+@pytest.mark.parametrize("epi", [ct.CT_EPI_NONE, ct.CT_EPI_BIAS, ct.CT_EPI_EXP_BIAS_RSQRT])
+@pytest.mark.parametrize("w", SKC_LAYERS, ids=lambda w: w.name)
+def test_shape_specialised_split_k(w, epi, misaligned):
+    """Every legal config of the shape-specialised kernels against the oracle:
+    conv gate, epilogue gates, and an input that is not 16-byte aligned (the
+    kernels then load the window word by word)."""
+    w = w.with_(epilogue=epi)
+    cfgs = _skc_configs(w)
+    say(f"[conv-skc] {w.name} epi={epi} misaligned={misaligned}: {len(cfgs)} configs")
+    assert cfgs
+    inp = wl.conv_inputs(w)
+    y, a = oracle_full(w, inp)
+    ref = y if epi == ct.CT_EPI_NONE else O.channel_epilogue(
+        y, epi, inp["bias"].astype(np.float64), inp["var"].astype(np.float64), 1e-5)
+    S = float(a.max())
+    xd = to_dev(inp["x"], w.dtype)
+    if misaligned:
+        buf = torch.empty(xd.numel() + 1, dtype=xd.dtype, device=DEV)
+        buf[1:].copy_(xd.reshape(-1))
+        xd = buf[1:].view(xd.shape)
+        assert xd.data_ptr() % 16 != 0
+    k = to_dev(inp["w"], w.dtype)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    v = torch.from_numpy(inp["var"]).to(DEV)
+    for cfg in cfgs:
+        got = ct.conv2d(xd, k, w.stride, w.pad, epi, b, v, 1e-5, config=cfg)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy().astype(np.float64)
+        what = (ct.variants()[cfg.variant]["name"], cfg.split_k, cfg.stages, cfg.kc)
+        assert np.all(np.isfinite(got)), what
+        if epi == ct.CT_EPI_EXP_BIAS_RSQRT:
+            rel = float((np.abs(got - ref) / np.abs(ref)).max())
+            assert rel <= 1e-4 * S + 1e-5, (what, rel)
+        else:
+            assert float(np.abs(got - ref).max()) <= 1e-4 * S, what
+
+
+@pytest.mark.parametrize("w", SKC_LAYERS + [wl.CONV_WORKLOADS["resnet_final_c512_7x7_k3"],
+                                            wl.CONV_WORKLOADS["r18_c256to512_14x14_k3s2"]],
+                         ids=lambda w: w.name)
+def test_shape_specialised_integers_bit_exact(w):
+    inp = wl.small_int_inputs(w)
+    y, _ = O.conv2d_nchw(inp["x"].astype(np.float64), inp["w"].astype(np.float64), w.stride, w.pad)
+    cfgs = _skc_configs(w)
+    say(f"[conv-skc-int] {w.name}: {len(cfgs)} configs")
+    assert cfgs
+    for cfg in cfgs:
+        assert np.array_equal(run(w, inp, config=cfg), y), (ct.variants()[cfg.variant]["name"],
+                                                            cfg.split_k, cfg.stages, cfg.kc)
+
+
 def test_split_reduction_is_deterministic():
     w = wl.CONV_WORKLOADS["resnet_final_c512_7x7_k3"]
     inp = wl.conv_inputs(w)
