@@ -72,6 +72,10 @@ struct IgemmVariant {
     hipError_t (*launch)(const ConvParams& p, hipStream_t stream);
     // bytes of ConvParams::aux the launch needs (null: none)
     long long (*aux_bytes)(const ConvParams& p);
+    // nonzero: the variant keeps each tile's split reduction inside one XCD,
+    // relying on workgroup b running on XCD b % 8; legal only where the
+    // runtime has observed that placement
+    int xcd_local;
 };
 
 // Kernel-file registries.
@@ -92,6 +96,9 @@ hipError_t launch_bcast_channel(const float* var, void* out, int N, int C, int H
                                 int out_dtype, hipStream_t stream);
 hipError_t launch_bcast_flat(const float* var, void* out, int N, int C, int HW,
                              int out_dtype, hipStream_t stream);
+
+// out[b] = the XCD that workgroup b of a `blocks`-workgroup launch ran on.
+hipError_t launch_xcc_probe(int* out, int blocks, hipStream_t stream);
 
 // Deterministic device fill used by the tuner's scratch inputs:
 // v[i] = lo + (hi - lo) * u(i, seed), u a counter-based hash in [0, 1).

@@ -36,6 +36,17 @@
 // to arrive sums the S partials in split order 0..S-1 (run-to-run
 // identical), applies the epilogue and stores y.  Workgroup b handles split
 // b % S of output-channel tile b / S.
+//
+// XCD-local form (XL).  Each round trip of that protocol at device scope --
+// the coherent partial store, the ticket, the reducer's loads -- goes past
+// the L2 of the workgroup's XCD and costs about half a microsecond.  On an
+// MI355X workgroup b runs on XCD b % 8, and each XCD's L2 is the coherence
+// point of its CUs.  The XL form gives all S workgroups of a tile the same
+// b % 8 (tile = b%8 + 8*((b/8)/S), split = (b/8) % S), so the protocol runs
+// through that one L2: plain stores, a workgroup-scope atomic (executed in
+// L2), loads that skip the CU's L1.  Kernel boundaries write the L2 back.
+// The runtime enables XL variants only on a device where a probe launch
+// has observed the b % 8 placement.
 #include "ct_device.hpp"
 #include "igemm_common.hpp"
 
@@ -50,6 +61,7 @@ typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 
 constexpr int kBufWord3 = 0x00020000;  // raw buffer, 32-bit elements
 constexpr int kCoherent = 16;          // cache policy: device-coherent (sc1)
+constexpr int kSkipL1 = 1;             // cache policy: sc0, the load misses the CU's L1
 constexpr int kRowsM = 16;             // output channels per tile
 constexpr int kRS = 52;                // reduction / partial row: 49 columns, 16-byte rows
 constexpr int kSlab = kRowsM * kRS;    // floats per partial tile
@@ -101,7 +113,8 @@ struct SkcParams {
     const float* var;
     float eps;
     int CI, CO, S, stages, epilogue;
-    int pad_[2];
+    int tiles;  // output-channel tiles
+    int pad_;
 };
 static_assert(sizeof(SkcParams) <= 128, "two kernel-argument lines");
 
@@ -128,7 +141,8 @@ struct SkcCfg {
 };
 
 // XV: x is 16-byte aligned, so the window loads are 16-byte loads.
-template <class SH, int NW, int CPL, bool XV>
+// XL: XCD-local split reduction (see above).
+template <class SH, int NW, int CPL, bool XV, bool XL>
 __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
     using C = SkcCfg<SH, NW, CPL>;
     constexpr int NT = C::NT, KC = C::KC, KSTEP = C::KSTEP, XE = C::XE, NB = C::NB, D = C::D;
@@ -141,8 +155,17 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
     const int wave = tid >> 6;
     const int li = lane & 15;
     const int lg = lane >> 4;
-    const int tile = blockIdx.x / p.S;
-    const int split = blockIdx.x - tile * p.S;
+    int tile, split;
+    if constexpr (XL) {
+        const int idx = blockIdx.x >> 3;
+        const int q = idx / p.S;
+        tile = (blockIdx.x & 7) + 8 * q;
+        split = idx - q * p.S;
+        if (tile >= p.tiles) return;  // the last XCD rounds may be short
+    } else {
+        tile = blockIdx.x / p.S;
+        split = blockIdx.x - tile * p.S;
+    }
     const int co0 = tile * kRowsM;
     const int co_a = co0 + li;
     const bool row_ok = co_a < p.CO;
@@ -328,13 +351,15 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
         v.y = __float_as_uint(sum[1]);
         v.z = __float_as_uint(sum[2]);
         v.w = __float_as_uint(sum[3]);
-        __builtin_amdgcn_raw_buffer_store_b128(v, prs, (split * kSlab + fo) * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b128(v, prs, (split * kSlab + fo) * 4, 0, XL ? 0 : kCoherent);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial store is complete
     __syncthreads();
     if (tid == 0) {
-        const unsigned old = __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned old = XL ? __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_WORKGROUP)
+                                : __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == (unsigned)(p.S - 1)) ? 1 : 0;
     }
     __syncthreads();
@@ -349,7 +374,8 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
 #pragma unroll
             for (int j = 0; j < SB; ++j)
                 v[j] = (s0 + j < p.S) ? __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                       prs, ((s0 + j) * kSlab + fo) * 4, 0, kCoherent))
+                                                                       prs, ((s0 + j) * kSlab + fo) * 4, 0,
+                                                                       XL ? kSkipL1 : kCoherent))
                                       : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int j = 0; j < SB; ++j)
@@ -357,11 +383,15 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
         }
         store_out(tot);
     }
-    if (tid == 0)
-        __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        if constexpr (XL)
+            __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        else
+            __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
-template <class SH, int NW, int CPL, bool XV = true>
+template <class SH, int NW, int CPL, bool XL>
 int skc_lds_bytes(const ConvParams& p) {
     using C = SkcCfg<SH, NW, CPL>;
     if (p.N != 1 || p.H != SH::H || p.W != SH::W || p.KH != SH::KH || p.KW != SH::KW ||
@@ -374,13 +404,13 @@ int skc_lds_bytes(const ConvParams& p) {
     return 4 * C::WORDS;
 }
 
-template <class SH, int NW, int CPL>
+template <class SH, int NW, int CPL, bool XL>
 hipError_t skc_launch(const ConvParams& p, hipStream_t stream) {
     using C = SkcCfg<SH, NW, CPL>;
-    const int bytes = skc_lds_bytes<SH, NW, CPL>(p);
+    const int bytes = skc_lds_bytes<SH, NW, CPL, XL>(p);
     if (bytes > 163840 - 64) return hipErrorInvalidValue;
     const bool xv = (reinterpret_cast<uintptr_t>(p.x) & 15) == 0;
-    auto kern = xv ? igemm_f32_skc_kernel<SH, NW, CPL, true> : igemm_f32_skc_kernel<SH, NW, CPL, false>;
+    auto kern = xv ? igemm_f32_skc_kernel<SH, NW, CPL, true, XL> : igemm_f32_skc_kernel<SH, NW, CPL, false, XL>;
     static std::atomic<int> lds_limit[2] = {65536, 65536};
     if (bytes > lds_limit[xv].load(std::memory_order_relaxed)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -403,7 +433,8 @@ hipError_t skc_launch(const ConvParams& p, hipStream_t stream) {
     q.S = p.S;
     q.stages = p.stages;
     q.epilogue = p.epilogue;
-    const long long grid = (long long)p.tiles_m * p.tiles_n * p.S;
+    q.tiles = p.tiles_m;  // one column tile: the whole output
+    const long long grid = XL ? 8LL * ((p.tiles_m + 7) / 8) * p.S : (long long)p.tiles_m * p.tiles_n * p.S;
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), bytes, stream, q);
     return hipGetLastError();
@@ -414,17 +445,22 @@ using Layer14s2 = LayerShape<14, 14, 3, 3, 2, 1>;  // 14x14 -> 7x7, 3x3, stride 
 
 // descriptor: 16x16x4 instruction, waves 1 x 1 x NW (CO x P x K), tile 16 x 64
 // (49 columns used), a stage of exactly 4*NW*CPL channels
-#define CT_SKC_VARIANT(NAME, SH, NW, CPL)                                                              \
-    {NAME, DT_F32, 16, 16, 4, 1, 1, NW, 1, 4, 4 * NW * CPL, &skc_lds_bytes<SH, NW, CPL>, \
-     &skc_launch<SH, NW, CPL>, nullptr}
+#define CT_SKC_VARIANT(NAME, SH, NW, CPL, XL)                                                 \
+    {NAME, DT_F32, 16, 16, 4, 1, 1, NW, 1, 4, 4 * NW * CPL, &skc_lds_bytes<SH, NW, CPL, XL>, \
+     &skc_launch<SH, NW, CPL, XL>, nullptr, XL}
 
 const IgemmVariant kSkcVariants[] = {
-    CT_SKC_VARIANT("f32skc7_w8_c2", Layer7s1, 8, 2),
-    CT_SKC_VARIANT("f32skc7_w4_c2", Layer7s1, 4, 2),
-    CT_SKC_VARIANT("f32skc7_w4_c4", Layer7s1, 4, 4),
-    CT_SKC_VARIANT("f32skc7_w8_c1", Layer7s1, 8, 1),
-    CT_SKC_VARIANT("f32skc14s2_w8_c1", Layer14s2, 8, 1),
-    CT_SKC_VARIANT("f32skc14s2_w4_c2", Layer14s2, 4, 2),
+    CT_SKC_VARIANT("f32skc7_w8_c2", Layer7s1, 8, 2, false),
+    CT_SKC_VARIANT("f32skc7_w4_c2", Layer7s1, 4, 2, false),
+    CT_SKC_VARIANT("f32skc7_w4_c4", Layer7s1, 4, 4, false),
+    CT_SKC_VARIANT("f32skc7_w8_c1", Layer7s1, 8, 1, false),
+    CT_SKC_VARIANT("f32skc14s2_w8_c1", Layer14s2, 8, 1, false),
+    CT_SKC_VARIANT("f32skc14s2_w4_c2", Layer14s2, 4, 2, false),
+    CT_SKC_VARIANT("f32skc7x_w8_c2", Layer7s1, 8, 2, true),
+    CT_SKC_VARIANT("f32skc7x_w4_c2", Layer7s1, 4, 2, true),
+    CT_SKC_VARIANT("f32skc7x_w8_c1", Layer7s1, 8, 1, true),
+    CT_SKC_VARIANT("f32skc14s2x_w8_c1", Layer14s2, 8, 1, true),
+    CT_SKC_VARIANT("f32skc14s2x_w4_c2", Layer14s2, 4, 2, true),
 };
 
 }  // namespace

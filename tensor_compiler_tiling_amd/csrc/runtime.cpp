@@ -328,7 +328,39 @@ struct Resolved {
     long long grid, ws_bytes, aux_bytes;
 };
 
-// Legality of a tile config for a shape; never launches anything.
+// Whether workgroup b of a launch runs on XCD b % 8 on the current device:
+// observed once per device with a probe launch of 4096 workgroups (false
+// when there is no device or the probe fails).
+bool xcd_round_robin() {
+    static std::mutex mu;
+    static std::map<int, bool> seen;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = seen.find(dev);
+    if (it != seen.end()) return it->second;
+    constexpr int kBlocks = 4096;
+    bool ok = false;
+    int* d = nullptr;
+    if (hipMalloc((void**)&d, kBlocks * sizeof(int)) == hipSuccess) {
+        std::vector<int> h(kBlocks, -1);
+        if (launch_xcc_probe(d, kBlocks, nullptr) == hipSuccess && hipDeviceSynchronize() == hipSuccess &&
+            hipMemcpy(h.data(), d, kBlocks * sizeof(int), hipMemcpyDeviceToHost) == hipSuccess) {
+            ok = true;
+            for (int b = 0; b < kBlocks; ++b) ok = ok && h[b] == b % 8;
+        }
+        (void)hipFree(d);
+    }
+    (void)hipGetLastError();
+    seen[dev] = ok;
+    return ok;
+}
+
+// Legality of a tile config for a shape; launches nothing except, once per
+// device, the workgroup-placement probe of XCD-local variants.
 bool legal(const Shape& s, const ct_tile_config& c, Resolved* out, std::string* why) {
     const auto& vs = variants();
     auto no = [&](const char* m) {
@@ -367,6 +399,8 @@ bool legal(const Shape& s, const ct_tile_config& c, Resolved* out, std::string* 
     if (ws > kMaxWorkspace) return no("split workspace too large");
     const long long aux = v.ig->aux_bytes ? v.ig->aux_bytes(lp) : 0;
     if (aux > kMaxWorkspace) return no("reordered filter too large");
+    if (v.ig->xcd_local && !xcd_round_robin())
+        return no("workgroups are not placed round-robin over 8 XCDs on this device");
     if (out) {
         out->v = &v;
         out->tiles_m = (int)tiles_m;
@@ -711,13 +745,20 @@ bool default_config(const Shape& s, ct_tile_config* out) {
 
 // The config fwd uses: cached winner, else default; variant -1 = direct.
 ct_tile_config choose(const Shape& s, int* from_cache) {
+    ct_tile_config c_cached{};
+    bool have = false;
     {
         std::lock_guard<std::mutex> lk(g_cache_mu);
         auto it = g_cache.find(s.key());
         if (it != g_cache.end()) {
-            if (from_cache) *from_cache = 1;
-            return it->second.cfg;
+            c_cached = it->second.cfg;
+            have = true;
         }
+    }
+    // a cached config may name a variant this device cannot run
+    if (have && legal(s, c_cached, nullptr, nullptr)) {
+        if (from_cache) *from_cache = 1;
+        return c_cached;
     }
     if (from_cache) *from_cache = 0;
     ct_tile_config c{};

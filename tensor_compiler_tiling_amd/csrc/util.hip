@@ -50,7 +50,20 @@ __global__ __launch_bounds__(256) void compare_kernel(const float* a, const floa
     if (local) atomicAdd(bad, local);
 }
 
+// Which XCD (accelerator complex die) each workgroup ran on: the XCC_ID
+// hardware register (id 20), bits 3:0.
+__global__ __launch_bounds__(64) void xcc_probe_kernel(int* out) {
+    if (threadIdx.x == 0) out[blockIdx.x] = (int)(__builtin_amdgcn_s_getreg(20 | (3 << 11)) & 15);
+}
+
 }  // namespace
+
+hipError_t launch_xcc_probe(int* out, int blocks, hipStream_t stream) {
+    if (blocks < 1) return hipErrorInvalidValue;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(xcc_probe_kernel, dim3((unsigned)blocks), dim3(64), 0, stream, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_fill_uniform(void* dst, long long n, int dtype, float lo, float hi,
                                unsigned seed, hipStream_t stream) {

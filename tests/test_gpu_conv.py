@@ -201,6 +201,53 @@ def test_shape_specialised_integers_bit_exact(w):
                                                             cfg.split_k, cfg.stages, cfg.kc)
 
 
+def test_xcd_local_variants_enabled():
+    """The XCD-local split-K variants are legal on this device only if the
+    runtime's placement probe saw workgroup b run on XCD b % 8."""
+    w = wl.CONV_WORKLOADS["resnet_final_c512_7x7_k3"]
+    names = {ct.variants()[c.variant]["name"] for c in legal_configs(w)}
+    xl = sorted(n for n in names if n.startswith("f32skc7x_"))
+    say(f"[conv-xcd-local] legal XCD-local variants: {xl}")
+    assert xl, "placement probe did not observe round-robin XCD placement"
+
+
+def test_split_reduction_interleaved_configs():
+    """Back-to-back launches on one stream of the shape-specialised split-K
+    kernels with split counts that change from launch to launch, interleaved
+    with the other split-K kernels that share the stream's tickets and
+    workspace: each result is bit-identical to the first run of its config,
+    and the first runs match the oracle."""
+    w = wl.CONV_WORKLOADS["resnet_final_c512_7x7_k3"]
+    inp = wl.conv_inputs(w)
+    y, a = oracle_full(w, inp)
+    x = to_dev(inp["x"], w.dtype)
+    k = to_dev(inp["w"], w.dtype)
+    cfgs = [c for c in legal_configs(w) if c.split_k > 1]
+    skc = [c for c in cfgs if ct.variants()[c.variant]["name"].startswith("f32skc")]
+    other = [c for c in cfgs if not ct.variants()[c.variant]["name"].startswith("f32skc")][:4]
+    assert len({c.split_k for c in skc}) > 1 and other
+    order = []
+    for rep in range(3):
+        for i, c in enumerate(skc):
+            order.append(c)
+            if i % 2 == rep % 2:
+                order.append(other[(i + rep) % len(other)])
+    first = {}
+    outs = []
+    for c in order:
+        outs.append((c, ct.conv2d(x, k, 1, 1, config=c)))
+    torch.cuda.synchronize()
+    for c, out in outs:
+        key = (c.variant, c.split_k, c.stages, c.kc)
+        if key not in first:
+            first[key] = out
+            err = float(np.abs(out.cpu().numpy().astype(np.float64) - y).max())
+            assert err <= 1e-4 * float(a.max()), (ct.variants()[c.variant]["name"], key, err)
+        else:
+            assert torch.equal(out, first[key]), (ct.variants()[c.variant]["name"], key)
+    say(f"[conv-split-interleaved] {len(order)} launches, {len(first)} configs")
+
+
 def test_split_reduction_is_deterministic():
     w = wl.CONV_WORKLOADS["resnet_final_c512_7x7_k3"]
     inp = wl.conv_inputs(w)
