@@ -44,10 +44,16 @@ def kernel_sources(kernel: str):
     """The source files a kernel (variant name, or "broadcast") is built from."""
     if kernel == "broadcast":
         main = "broadcast.hip"
-    elif kernel.startswith("f32sk_"):
+    elif kernel.startswith("f32skc"):
+        main = "igemm_f32_skc.hip"
+    elif kernel.startswith("f32sk16"):
+        main = "igemm_f32_sk16.hip"
+    elif kernel.startswith(("f32sk_", "f32skx_")):
         main = "igemm_f32_sk.hip"
     elif kernel.startswith("f32_"):
         main = "igemm_f32.hip"
+    elif kernel.startswith(("h2f16_", "h2bf16_")):
+        main = "igemm_f16v2.hip"
     elif kernel.startswith(("f16_", "bf16_")):
         main = "igemm_f16.hip"
     else:

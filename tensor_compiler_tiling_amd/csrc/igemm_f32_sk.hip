@@ -78,11 +78,17 @@ __host__ __device__ inline SkLayout sk_layout(int kc, int RWp, int KS) {
 typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 constexpr int kBufWord3 = 0x00020000;  // raw (untyped) buffer, 32-bit elements
 constexpr int kCoherent = 16;          // cache policy: device-coherent (sc1)
+constexpr int kSkipL1 = 1;             // cache policy: sc0, the load misses the CU's L1
 
 // Divisors the kernel needs arrive in ConvParams' FastDiv slots:
 //   fd_wstr = OH*OW, fd_wp = Wp, fd_rwp = XCS, fd_hp = Hp, fd_ow = OW,
 //   fd_t = KH*KW, fd_kw = KW.
-template <int KL>
+// XL: XCD-local split reduction -- every split of a tile has the same
+// workgroup index mod 8, so on an MI355X (workgroup b on XCD b % 8) the
+// partial stores, the ticket and the partial loads complete in that XCD's
+// L2 rather than at device scope; legal only where the runtime has observed
+// that placement.
+template <int KL, bool XL>
 __global__ __launch_bounds__(kSkThreads) void igemm_f32_sk_kernel(ConvParams p) {
     fetch_kernargs(p);
     constexpr int KS = 8 * KL;
@@ -106,8 +112,17 @@ __global__ __launch_bounds__(kSkThreads) void igemm_f32_sk_kernel(ConvParams p) 
     float* e_rs = e_bias + kSkTileM;
 
     const int tiles = p.tiles_m * p.tiles_n;
-    const int tile = blockIdx.x % tiles;
-    const int split = blockIdx.x / tiles;
+    int tile, split;
+    if constexpr (XL) {
+        const int idx = blockIdx.x >> 3;
+        const int q = idx / p.S;
+        tile = (blockIdx.x & 7) + 8 * q;
+        split = idx - q * p.S;
+        if (tile >= tiles) return;  // the last XCD rounds may be short
+    } else {
+        tile = blockIdx.x % tiles;
+        split = blockIdx.x / tiles;
+    }
     const int tm = tile % p.tiles_m;
     const int tn = tile / p.tiles_m;
     const int co0 = tm * kSkTileM;
@@ -331,15 +346,17 @@ __global__ __launch_bounds__(kSkThreads) void igemm_f32_sk_kernel(ConvParams p) 
                 v.z = __float_as_uint(acc[rn][4 * r4 + 2]);
                 v.w = __float_as_uint(acc[rn][4 * r4 + 3]);
                 const int f = split * TILE_F4 + (rn * 4 + r4) * 64 + lane;
-                __builtin_amdgcn_raw_buffer_store_b128(v, prs, f * 16, 0, kCoherent);
+                __builtin_amdgcn_raw_buffer_store_b128(v, prs, f * 16, 0, XL ? 0 : kCoherent);
             }
         }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
     __syncthreads();
     if (tid == 0) {
-        const unsigned old = __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned old = XL ? __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                                : __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == (unsigned)(p.S - 1)) ? 1 : 0;
     }
     __syncthreads();
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(kSkThreads) void igemm_f32_sk_kernel(ConvParams p) 
                 const int f = (s0 + j) * TILE_F4 + tid + u * kSkThreads;
                 v[u][j] = (col_ok[u] && s0 + j < p.S)
                               ? __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                prs, f * 16, 0, kCoherent))
+                                                                prs, f * 16, 0, XL ? kSkipL1 : kCoherent))
                               : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
             }
 #pragma unroll
@@ -392,8 +409,12 @@ __global__ __launch_bounds__(kSkThreads) void igemm_f32_sk_kernel(ConvParams p) 
                     apply_epilogue(p.epilogue, sum[u][i], e_bias[row], e_rs[row]);
         }
     }
-    if (tid == 0)
-        __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        if constexpr (XL)
+            __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        else
+            __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 template <int KL>
@@ -406,11 +427,11 @@ int sk_lds_bytes(const ConvParams& p) {
     return 4 * sk_layout(p.kc, p.R * p.Wp, 8 * KL).words;
 }
 
-template <int KL>
+template <int KL, bool XL>
 hipError_t sk_launch(const ConvParams& p, hipStream_t stream) {
     const int bytes = sk_lds_bytes<KL>(p);
     if (bytes > 163840 - 64) return hipErrorInvalidValue;
-    auto kern = igemm_f32_sk_kernel<KL>;
+    auto kern = igemm_f32_sk_kernel<KL, XL>;
     static std::atomic<int> lds_limit{65536};
     if (bytes > lds_limit.load(std::memory_order_relaxed)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -430,20 +451,24 @@ hipError_t sk_launch(const ConvParams& p, hipStream_t stream) {
     q.fd_ow = make_fastdiv((uint32_t)p.OW);
     q.fd_t = make_fastdiv((uint32_t)p.T);
     q.fd_kw = make_fastdiv((uint32_t)p.KW);
-    const long long grid = (long long)p.tiles_m * p.tiles_n * p.S;
+    const long long tiles = (long long)p.tiles_m * p.tiles_n;
+    const long long grid = XL ? 8 * ((tiles + 7) / 8) * p.S : tiles * p.S;
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kSkThreads), bytes, stream, q);
     return hipGetLastError();
 }
 
 // descriptor: 32x32x2 instruction, waves 1 x 1 x 4 (CO x P x K), reps 1 x 2
-#define CT_SK_VARIANT(NAME, KL) \
-    {NAME, DT_F32, 32, 32, 2, 1, 1, 4, 1, 2, 8 * KL, &sk_lds_bytes<KL>, &sk_launch<KL>}
+#define CT_SK_VARIANT(NAME, KL, XL) \
+    {NAME, DT_F32, 32, 32, 2, 1, 1, 4, 1, 2, 8 * KL, &sk_lds_bytes<KL>, &sk_launch<KL, XL>, nullptr, XL}
 
 const IgemmVariant kSkVariants[] = {
-    CT_SK_VARIANT("f32sk_m32n64_kl72", 72),
-    CT_SK_VARIANT("f32sk_m32n64_kl36", 36),
-    CT_SK_VARIANT("f32sk_m32n64_kl20", 20),
+    CT_SK_VARIANT("f32sk_m32n64_kl72", 72, false),
+    CT_SK_VARIANT("f32sk_m32n64_kl36", 36, false),
+    CT_SK_VARIANT("f32sk_m32n64_kl20", 20, false),
+    CT_SK_VARIANT("f32skx_m32n64_kl72", 72, true),
+    CT_SK_VARIANT("f32skx_m32n64_kl36", 36, true),
+    CT_SK_VARIANT("f32skx_m32n64_kl20", 20, true),
 };
 
 }  // namespace

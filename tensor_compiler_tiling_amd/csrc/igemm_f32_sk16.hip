@@ -60,6 +60,7 @@ constexpr int kRedStride = 68;                     // padded row of the reductio
 constexpr int kChMax = 4;                          // window words per lane kept as offsets: 4*64
 constexpr int kBufWord3 = 0x00020000;              // raw buffer, 32-bit elements
 constexpr int kCoherent = 16;                      // cache policy: device-coherent (sc1)
+constexpr int kSkipL1 = 1;                         // cache policy: sc0, the load misses the CU's L1
 
 __device__ __forceinline__ uint32_t fdiv16(uint32_t n, FastDiv f) {
     return (uint32_t)(((uint64_t)__umulhi(n, f.mul) + n) >> f.shift);
@@ -94,7 +95,12 @@ __host__ __device__ inline Sk16Layout sk16_layout(int kc, int RWp, int KS, int N
 
 // Divisors in ConvParams: fd_wstr = OH*OW, fd_wp = Wp, fd_rwp = XCS,
 // fd_hp = Hp, fd_ow = OW, fd_t = KH*KW, fd_kw = KW, fd_w = W, fd_hw = H*W.
-template <int NW, int KSTEP, bool STAGED>
+// XL: XCD-local split reduction -- every split of a tile has the same
+// workgroup index mod 8, so on an MI355X (workgroup b on XCD b % 8) the
+// partial stores, the ticket and the partial loads complete in that XCD's
+// L2 rather than at device scope; legal only where the runtime has observed
+// that placement.
+template <int NW, int KSTEP, bool STAGED, bool XL>
 __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
     fetch_kernargs(p);
     constexpr int XE = 16;  // staged window words per thread
@@ -119,8 +125,17 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
     float* Xs = lds;
     int* ktab = reinterpret_cast<int*>(lds + L.ktab_off);
 
-    const int tile = blockIdx.x / p.S;
-    const int split = blockIdx.x - tile * p.S;
+    int tile, split;
+    if constexpr (XL) {
+        const int idx = blockIdx.x >> 3;
+        const int q = idx / p.S;
+        tile = (blockIdx.x & 7) + 8 * q;
+        split = idx - q * p.S;
+        if (tile >= p.tiles_m * p.tiles_n) return;  // the last XCD rounds may be short
+    } else {
+        tile = blockIdx.x / p.S;
+        split = blockIdx.x - tile * p.S;
+    }
     const int tm = tile % p.tiles_m;
     const int tn = tile / p.tiles_m;
     const int co0 = tm * kTileM;
@@ -477,13 +492,15 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
         v.y = __float_as_uint(sum[1]);
         v.z = __float_as_uint(sum[2]);
         v.w = __float_as_uint(sum[3]);
-        __builtin_amdgcn_raw_buffer_store_b128(v, prs, (split * TILE_F + fo) * 4, 0, kCoherent);
+        __builtin_amdgcn_raw_buffer_store_b128(v, prs, (split * TILE_F + fo) * 4, 0, XL ? 0 : kCoherent);
     }
     __builtin_amdgcn_s_waitcnt(0);  // this thread's partial store is complete
     __syncthreads();
     if (tid == 0) {
-        const unsigned old = __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned old = XL ? __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)
+                                : __hip_atomic_fetch_add(&p.tickets[tile * kTicketStride], 1u,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old == (unsigned)(p.S - 1)) ? 1 : 0;
     }
     __syncthreads();
@@ -500,7 +517,7 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
             for (int j = 0; j < SB; ++j)
                 v[j] = (s0 + j < p.S) ? __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
                                                                        prs, ((s0 + j) * TILE_F + fo) * 4, 0,
-                                                                       kCoherent))
+                                                                       XL ? kSkipL1 : kCoherent))
                                       : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int j = 0; j < SB; ++j)
@@ -508,8 +525,12 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_sk16_kernel(ConvParams p) {
         }
         store_out(tot);
     }
-    if (tid == 0)
-        __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+        if constexpr (XL)
+            __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        else
+            __hip_atomic_store(&p.tickets[tile * kTicketStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 template <int NW, int KSTEP, bool STAGED>
@@ -530,7 +551,7 @@ int sk16_lds_bytes(const ConvParams& p) {
     return 4 * sk16_layout(p.kc, p.R * p.Wp, KS, NW).words;
 }
 
-template <int NW, int KSTEP, bool STAGED>
+template <int NW, int KSTEP, bool STAGED, bool XL>
 hipError_t sk16_launch(const ConvParams& p, hipStream_t stream) {
     if (STAGED) {
         const long long HW = (long long)p.H * p.W;
@@ -539,11 +560,11 @@ hipError_t sk16_launch(const ConvParams& p, hipStream_t stream) {
                              ((p.kc * HW) & 3) == 0 && ((p.CI * HW) & 3) == 0 &&
                              ((p.kc * p.T) & 3) == 0;
         // same tile config, same result: the direct-window form takes any layout
-        if (!aligned) return sk16_launch<NW, KSTEP, false>(p, stream);
+        if (!aligned) return sk16_launch<NW, KSTEP, false, XL>(p, stream);
     }
     const int bytes = sk16_lds_bytes<NW, KSTEP, STAGED>(p);
     if (bytes > 163840 - 64) return hipErrorInvalidValue;
-    auto kern = igemm_f32_sk16_kernel<NW, KSTEP, STAGED>;
+    auto kern = igemm_f32_sk16_kernel<NW, KSTEP, STAGED, XL>;
     static std::atomic<int> lds_limit{65536};
     if (bytes > lds_limit.load(std::memory_order_relaxed)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -565,29 +586,34 @@ hipError_t sk16_launch(const ConvParams& p, hipStream_t stream) {
     q.fd_kw = make_fastdiv((uint32_t)p.KW);
     q.fd_w = make_fastdiv((uint32_t)p.W);
     q.fd_hw = make_fastdiv((uint32_t)(p.H * p.W));
-    const long long grid = (long long)p.tiles_m * p.tiles_n * p.S;
+    const long long tiles = (long long)p.tiles_m * p.tiles_n;
+    const long long grid = XL ? 8 * ((tiles + 7) / 8) * p.S : tiles * p.S;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((igemm_f32_sk16_kernel<NW, KSTEP, STAGED>), dim3((unsigned)grid), dim3(NW * 64),
-                       bytes, stream, q);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), bytes, stream, q);
     return hipGetLastError();
 }
 
 // descriptor: 16x16x4 instruction, waves 1 x 1 x NW (CO x P x K), reps 1 x 4;
 // NW waves of KSTEP steps hold a stage of up to NW*4*KSTEP reduction values
-#define CT_SK16_VARIANT(NAME, NW, KSTEP, STAGED)                                                 \
+#define CT_SK16_VARIANT(NAME, NW, KSTEP, STAGED, XL)                                             \
     {NAME, DT_F32, 16, 16, 4, 1, 1, NW, 1, 4, NW * 4 * KSTEP, &sk16_lds_bytes<NW, KSTEP, STAGED>, \
-     &sk16_launch<NW, KSTEP, STAGED>}
+     &sk16_launch<NW, KSTEP, STAGED, XL>, nullptr, XL}
 
 const IgemmVariant kSk16Variants[] = {
-    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt9", 4, 36, false),
-    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt5", 4, 20, false),
-    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt3", 4, 12, false),
-    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt9", 4, 36, true),
-    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt5", 4, 20, true),
-    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt3", 4, 12, true),
-    CT_SK16_VARIANT("f32sk16_m16n64_w8_s18", 8, 18, false),
-    CT_SK16_VARIANT("f32sk16s_m16n64_w8_s18", 8, 18, true),
-    CT_SK16_VARIANT("f32sk16s_m16n64_w8_s10", 8, 10, true),
+    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt9", 4, 36, false, false),
+    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt5", 4, 20, false, false),
+    CT_SK16_VARIANT("f32sk16_m16n64_w4_kt3", 4, 12, false, false),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt9", 4, 36, true, false),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt5", 4, 20, true, false),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w4_kt3", 4, 12, true, false),
+    CT_SK16_VARIANT("f32sk16_m16n64_w8_s18", 8, 18, false, false),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w8_s18", 8, 18, true, false),
+    CT_SK16_VARIANT("f32sk16s_m16n64_w8_s10", 8, 10, true, false),
+    CT_SK16_VARIANT("f32sk16x_m16n64_w4_kt9", 4, 36, false, true),
+    CT_SK16_VARIANT("f32sk16x_m16n64_w4_kt5", 4, 20, false, true),
+    CT_SK16_VARIANT("f32sk16x_m16n64_w4_kt3", 4, 12, false, true),
+    CT_SK16_VARIANT("f32sk16x_m16n64_w8_s18", 8, 18, false, true),
+    CT_SK16_VARIANT("f32sk16sx_m16n64_w8_s10", 8, 10, true, true),
 };
 
 }  // namespace
