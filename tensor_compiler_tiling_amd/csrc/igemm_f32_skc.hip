@@ -83,22 +83,29 @@ constexpr int window_slot(int words) {
     return x;
 }
 
-template <int H_, int W_, int KH_, int KW_, int STR_, int PAD_>
+// TQ: the output is cut into TQ x TQ column tiles of (OH/TQ) x (OW/TQ)
+// pixels (a 14 x 14 output into four 7 x 7 quadrants); the LDS window always
+// holds the whole zero-padded image, and a tile reads it at its own offset.
+template <int H_, int W_, int KH_, int KW_, int STR_, int PAD_, int TQ_ = 1>
 struct LayerShape {
-    static constexpr int H = H_, W = W_, KH = KH_, KW = KW_, STR = STR_, PAD = PAD_;
+    static constexpr int H = H_, W = W_, KH = KH_, KW = KW_, STR = STR_, PAD = PAD_, TQ = TQ_;
     static constexpr int OH = (H + 2 * PAD - KH) / STR + 1;
     static constexpr int OW = (W + 2 * PAD - KW) / STR + 1;
     static constexpr int P = OH * OW;  // batch 1
+    static constexpr int OTH = OH / TQ, OTW = OW / TQ;  // a column tile's output rows, columns
+    static constexpr int PT = OTH * OTW;                // pixels of a column tile
+    static constexpr int NQ = TQ * TQ;                  // column tiles
     static constexpr int T = KH * KW;
     static constexpr int HW = H * W;
     static constexpr int WP = W + 2 * PAD;           // window row pitch
     static constexpr int R = (OH - 1) * STR + KH;    // window rows (padded rows 0..R-1)
     static constexpr int XCS = window_slot(R * WP);  // words per channel slot
-    static constexpr int NBM = P / 16;               // 16-column matrix blocks
-    static constexpr int VT = P - 16 * NBM;          // VALU tail columns
+    static constexpr int NBM = PT / 16;              // 16-column matrix blocks
+    static constexpr int VT = PT - 16 * NBM;         // VALU tail columns
+    static_assert(OH % TQ == 0 && OW % TQ == 0, "whole column tiles");
     static_assert(VT <= 1, "at most one VALU tail column");
     static_assert(PAD + H <= R && PAD + W <= WP, "the window holds the whole image");
-    static_assert(P <= kRS, "partial rows hold every column");
+    static_assert(PT <= kRS, "partial rows hold every column");
 };
 
 // Kernel arguments: two 64-byte lines, all loaded at entry.
@@ -166,7 +173,10 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
         tile = blockIdx.x / p.S;
         split = blockIdx.x - tile * p.S;
     }
-    const int co0 = tile * kRowsM;
+    const int tm = tile / SH::NQ;  // output-channel tile
+    const int tq = tile - tm * SH::NQ;  // column tile
+    const int qy0 = (tq / SH::TQ) * SH::OTH, qx0 = (tq % SH::TQ) * SH::OTW;  // its first output row, column
+    const int co0 = tm * kRowsM;
     const int co_a = co0 + li;
     const bool row_ok = co_a < p.CO;
     const int K = p.CI * T;
@@ -174,7 +184,7 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
     // output-side constants: thread (orow, oq) owns columns 4*oq .. 4*oq+3
     const int orow = (tid & 255) >> 4;
     const int oq = tid & 15;
-    const bool out_thread = tid < 256 && oq * 4 < SH::P;
+    const bool out_thread = tid < 256 && oq * 4 < SH::PT;
     const int oco = co0 + orow;
     float e_b = 0.0f, e_v = 1.0f;
     if (out_thread && oco < p.CO && p.epilogue != EPI_NONE) {
@@ -242,8 +252,8 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int px = nb < SH::NBM ? nb * 16 + li : 16 * SH::NBM;  // tail: the one extra column
-        const int oy = px / SH::OW;
-        const int ox = px - oy * SH::OW;
+        const int oy = qy0 + px / SH::OTW;
+        const int ox = qx0 + px % SH::OTW;
         bptr[nb] = lds + cl_lane * SH::XCS + oy * SH::STR * SH::WP + ox * SH::STR;
     }
     // padding words are the same in every stage: zero the windows once
@@ -333,8 +343,11 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
         if (!(out_thread && oco < p.CO)) return;
         float* yrow = p.y + (long long)oco * SH::P;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * oq + i < SH::P) yrow[4 * oq + i] = apply_epilogue(p.epilogue, v[i], e_b, e_r);
+        for (int i = 0; i < 4; ++i) {
+            const int c = 4 * oq + i;  // pixel of the column tile
+            if (c < SH::PT)
+                yrow[(qy0 + c / SH::OTW) * SH::OW + qx0 + c % SH::OTW] = apply_epilogue(p.epilogue, v[i], e_b, e_r);
+        }
     };
     if (p.S == 1) {
         store_out(sum);
@@ -401,6 +414,8 @@ int skc_lds_bytes(const ConvParams& p) {
     // whole 16-byte groups per stage, also at the end of the input
     if (((long long)p.CI * SH::HW) % 4 != 0) return 1 << 30;
     if ((long long)p.S * kSlab * 4 >= (1LL << 31)) return 1 << 30;
+    // the runtime's column tiles (64 columns each) must be the kernel's
+    if ((p.P + 63) / 64 != SH::NQ) return 1 << 30;
     return 4 * C::WORDS;
 }
 
@@ -433,8 +448,8 @@ hipError_t skc_launch(const ConvParams& p, hipStream_t stream) {
     q.S = p.S;
     q.stages = p.stages;
     q.epilogue = p.epilogue;
-    q.tiles = p.tiles_m;  // one column tile: the whole output
-    const long long grid = XL ? 8LL * ((p.tiles_m + 7) / 8) * p.S : (long long)p.tiles_m * p.tiles_n * p.S;
+    q.tiles = p.tiles_m * SH::NQ;
+    const long long grid = XL ? 8LL * ((q.tiles + 7) / 8) * p.S : (long long)q.tiles * p.S;
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), bytes, stream, q);
     return hipGetLastError();
@@ -442,6 +457,7 @@ hipError_t skc_launch(const ConvParams& p, hipStream_t stream) {
 
 using Layer7s1 = LayerShape<7, 7, 3, 3, 1, 1>;    // 7x7 -> 7x7, 3x3, stride 1, pad 1
 using Layer14s2 = LayerShape<14, 14, 3, 3, 2, 1>;  // 14x14 -> 7x7, 3x3, stride 2, pad 1
+using Layer14q = LayerShape<14, 14, 3, 3, 1, 1, 2>;  // 14x14 -> 14x14 in four 7x7 quadrants
 
 // descriptor: 16x16x4 instruction, waves 1 x 1 x NW (CO x P x K), tile 16 x 64
 // (49 columns used), a stage of exactly 4*NW*CPL channels
@@ -461,6 +477,12 @@ const IgemmVariant kSkcVariants[] = {
     CT_SKC_VARIANT("f32skc7x_w8_c1", Layer7s1, 8, 1, true),
     CT_SKC_VARIANT("f32skc14s2x_w8_c1", Layer14s2, 8, 1, true),
     CT_SKC_VARIANT("f32skc14s2x_w4_c2", Layer14s2, 4, 2, true),
+    CT_SKC_VARIANT("f32skc14q_w8_c2", Layer14q, 8, 2, false),
+    CT_SKC_VARIANT("f32skc14q_w4_c4", Layer14q, 4, 4, false),
+    CT_SKC_VARIANT("f32skc14q_w4_c2", Layer14q, 4, 2, false),
+    CT_SKC_VARIANT("f32skc14q_w4_c1", Layer14q, 4, 1, false),
+    CT_SKC_VARIANT("f32skc14qx_w4_c2", Layer14q, 4, 2, true),
+    CT_SKC_VARIANT("f32skc14qx_w4_c1", Layer14q, 4, 1, true),
 };
 
 }  // namespace

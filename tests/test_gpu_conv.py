@@ -136,12 +136,15 @@ def test_ones_count_valid_taps():
     assert np.array_equal(got[0], np.broadcast_to(512 * exp, (512, 7, 7)))
 
 
-# Layers with the compiled geometries of the 49-pixel split-K kernels
-# ("f32skc*": 7x7 stride 1 and 14x14 stride 2, 3x3, pad 1), at output-channel
-# counts that leave a partial 16-row tile.
+# Layers with the compiled geometries of the shape-specialised kernels
+# ("f32skc*": 7x7 stride 1, 14x14 stride 2 and 14x14 stride 1 in 7x7
+# quadrants, 3x3, pad 1), at output-channel counts that leave a partial
+# 16-row tile.
 SKC_LAYERS = [
     wl.ConvWorkload("skc_7x7_ci64_co40", 111, 1, 64, 7, 7, 40, 3, 3, 1, 1),
     wl.ConvWorkload("skc_14x14s2_ci64_co24", 112, 1, 64, 14, 14, 24, 3, 3, 2, 1),
+    # 14x14 stride 1: four 7x7 quadrant column tiles
+    wl.ConvWorkload("skc_14x14q_ci64_co40", 113, 1, 64, 14, 14, 40, 3, 3, 1, 1),
 ]
 
 
@@ -188,7 +191,8 @@ def test_shape_specialised_split_k(w, epi, misaligned):
 
 
 @pytest.mark.parametrize("w", SKC_LAYERS + [wl.CONV_WORKLOADS["resnet_final_c512_7x7_k3"],
-                                            wl.CONV_WORKLOADS["r18_c256to512_14x14_k3s2"]],
+                                            wl.CONV_WORKLOADS["r18_c256to512_14x14_k3s2"],
+                                            wl.CONV_WORKLOADS["resnet_c64_14x14_k3"]],
                          ids=lambda w: w.name)
 def test_shape_specialised_integers_bit_exact(w):
     inp = wl.small_int_inputs(w)
