@@ -459,6 +459,7 @@ using Layer7s1 = LayerShape<7, 7, 3, 3, 1, 1>;    // 7x7 -> 7x7, 3x3, stride 1, 
 using Layer14s2 = LayerShape<14, 14, 3, 3, 2, 1>;  // 14x14 -> 7x7, 3x3, stride 2, pad 1
 using Layer14q = LayerShape<14, 14, 3, 3, 1, 1, 2>;  // 14x14 -> 14x14 in four 7x7 quadrants
 using Layer14q1 = LayerShape<14, 14, 1, 1, 1, 0, 2>;  // 1x1 filter, 14x14, in four 7x7 quadrants
+using Layer28s2q = LayerShape<28, 28, 3, 3, 2, 1, 2>;  // 28x28 -> 14x14 stride 2, in four 7x7 quadrants
 
 // descriptor: 16x16x4 instruction, waves 1 x 1 x NW (CO x P x K), tile 16 x 64
 // (49 columns used), a stage of exactly 4*NW*CPL channels
@@ -488,6 +489,9 @@ const IgemmVariant kSkcVariants[] = {
     CT_SKC_VARIANT("f32skc14q1x_w4_c4", Layer14q1, 4, 4, true),
     CT_SKC_VARIANT("f32skc14q1x_w4_c8", Layer14q1, 4, 8, true),
     CT_SKC_VARIANT("f32skc14q1x_w8_c4", Layer14q1, 8, 4, true),
+    CT_SKC_VARIANT("f32skc28s2q_w4_c1", Layer28s2q, 4, 1, false),
+    CT_SKC_VARIANT("f32skc28s2qx_w4_c1", Layer28s2q, 4, 1, true),
+    CT_SKC_VARIANT("f32skc28s2qx_w8_c1", Layer28s2q, 8, 1, true),
 };
 
 }  // namespace
