@@ -20,7 +20,9 @@
 //    pixel records;
 //  - LDS holds two copies of (filter tile, window): the next stage's global
 //    loads are issued before the current stage's matrix steps and written to
-//    the other copy after them, with one barrier per stage;
+//    the other copy after them, with one barrier per stage; the window loads
+//    (from HBM) go out two stages ahead into a second register set, the
+//    filter loads (an L2-resident reordered copy) one stage ahead;
 //  - a stage's 9*KC/16 matrix steps are unrolled, each reading the next
 //    step's fragments before issuing its own instructions.
 // The window's padding is zeroed once at kernel start and never written
@@ -261,25 +263,35 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     }
 
     using XV = typename PxVec<PX>::T;
+    // Staging registers.  The filter tile (from the small reordered copy,
+    // an L2 hit) is loaded one stage ahead; the input window (from HBM) two
+    // stages ahead, into two register sets, so each window load has two
+    // stages of matrix work to arrive.
+    struct XRegs {
+        XV v[XPT][8];
+    };
     uint4v wreg[WPT];
-    XV xreg[XPT][8];
-    auto load_stage = [&](int s_abs, int c0) {
+    XRegs xa, xb;
+    auto load_w = [&](int s_abs) {
 #pragma unroll
         for (int j = 0; j < WPT; ++j)
             if (wsrc[j] >= 0)
                 wreg[j] = *reinterpret_cast<const uint4v*>(wpk + wsrc[j] + s_abs * (T * KC));
+    };
+    auto load_x = [&](XRegs& rg, int c0) {
 #pragma unroll
         for (int j = 0; j < XPT; ++j) {
             if (xsrc[j] < 0) continue;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int c = c0 + xch[j] + i;
-                xreg[j][i] = c < p.CI ? *reinterpret_cast<const XV*>(xg + xsrc[j] + (long long)(c0 + i) * HW)
+                rg.v[j][i] = c < p.CI ? *reinterpret_cast<const XV*>(xg + xsrc[j] + (long long)(c0 + i) * HW)
                                       : XV{};
             }
         }
     };
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](const XRegs& rg, int buf) {
+        const auto& xreg = rg.v;
         uint16_t* Wb = Wsb + buf * C::WB;
         uint16_t* Xb = Xsb + buf * XB;
 #pragma unroll
@@ -336,25 +348,33 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
         }
     };
 
-    // ---- stages of this split: load ahead, multiply, store ahead, one barrier
+    // ---- stages of this split: loads two stages ahead, multiply, store the
+    //      next stage, one barrier per stage
     const int s_first = split * p.stages;
     int nst = p.stages;
     if (s_first + nst > NS) nst = NS - s_first;
     __syncthreads();  // windows zeroed before any stage writes into them
     if (nst > 0) {
-        load_stage(s_first, s_first * KC);
-        store_stage(0);
+        load_w(s_first);
+        load_x(xa, s_first * KC);
+        if (nst > 1) load_x(xb, (s_first + 1) * KC);
+        store_stage(xa, 0);
     }
     __syncthreads();
-    for (int st = 0; st < nst; ++st) {
-        const bool more = st + 1 < nst;
-        if (more) load_stage(s_first + st + 1, (s_first + st + 1) * KC);
+    // stage st: `held` has stage st+1's window, `free` takes stage st+2's
+    auto step = [&](int st, XRegs& held, XRegs& free) {
+        if (st + 1 < nst) load_w(s_first + st + 1);
+        if (st + 2 < nst) load_x(free, (s_first + st + 2) * KC);
         // keep the loads here, ahead of the matrix steps: left free, the
         // compiler sinks them to their LDS writes and the latency is exposed
         asm volatile("" ::: "memory");
         mfma_stage(st & 1);
-        if (more) store_stage((st + 1) & 1);
+        if (st + 1 < nst) store_stage(held, (st + 1) & 1);
         __syncthreads();
+    };
+    for (int st = 0; st < nst; st += 2) {
+        step(st, xb, xa);
+        if (st + 1 < nst) step(st + 1, xa, xb);
     }
 
     // ---- split reduction across workgroups (device-scope atomics) -------------
