@@ -9,8 +9,9 @@ with ct_cache_load so that ct_conv2d_nchw_fwd dispatches to it.
 
     python -m tensor_compiler_tiling_amd.tune_all [--out PATH] [--ms MS] [names...]
 
-With no names every convolution workload is tuned.  The default output is the
-log shipped with the package for gfx950 (tuned/gfx950.jsonl).
+With no names every convolution workload is tuned and the log is rewritten;
+with names, the log's records of the other shapes are kept.  The default
+output is the log shipped with the package for gfx950 (tuned/gfx950.jsonl).
 """
 from __future__ import annotations
 
@@ -38,6 +39,9 @@ def main(argv=None) -> int:
 
     names = a.names or list(wl.CONV_WORKLOADS)
     ct.check(ct.ct_cache_clear(), "cache clear")
+    if a.names and os.path.exists(a.out):
+        # retuning some shapes: keep the log's records of the others
+        ct.check(ct.ct_cache_load(a.out), "cache load")
     for name in names:
         w = wl.CONV_WORKLOADS[name]
         tdt = {wl.F32: torch.float32, wl.F16: torch.float16, wl.BF16: torch.bfloat16}[w.dtype]
