@@ -76,6 +76,9 @@ struct IgemmVariant {
     // relying on workgroup b running on XCD b % 8; legal only where the
     // runtime has observed that placement
     int xcd_local;
+    // nonzero: the width (output pixels) of the variant's column tiles, when
+    // it is not waves_n * reps_n * mfma_n
+    int tile_n;
 };
 
 // Kernel-file registries.

@@ -65,6 +65,8 @@ constexpr int kSkipL1 = 1;             // cache policy: sc0, the load misses the
 constexpr int kRowsM = 16;             // output channels per tile
 constexpr int kRS = 52;                // reduction / partial row: 49 columns, 16-byte rows
 constexpr int kSlab = kRowsM * kRS;    // floats per partial tile
+constexpr int kTileP = 49;             // pixels of a column tile (7 x 7), the runtime's tile width
+static_assert(kRS == (kTileP + 3) / 4 * 4, "partial rows are the runtime's 16-byte padded tile rows");
 
 // Workgroup barrier for LDS traffic only: loads into registers may still be
 // in flight (the compiler waits for each where its value is used).
@@ -84,11 +86,16 @@ constexpr int window_slot(int words) {
 }
 
 // TQ: the output is cut into TQ x TQ column tiles of (OH/TQ) x (OW/TQ)
-// pixels (a 14 x 14 output into four 7 x 7 quadrants); the LDS window always
-// holds the whole zero-padded image, and a tile reads it at its own offset.
-template <int H_, int W_, int KH_, int KW_, int STR_, int PAD_, int TQ_ = 1>
+// pixels (a 14 x 14 output into four 7 x 7 quadrants).
+// WIN = false: the LDS window holds the whole zero-padded image (staged with
+// 16-byte loads of the channels' contiguous data, padding zeroed once), and a
+// tile reads it at its own offset.  WIN = true: the window holds only the
+// tile's receptive field, (OTH-1)*STR+KH rows x (OTW-1)*STR+KW columns,
+// staged word by word with zeros for padding (large images).
+template <int H_, int W_, int KH_, int KW_, int STR_, int PAD_, int TQ_ = 1, bool WIN_ = false>
 struct LayerShape {
     static constexpr int H = H_, W = W_, KH = KH_, KW = KW_, STR = STR_, PAD = PAD_, TQ = TQ_;
+    static constexpr bool WIN = WIN_;
     static constexpr int OH = (H + 2 * PAD - KH) / STR + 1;
     static constexpr int OW = (W + 2 * PAD - KW) / STR + 1;
     static constexpr int P = OH * OW;  // batch 1
@@ -97,14 +104,15 @@ struct LayerShape {
     static constexpr int NQ = TQ * TQ;                  // column tiles
     static constexpr int T = KH * KW;
     static constexpr int HW = H * W;
-    static constexpr int WP = W + 2 * PAD;           // window row pitch
-    static constexpr int R = (OH - 1) * STR + KH;    // window rows (padded rows 0..R-1)
-    static constexpr int XCS = window_slot(R * WP);  // words per channel slot
+    static constexpr int WR = WIN ? (OTH - 1) * STR + KH : (OH - 1) * STR + KH;  // window rows
+    static constexpr int WP = WIN ? (OTW - 1) * STR + KW : W + 2 * PAD;          // window row pitch
+    static constexpr int RC = WR * WP;               // window words per channel
+    static constexpr int XCS = window_slot(RC);      // words per channel slot
     static constexpr int NBM = PT / 16;              // 16-column matrix blocks
     static constexpr int VT = PT - 16 * NBM;         // VALU tail columns
     static_assert(OH % TQ == 0 && OW % TQ == 0, "whole column tiles");
     static_assert(VT <= 1, "at most one VALU tail column");
-    static_assert(PAD + H <= R && PAD + W <= WP, "the window holds the whole image");
+    static_assert(WIN || (PAD + H <= WR && PAD + W <= WP), "the window holds the whole image");
     static_assert(PT <= kRS, "partial rows hold every column");
 };
 
@@ -130,7 +138,9 @@ struct SkcCfg {
     static constexpr int NT = NW * 64;
     static constexpr int KC = 4 * NW * CPL;        // channels per stage
     static constexpr int KSTEP = CPL * SH::T;      // matrix steps per wave per stage
-    static constexpr int XE = cround4((KC * SH::HW + NT - 1) / NT);  // window words per thread
+    // window words per thread: whole-image form, the stage's KC*H*W floats in
+    // 16-byte groups; windowed form, the KC*RC window words one by one
+    static constexpr int XE = SH::WIN ? (KC * SH::RC + NT - 1) / NT : cround4((KC * SH::HW + NT - 1) / NT);
     // LDS words: windows | reduction | tail | one word that takes the stores
     // of staged words past the stage's data.  The window zeroing covers whole
     // rounds of the threads' 16-byte stores (it may run into the reduction
@@ -138,12 +148,12 @@ struct SkcCfg {
     static constexpr int RED_OFF = KC * SH::XCS;
     static constexpr int TAIL_OFF = RED_OFF + NW * kSlab;
     static constexpr int DUMMY = TAIL_OFF + NW * kRowsM;
-    static constexpr int ZERO_ROUNDS = (KC * SH::XCS / 4 + NT - 1) / NT;
+    static constexpr int ZERO_ROUNDS = SH::WIN ? 0 : (KC * SH::XCS / 4 + NT - 1) / NT;
     static constexpr int WORDS = (DUMMY + 1 > ZERO_ROUNDS * NT * 4) ? DUMMY + 1 : ZERO_ROUNDS * NT * 4;
     static constexpr int NB = SH::NBM + SH::VT;    // B reads per step
     static constexpr int D = 2;                    // B reads run D steps ahead
     static_assert(NT >= 256, "the reduction uses 16 x 16 threads");
-    static_assert((KC * SH::HW) % 4 == 0, "a stage is whole 16-byte groups");
+    static_assert(SH::WIN || (KC * SH::HW) % 4 == 0, "a stage is whole 16-byte groups");
     static_assert(SH::T <= 64, "a filter run of the zero block");
 };
 
@@ -202,7 +212,22 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
         const int c0 = (split * p.stages + st) * KC;
         const int E = min(KC, p.CI - c0) * HW;  // valid words of the stage (<= 0: none)
         const float* xblk = p.x + (long long)c0 * HW;
-        if constexpr (XV) {
+        if constexpr (SH::WIN) {
+            // word e = c*RC + r*WP + col of the tile's receptive field: image
+            // row qy0*STR - PAD + r, column qx0*STR - PAD + col; zero outside
+            const int cv = min(KC, p.CI - c0);
+#pragma unroll
+            for (int j = 0; j < XE; ++j) {
+                const int e = j * NT + tid;
+                const int c = e / SH::RC;
+                const int rem = e - c * SH::RC;
+                const int r = rem / SH::WP;
+                const int iy = qy0 * SH::STR - SH::PAD + r;
+                const int ix = qx0 * SH::STR - SH::PAD + rem - r * SH::WP;
+                const bool ok = e < KC * SH::RC && c < cv && iy >= 0 && iy < SH::H && ix >= 0 && ix < SH::W;
+                xr[j] = ok ? xblk[c * HW + iy * SH::W + ix] : 0.0f;
+            }
+        } else if constexpr (XV) {
 #pragma unroll
             for (int j = 0; j < XE / 4; ++j) {
                 const int f = 4 * (j * NT + tid);
@@ -236,33 +261,45 @@ __global__ __launch_bounds__(NW * 64) void igemm_f32_skc_kernel(SkcParams p) {
     // window destination of each staged word (past the stage's data: the
     // dummy word)
     int xdst[XE];
+    if constexpr (SH::WIN) {
 #pragma unroll
-    for (int j = 0; j < XE / 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int f = 4 * (j * NT + tid) + i;
-            const int c = f / HW;
-            const int r = f - c * HW;
-            const int iy = r / SH::W;
-            const int ix = r - iy * SH::W;
-            xdst[4 * j + i] = f < KC * HW ? c * SH::XCS + (iy + SH::PAD) * SH::WP + ix + SH::PAD : C::DUMMY;
+        for (int j = 0; j < XE; ++j) {
+            const int e = j * NT + tid;
+            const int c = e / SH::RC;
+            xdst[j] = e < KC * SH::RC ? c * SH::XCS + e - c * SH::RC : C::DUMMY;
         }
+    } else {
+#pragma unroll
+        for (int j = 0; j < XE / 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int f = 4 * (j * NT + tid) + i;
+                const int c = f / HW;
+                const int r = f - c * HW;
+                const int iy = r / SH::W;
+                const int ix = r - iy * SH::W;
+                xdst[4 * j + i] = f < KC * HW ? c * SH::XCS + (iy + SH::PAD) * SH::WP + ix + SH::PAD : C::DUMMY;
+            }
+    }
     // B read bases: lane slot plus the column's (0,0)-tap offset
     const float* bptr[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
         const int px = nb < SH::NBM ? nb * 16 + li : 16 * SH::NBM;  // tail: the one extra column
-        const int oy = qy0 + px / SH::OTW;
-        const int ox = qx0 + px % SH::OTW;
+        // window row / column of the pixel's (0,0) tap: the whole-image window
+        // starts at padded row and column 0, the tile window at the tile
+        const int oy = (SH::WIN ? 0 : qy0) + px / SH::OTW;
+        const int ox = (SH::WIN ? 0 : qx0) + px % SH::OTW;
         bptr[nb] = lds + cl_lane * SH::XCS + oy * SH::STR * SH::WP + ox * SH::STR;
     }
-    // padding words are the same in every stage: zero the windows once
-    {
+    // whole-image form: padding words are the same in every stage, zero the
+    // windows once (the tile-window form stages its zeros with the data)
+    if constexpr (!SH::WIN) {
         floatx4* xz = reinterpret_cast<floatx4*>(lds);
 #pragma unroll
         for (int i = 0; i < C::ZERO_ROUNDS; ++i) xz[i * NT + tid] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        lds_sync();
     }
-    lds_sync();
 
     floatx4 acc[SH::NBM];
 #pragma unroll
@@ -412,10 +449,10 @@ int skc_lds_bytes(const ConvParams& p) {
         return 1 << 30;  // compiled for one layer geometry
     if (p.kc != C::KC) return 1 << 30;  // a stage is exactly the lanes' channels
     // whole 16-byte groups per stage, also at the end of the input
-    if (((long long)p.CI * SH::HW) % 4 != 0) return 1 << 30;
+    if (!SH::WIN && ((long long)p.CI * SH::HW) % 4 != 0) return 1 << 30;
     if ((long long)p.S * kSlab * 4 >= (1LL << 31)) return 1 << 30;
-    // the runtime's column tiles (64 columns each) must be the kernel's
-    if ((p.P + 63) / 64 != SH::NQ) return 1 << 30;
+    // the runtime's column tiles (kTileP columns each) must be the kernel's
+    if ((p.P + kTileP - 1) / kTileP != SH::NQ) return 1 << 30;
     return 4 * C::WORDS;
 }
 
@@ -460,12 +497,14 @@ using Layer14s2 = LayerShape<14, 14, 3, 3, 2, 1>;  // 14x14 -> 7x7, 3x3, stride 
 using Layer14q = LayerShape<14, 14, 3, 3, 1, 1, 2>;  // 14x14 -> 14x14 in four 7x7 quadrants
 using Layer14q1 = LayerShape<14, 14, 1, 1, 1, 0, 2>;  // 1x1 filter, 14x14, in four 7x7 quadrants
 using Layer28s2q = LayerShape<28, 28, 3, 3, 2, 1, 2>;  // 28x28 -> 14x14 stride 2, in four 7x7 quadrants
+using Layer56w = LayerShape<56, 56, 3, 3, 1, 1, 8, true>;   // 56x56, 64 tiles of 7x7, tile windows
+using Layer56s2w = LayerShape<56, 56, 3, 3, 2, 1, 4, true>; // 56x56 -> 28x28 stride 2, 16 tiles, tile windows
 
-// descriptor: 16x16x4 instruction, waves 1 x 1 x NW (CO x P x K), tile 16 x 64
-// (49 columns used), a stage of exactly 4*NW*CPL channels
+// descriptor: 16x16x4 instruction, waves 1 x 1 x NW (CO x P x K), reps 1 x 4,
+// column tiles of kTileP = 49 pixels, a stage of exactly 4*NW*CPL channels
 #define CT_SKC_VARIANT(NAME, SH, NW, CPL, XL)                                                 \
     {NAME, DT_F32, 16, 16, 4, 1, 1, NW, 1, 4, 4 * NW * CPL, &skc_lds_bytes<SH, NW, CPL, XL>, \
-     &skc_launch<SH, NW, CPL, XL>, nullptr, XL}
+     &skc_launch<SH, NW, CPL, XL>, nullptr, XL, kTileP}
 
 const IgemmVariant kSkcVariants[] = {
     CT_SKC_VARIANT("f32skc7_w8_c2", Layer7s1, 8, 2, false),
@@ -492,6 +531,14 @@ const IgemmVariant kSkcVariants[] = {
     CT_SKC_VARIANT("f32skc28s2q_w4_c1", Layer28s2q, 4, 1, false),
     CT_SKC_VARIANT("f32skc28s2qx_w4_c1", Layer28s2q, 4, 1, true),
     CT_SKC_VARIANT("f32skc28s2qx_w8_c1", Layer28s2q, 8, 1, true),
+    CT_SKC_VARIANT("f32skc56w_w8_c2", Layer56w, 8, 2, false),
+    CT_SKC_VARIANT("f32skc56w_w4_c4", Layer56w, 4, 4, false),
+    CT_SKC_VARIANT("f32skc56w_w4_c2", Layer56w, 4, 2, false),
+    CT_SKC_VARIANT("f32skc56wx_w4_c2", Layer56w, 4, 2, true),
+    CT_SKC_VARIANT("f32skc56s2w_w8_c2", Layer56s2w, 8, 2, false),
+    CT_SKC_VARIANT("f32skc56s2w_w4_c2", Layer56s2w, 4, 2, false),
+    CT_SKC_VARIANT("f32skc56s2wx_w4_c2", Layer56s2w, 4, 2, true),
+    CT_SKC_VARIANT("f32skc56s2wx_w8_c1", Layer56s2w, 8, 1, true),
 };
 
 }  // namespace

@@ -169,7 +169,7 @@ const std::vector<Variant>& variants() {
                 v.desc.reps_m = t[i].reps_m;
                 v.desc.reps_n = t[i].reps_n;
                 v.desc.tile_m = t[i].waves_m * t[i].reps_m * t[i].mfma_m;
-                v.desc.tile_n = t[i].waves_n * t[i].reps_n * t[i].mfma_n;
+                v.desc.tile_n = t[i].tile_n ? t[i].tile_n : t[i].waves_n * t[i].reps_n * t[i].mfma_n;
                 v.desc.kc_max = t[i].kc_max;
                 v.desc.threads = t[i].waves_m * t[i].waves_n * t[i].waves_k * 64;
                 v.ig = &t[i];
@@ -329,11 +329,18 @@ struct Resolved {
 };
 
 // Whether workgroup b of a launch runs on XCD b % 8 on the current device:
-// observed once per device with a probe launch of 4096 workgroups (false
-// when there is no device or the probe fails).
+// observed once per device with a probe launch of 4096 workgroups (false if
+// the probe fails).  On a host with no device nothing can launch, and the
+// tuning log's XCD-local records are taken as they were measured; any
+// launch happens on a device, where the probe decides.
 bool xcd_round_robin() {
     static std::mutex mu;
     static std::map<int, bool> seen;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) {
+        (void)hipGetLastError();
+        return true;
+    }
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
         (void)hipGetLastError();
@@ -395,7 +402,8 @@ bool legal(const Shape& s, const ct_tile_config& c, Resolved* out, std::string* 
     const long long tiles_n = (s.P + v.desc.tile_n - 1) / v.desc.tile_n;
     const long long grid = tiles_m * tiles_n * c.split_k;
     if (tiles_m * tiles_n > (1LL << 30) || grid > 0x7fffffffLL) return no("grid too large");
-    const long long ws = c.split_k > 1 ? grid * v.desc.tile_m * v.desc.tile_n * 4LL : 0;
+    // partial tiles: tile_m rows of tile_n floats, rows padded to 16 bytes
+    const long long ws = c.split_k > 1 ? grid * v.desc.tile_m * round_up(v.desc.tile_n, 4) * 4LL : 0;
     if (ws > kMaxWorkspace) return no("split workspace too large");
     const long long aux = v.ig->aux_bytes ? v.ig->aux_bytes(lp) : 0;
     if (aux > kMaxWorkspace) return no("reordered filter too large");

@@ -138,8 +138,9 @@ def test_ones_count_valid_taps():
 
 # Layers with the compiled geometries of the shape-specialised kernels
 # ("f32skc*": 3x3 pad 1 at 7x7 stride 1, 14x14 stride 2 and 14x14 stride 1
-# in 7x7 quadrants; 1x1 at 14x14 and 3x3 stride 2 at 28x28 in quadrants), at
-# output-channel counts that leave a partial 16-row tile.
+# in 7x7 quadrants; 1x1 at 14x14 and 3x3 stride 2 at 28x28 in quadrants;
+# 3x3 at 56x56, stride 1 and 2, in tile windows), at output-channel counts
+# that leave a partial 16-row tile.
 SKC_LAYERS = [
     wl.ConvWorkload("skc_7x7_ci64_co40", 111, 1, 64, 7, 7, 40, 3, 3, 1, 1),
     wl.ConvWorkload("skc_14x14s2_ci64_co24", 112, 1, 64, 14, 14, 24, 3, 3, 2, 1),
@@ -149,6 +150,9 @@ SKC_LAYERS = [
     wl.ConvWorkload("skc_14x14q_1x1_ci64_co40", 114, 1, 64, 14, 14, 40, 1, 1, 1, 0),
     # 28x28 stride 2: a 14x14 output in quadrants
     wl.ConvWorkload("skc_28x28s2q_ci32_co24", 115, 1, 32, 28, 28, 24, 3, 3, 2, 1),
+    # 56x56, stride 1 and 2: 7x7 tiles, each staging only its receptive field
+    wl.ConvWorkload("skc_56x56w_ci64_co24", 116, 1, 64, 56, 56, 24, 3, 3, 1, 1),
+    wl.ConvWorkload("skc_56x56s2w_ci64_co40", 117, 1, 64, 56, 56, 40, 3, 3, 2, 1),
 ]
 
 
