@@ -498,6 +498,11 @@ using Layer14q = LayerShape<14, 14, 3, 3, 1, 1, 2>;  // 14x14 -> 14x14 in four 7
 using Layer14q1 = LayerShape<14, 14, 1, 1, 1, 0, 2>;  // 1x1 filter, 14x14, in four 7x7 quadrants
 using Layer28s2q = LayerShape<28, 28, 3, 3, 2, 1, 2>;  // 28x28 -> 14x14 stride 2, in four 7x7 quadrants
 using Layer56w = LayerShape<56, 56, 3, 3, 1, 1, 8, true>;   // 56x56, 64 tiles of 7x7, tile windows
+// tile-window forms of the smaller geometries
+using Layer7w = LayerShape<7, 7, 3, 3, 1, 1, 1, true>;
+using Layer14qw = LayerShape<14, 14, 3, 3, 1, 1, 2, true>;
+using Layer14q1w = LayerShape<14, 14, 1, 1, 1, 0, 2, true>;
+using Layer28s2w = LayerShape<28, 28, 3, 3, 2, 1, 2, true>;
 using Layer56s2w = LayerShape<56, 56, 3, 3, 2, 1, 4, true>; // 56x56 -> 28x28 stride 2, 16 tiles, tile windows
 
 // descriptor: 16x16x4 instruction, waves 1 x 1 x NW (CO x P x K), reps 1 x 4,
@@ -539,6 +544,14 @@ const IgemmVariant kSkcVariants[] = {
     CT_SKC_VARIANT("f32skc56s2w_w4_c2", Layer56s2w, 4, 2, false),
     CT_SKC_VARIANT("f32skc56s2wx_w4_c2", Layer56s2w, 4, 2, true),
     CT_SKC_VARIANT("f32skc56s2wx_w8_c1", Layer56s2w, 8, 1, true),
+    CT_SKC_VARIANT("f32skc7wx_w8_c1", Layer7w, 8, 1, true),
+    CT_SKC_VARIANT("f32skc7wx_w8_c2", Layer7w, 8, 2, true),
+    CT_SKC_VARIANT("f32skc14qwx_w4_c1", Layer14qw, 4, 1, true),
+    CT_SKC_VARIANT("f32skc14qw_w8_c2", Layer14qw, 8, 2, false),
+    CT_SKC_VARIANT("f32skc14q1wx_w4_c4", Layer14q1w, 4, 4, true),
+    CT_SKC_VARIANT("f32skc28s2wx_w4_c1", Layer28s2w, 4, 1, true),
+    CT_SKC_VARIANT("f32skc28s2wx_w8_c1", Layer28s2w, 8, 1, true),
+    CT_SKC_VARIANT("f32skc28s2w_w8_c2", Layer28s2w, 8, 2, false),
 };
 
 }  // namespace
