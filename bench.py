@@ -46,6 +46,8 @@ def kernel_sources(kernel: str):
         main = "broadcast.hip"
     elif kernel.startswith("f32skc"):
         main = "igemm_f32_skc.hip"
+    elif kernel.startswith("f32skt"):
+        main = "igemm_f32_skt.hip"
     elif kernel.startswith("f32sk16"):
         main = "igemm_f32_sk16.hip"
     elif kernel.startswith(("f32sk_", "f32skx_")):

@@ -86,6 +86,7 @@ const IgemmVariant* igemm_f32_variants(int* count);
 const IgemmVariant* igemm_f32_sk_variants(int* count);
 const IgemmVariant* igemm_f32_sk16_variants(int* count);
 const IgemmVariant* igemm_f32_skc_variants(int* count);
+const IgemmVariant* igemm_f32_skt_variants(int* count);
 const IgemmVariant* igemm_f16_variants(int* count);
 const IgemmVariant* igemm_f16v2_variants(int* count);
 

@@ -139,8 +139,9 @@ def test_ones_count_valid_taps():
 # Layers with the compiled geometries of the shape-specialised kernels
 # ("f32skc*": 3x3 pad 1 at 7x7 stride 1, 14x14 stride 2 and 14x14 stride 1
 # in 7x7 quadrants; 1x1 at 14x14 and 3x3 stride 2 at 28x28 in quadrants;
-# 3x3 at 56x56, stride 1 and 2, in tile windows), at output-channel counts
-# that leave a partial 16-row tile.
+# 3x3 at 56x56, stride 1 and 2, in tile windows; "f32skt*": the 3-channel
+# 7x7 stride-2 layer at 224x224), at output-channel counts that leave a
+# partial 16-row tile, and the full first layer.
 SKC_LAYERS = [
     wl.ConvWorkload("skc_7x7_ci64_co40", 111, 1, 64, 7, 7, 40, 3, 3, 1, 1),
     wl.ConvWorkload("skc_14x14s2_ci64_co24", 112, 1, 64, 14, 14, 24, 3, 3, 2, 1),
@@ -153,11 +154,15 @@ SKC_LAYERS = [
     # 56x56, stride 1 and 2: 7x7 tiles, each staging only its receptive field
     wl.ConvWorkload("skc_56x56w_ci64_co24", 116, 1, 64, 56, 56, 24, 3, 3, 1, 1),
     wl.ConvWorkload("skc_56x56s2w_ci64_co40", 117, 1, 64, 56, 56, 40, 3, 3, 2, 1),
+    # 3-channel 7x7 stride-2 first layer: lane groups split the filter rows;
+    # 40 output channels leave a partial channel tile
+    wl.ConvWorkload("skt_stem_c3_224x224_k7s2_co40", 118, 1, 3, 224, 224, 40, 7, 7, 2, 3),
+    wl.CONV_WORKLOADS["r18_stem_c3_224x224_k7s2"],
 ]
 
 
 def _skc_configs(w):
-    return [c for c in legal_configs(w) if ct.variants()[c.variant]["name"].startswith("f32skc")]
+    return [c for c in legal_configs(w) if ct.variants()[c.variant]["name"].startswith(("f32skc", "f32skt"))]
 
 
 @pytest.mark.parametrize("misaligned", [False, True], ids=["aligned", "x_offset_4B"])
