@@ -31,6 +31,7 @@
 #include "igemm_common.hpp"
 
 #include <atomic>
+#include <type_traits>
 
 namespace ct {
 
@@ -43,6 +44,8 @@ typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
 
 constexpr int kPackCO = 256;  // reordered filter rows: a multiple of this
+constexpr int kBufRaw = 0x00020000;       // raw buffer descriptor, 32-bit elements
+constexpr unsigned kBufOut = 0x80000000u;  // an offset past every buffer (all are < 2 GiB): reads zeros
 
 template <int DT> struct HMma2;
 template <> struct HMma2<DT_F16> {
@@ -88,7 +91,7 @@ struct H2 {
     static constexpr int KCS = (CG + 1) * 8;   // halves per window pixel (odd x 16 B)
     static constexpr int WCH = TM * G;         // 16-byte filter chunks per stage
     static constexpr int WPT = (WCH + NT - 1) / NT;
-    static constexpr int XPT = NT >= 512 ? 1 : 2;  // window tasks per thread
+    static constexpr int XPT = NT >= 256 ? 1 : 2;  // window tasks per thread
     static constexpr int WB = TM * WST;        // halves per filter copy
     static_assert(G % 2 == 0, "a step takes two groups");
 };
@@ -121,6 +124,29 @@ __device__ __forceinline__ uint32_t pack2h(uint16_t lo, uint16_t hi) {
     return (uint32_t)lo | ((uint32_t)hi << 16);
 }
 
+// Raw buffer load of PX halves at byte offset off.
+template <int PX> struct BufLoad;
+template <> struct BufLoad<8> {
+    static __device__ __forceinline__ uint4v load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+};
+template <> struct BufLoad<4> {
+    static __device__ __forceinline__ uint2v load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_bit_cast(uint2v, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    }
+};
+template <> struct BufLoad<2> {
+    static __device__ __forceinline__ uint32_t load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    }
+};
+template <> struct BufLoad<1> {
+    static __device__ __forceinline__ uint16_t load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    }
+};
+
 // Divisors: fd_kw = KW.
 template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
 __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
@@ -133,7 +159,8 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform, and known to be: branches on it are not divergent
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM;
     const int wn = wave / WM;
     const int lj = lane & 31;
@@ -190,17 +217,23 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
             yoff[rn] = n * (long long)p.CO * p.OHW + rem;
         }
     }
-    // window offset of this lane's group 2s + lh at every step
+    // Window offset of this lane's group 2s + lh at step s.  With an even
+    // number of channel groups the two groups of a step share one tap, so
+    // the offset is a wave-uniform step part (tap and group 2s) plus the
+    // lane part lh*8, which goes into the lane's base address.
+    static_assert(CG % 2 == 0, "the two groups of a step share a tap");
     int koff[NSTEP];
 #pragma unroll
     for (int s = 0; s < NSTEP; ++s) {
-        const int g = 2 * s + lh;
-        const int t = g / CG;
-        const int cg = g - t * CG;
+        const int t = (2 * s) / CG;
+        const int cg = 2 * s - t * CG;
         const int ky = (int)(((uint64_t)__umulhi((uint32_t)t, p.fd_kw.mul) + (uint32_t)t) >> p.fd_kw.shift);
         const int kx = t - ky * p.KW;
-        koff[s] = (ky * p.Wp + kx) * KCS + cg * 8;
+        koff[s] = __builtin_amdgcn_readfirstlane((ky * p.Wp + kx) * KCS + cg * 8);
     }
+    int xlane[RN];
+#pragma unroll
+    for (int rn = 0; rn < RN; ++rn) xlane[rn] = pbase[rn] * KCS + lh * 8;
 
     // ---- epilogue tables; zero both windows ----------------------------------
     for (int m = tid; m < TM; m += NT) {
@@ -270,47 +303,21 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     struct XRegs {
         XV v[XPT][8];
     };
-    uint4v wreg[WPT];
-    XRegs xa, xb;
-    auto load_w = [&](int s_abs) {
+    // Loads are raw buffer loads with no condition around them.  A stage's
+    // descriptors start at that stage (x at its first channel, the reordered
+    // filter at its block), so a lane's byte offsets are fixed for the
+    // kernel: the filter chunk's, and the window task's plus i*HW*2 for its
+    // channel i.  A lane with no chunk or task passes an offset past the
+    // buffer and reads zeros.  (A load under a condition, or with a zero
+    // default, compiles to code on which the compiler must wait for every
+    // load in flight, the prefetches included.)
+    const long long x_bytes = (long long)p.N * p.CI * HW * 2;
+    const long long w_bytes = (long long)round_up(p.CO, kPackCO) * CIp * T * 2;
+    unsigned wvo[WPT], xvo[XPT];
 #pragma unroll
-        for (int j = 0; j < WPT; ++j)
-            if (wsrc[j] >= 0)
-                wreg[j] = *reinterpret_cast<const uint4v*>(wpk + wsrc[j] + s_abs * (T * KC));
-    };
-    auto load_x = [&](XRegs& rg, int c0) {
+    for (int j = 0; j < WPT; ++j) wvo[j] = wsrc[j] >= 0 ? (unsigned)wsrc[j] * 2u : kBufOut;
 #pragma unroll
-        for (int j = 0; j < XPT; ++j) {
-            if (xsrc[j] < 0) continue;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c = c0 + xch[j] + i;
-                rg.v[j][i] = c < p.CI ? *reinterpret_cast<const XV*>(xg + xsrc[j] + (long long)(c0 + i) * HW)
-                                      : XV{};
-            }
-        }
-    };
-    auto store_stage = [&](const XRegs& rg, int buf) {
-        const auto& xreg = rg.v;
-        uint16_t* Wb = Wsb + buf * C::WB;
-        uint16_t* Xb = Xsb + buf * XB;
-#pragma unroll
-        for (int j = 0; j < WPT; ++j)
-            if (wsrc[j] >= 0) *reinterpret_cast<uint4v*>(Wb + wdst[j]) = wreg[j];
-#pragma unroll
-        for (int j = 0; j < XPT; ++j) {
-            if (xsrc[j] < 0) continue;
-#pragma unroll
-            for (int u = 0; u < PX; ++u) {
-                uint4v o;
-                o.x = pack2h(px_half<PX>(xreg[j][0], u), px_half<PX>(xreg[j][1], u));
-                o.y = pack2h(px_half<PX>(xreg[j][2], u), px_half<PX>(xreg[j][3], u));
-                o.z = pack2h(px_half<PX>(xreg[j][4], u), px_half<PX>(xreg[j][5], u));
-                o.w = pack2h(px_half<PX>(xreg[j][6], u), px_half<PX>(xreg[j][7], u));
-                *reinterpret_cast<uint4v*>(Xb + xdst[j] + u * KCS) = o;
-            }
-        }
-    };
+    for (int j = 0; j < XPT; ++j) xvo[j] = xsrc[j] >= 0 ? (unsigned)xsrc[j] * 2u : kBufOut;
 
     floatx16 acc[RM][RN];
 #pragma unroll
@@ -320,7 +327,9 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[rm][rn][r] = 0.0f;
 
-    auto mfma_stage = [&](int buf) {
+    // issue(s): the loads to issue between the fragment reads and the
+    // instructions of matrix step s
+    auto mfma_stage = [&](int buf, auto&& issue) {
         const uint16_t* Wb = Wsb + buf * C::WB;
         const uint16_t* Xb = Xsb + buf * XB;
         uint4v a[2][RM], bf[2][RN];
@@ -331,12 +340,13 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
                                                           (2 * s + lh) * 8);
 #pragma unroll
             for (int rn = 0; rn < RN; ++rn)
-                br[rn] = *reinterpret_cast<const uint4v*>(Xb + pbase[rn] * KCS + koff[s]);
+                br[rn] = *reinterpret_cast<const uint4v*>(Xb + xlane[rn] + koff[s]);
         };
         frag(0, a[0], bf[0]);
 #pragma unroll
         for (int s = 0; s < NSTEP; ++s) {
             if (s + 1 < NSTEP) frag(s + 1, a[(s + 1) & 1], bf[(s + 1) & 1]);
+            issue(s);
             // the next step's reads stay ahead of this step's instructions
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -354,28 +364,124 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     int nst = p.stages;
     if (s_first + nst > NS) nst = NS - s_first;
     __syncthreads();  // windows zeroed before any stage writes into them
-    if (nst > 0) {
-        load_w(s_first);
-        load_x(xa, s_first * KC);
-        if (nst > 1) load_x(xb, (s_first + 1) * KC);
-        store_stage(xa, 0);
-    }
-    __syncthreads();
-    // stage st: `held` has stage st+1's window, `free` takes stage st+2's
-    auto step = [&](int st, XRegs& held, XRegs& free) {
-        if (st + 1 < nst) load_w(s_first + st + 1);
-        if (st + 2 < nst) load_x(free, (s_first + st + 2) * KC);
-        // keep the loads here, ahead of the matrix steps: left free, the
-        // compiler sinks them to their LDS writes and the latency is exposed
-        asm volatile("" ::: "memory");
-        mfma_stage(st & 1);
-        if (st + 1 < nst) store_stage(held, (st + 1) & 1);
+    // Stage indices past the split's last stage are clamped to it: the loads
+    // and LDS writes of every step are unconditional (the extra ones load the
+    // last stage again and write the buffer no later stage reads).  The loop
+    // comes in two copies, for the waves that stage window tasks (HX) and for
+    // those that do not, so that in each the number of loads issued per step
+    // is fixed and the compiler waits for exactly the ones a step consumes.
+    const int last = nst - 1;
+    auto run_stages = [&](auto hx_tag) {
+        constexpr bool HX = decltype(hx_tag)::value;
+        uint4v wreg[WPT];
+        XRegs xa, xb;
+        // Load units: filter chunk j of stage s_abs (j < WPT), and window
+        // channel i of every task of the stage starting at channel c0.
+        // Channels past CI in the last image read zeros; those past CI inside
+        // the tensor are zeroed by store_stage.
+        // (descriptor fields pass through readfirstlane: they are uniform,
+        // and a descriptor the compiler cannot prove uniform costs a loop
+        // over the lanes around each load)
+        auto load_w1 = [&](int j, int s_abs) {
+            const int sb = __builtin_amdgcn_readfirstlane(s_abs * (T * KC));  // halves
+            const int nrec = __builtin_amdgcn_readfirstlane((int)(w_bytes - 2LL * sb));
+            const __amdgpu_buffer_rsrc_t wrs =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wpk + sb), 0, nrec, kBufRaw);
+            wreg[j] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo[j], 0, 0));
+        };
+        auto load_x1 = [&](XRegs& rg, int i, int c0) {
+            // one descriptor per channel (scalar work only)
+            const int cb = __builtin_amdgcn_readfirstlane((int)((long long)(c0 + i) * HW));  // halves
+            const int nrec = __builtin_amdgcn_readfirstlane((int)(x_bytes - 2LL * cb));
+            const __amdgpu_buffer_rsrc_t xrs =
+                __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xg + cb), 0, nrec, kBufRaw);
+#pragma unroll
+            for (int j = 0; j < XPT; ++j) rg.v[j][i] = BufLoad<PX>::load(xrs, xvo[j]);
+        };
+        auto load_w = [&](int s_abs) {
+#pragma unroll
+            for (int j = 0; j < WPT; ++j) load_w1(j, s_abs);
+        };
+        auto load_x = [&](XRegs& rg, int c0) {
+            if constexpr (HX) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) load_x1(rg, i, c0);
+            }
+        };
+        // The next stages' loads, spread over the matrix steps so that no
+        // wave stalls on a full memory queue with its matrix work waiting:
+        // unit u (filter chunks, then window channels) goes out at step
+        // u * NSTEP / NU.
+        constexpr int NU = WPT + (HX ? 8 : 0);
+        auto spread_loads = [&](int s, int s_w, XRegs& rg, int c0) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if (u * NSTEP / NU != s) continue;
+                if (u < WPT)
+                    load_w1(u, s_w);
+                else
+                    load_x1(rg, u - WPT, c0);
+            }
+        };
+        // LDS writes of a stage: the filter chunks and the window's pixel
+        // records (channels past CI zeroed first).  c0: the stage's first
+        // channel.
+        auto store_stage = [&](XRegs& rg, int buf, int c0) {
+            uint16_t* Wb = Wsb + buf * C::WB;
+            uint16_t* Xb = Xsb + buf * XB;
+#pragma unroll
+            for (int j = 0; j < WPT; ++j)
+                if (wvo[j] != kBufOut) *reinterpret_cast<uint4v*>(Wb + wdst[j]) = wreg[j];
+            if constexpr (HX) {
+                auto& xreg = rg.v;
+#pragma unroll
+                for (int j = 0; j < XPT; ++j) {
+                    if (xvo[j] == kBufOut) continue;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        if (c0 + xch[j] + i >= p.CI) xreg[j][i] = XV{};
+#pragma unroll
+                    for (int u = 0; u < PX; ++u) {
+                        uint4v o;
+                        o.x = pack2h(px_half<PX>(xreg[j][0], u), px_half<PX>(xreg[j][1], u));
+                        o.y = pack2h(px_half<PX>(xreg[j][2], u), px_half<PX>(xreg[j][3], u));
+                        o.z = pack2h(px_half<PX>(xreg[j][4], u), px_half<PX>(xreg[j][5], u));
+                        o.w = pack2h(px_half<PX>(xreg[j][6], u), px_half<PX>(xreg[j][7], u));
+                        *reinterpret_cast<uint4v*>(Xb + xdst[j] + u * KCS) = o;
+                    }
+                }
+            }
+        };
+        if (nst > 0) {
+            load_w(s_first);
+            load_x(xa, s_first * KC);
+            load_x(xb, (s_first + min(1, last)) * KC);
+            store_stage(xa, 0, s_first * KC);
+        }
         __syncthreads();
+        // stage st: `held` has stage st+1's window, `free` takes stage st+2's
+        auto step = [&](int st, XRegs& held, XRegs& free) {
+            const int s_w = s_first + min(st + 1, last);
+            const int c0x = (s_first + min(st + 2, last)) * KC;
+            mfma_stage(st & 1, [&](int s) { spread_loads(s, s_w, free, c0x); });
+            // LDS writes after the matrix steps: interleaved with them, the
+            // window's register transposes lengthen the matrix phase by as
+            // much as they take
+            store_stage(held, (st + 1) & 1, (s_first + min(st + 1, last)) * KC);
+            __syncthreads();
+        };
+        int st = 0;
+        for (; st + 1 < nst; st += 2) {
+            step(st, xb, xa);
+            step(st + 1, xa, xb);
+        }
+        if (st < nst) step(st, xb, xa);
     };
-    for (int st = 0; st < nst; st += 2) {
-        step(st, xb, xa);
-        if (st + 1 < nst) step(st + 1, xa, xb);
-    }
+    // wave-uniform: does this wave hold any window task (task q = tid + j*NT)?
+    if (wave * 64 < n_xt)
+        run_stages(std::true_type{});
+    else
+        run_stages(std::false_type{});
 
     // ---- split reduction across workgroups (device-scope atomics) -------------
     const int wslot = wm + wn * WM;
@@ -456,8 +562,10 @@ int h2_bytes_for(const ConvParams& p, int px) {
     if (p.P >= (1LL << 31) || (long long)p.N * p.Hp >= (1LL << 31)) return 1 << 30;
     const long long CIp = round_up(p.CI, KC);
     const long long COp = round_up(p.CO, kPackCO);
-    // reordered filter offsets are 32-bit
-    if (COp * CIp * T >= (1LL << 31)) return 1 << 30;
+    // x and the reordered filter are read through buffer descriptors with
+    // 32-bit byte offsets; offset 2^31 must lie past both
+    if (COp * CIp * T * 2 >= (1LL << 31)) return 1 << 30;
+    if ((long long)p.N * p.CI * p.H * p.W * 2 >= (1LL << 31)) return 1 << 30;
     // the window tasks must fit the per-thread slots
     if ((long long)C::CG * p.R * (p.W / px) > (long long)C::XPT * C::NT) return 1 << 30;
     if ((long long)p.R * p.Wp * C::KCS >= (1LL << 28)) return 1 << 30;
