@@ -541,7 +541,9 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
 #pragma unroll
             for (int rn = 0; rn < RN; ++rn) {
                 if (yoff[rn] < 0) continue;
-                p.y[yoff[rn] + (long long)co * p.OHW] = apply_epilogue(p.epilogue, acc[rm][rn][r], eb, er);
+                // streamed out: the results are not read again by this launch
+                __builtin_nontemporal_store(apply_epilogue(p.epilogue, acc[rm][rn][r], eb, er),
+                                            &p.y[yoff[rn] + (long long)co * p.OHW]);
             }
         }
     }
