@@ -105,23 +105,28 @@ template <> struct PxVec<4> { typedef uint2v T; };
 template <> struct PxVec<2> { typedef uint32_t T; };
 template <> struct PxVec<1> { typedef uint16_t T; };
 
-template <int PX>
-__device__ __forceinline__ uint16_t px_half(const typename PxVec<PX>::T& v, int u) {
-    if constexpr (PX == 8) {
-        const uint32_t d = v[u >> 1];
-        return (u & 1) ? (uint16_t)(d >> 16) : (uint16_t)(d & 0xffffu);
-    } else if constexpr (PX == 4) {
-        const uint32_t d = v[u >> 1];
-        return (u & 1) ? (uint16_t)(d >> 16) : (uint16_t)(d & 0xffffu);
-    } else if constexpr (PX == 2) {
-        return (u & 1) ? (uint16_t)(v >> 16) : (uint16_t)(v & 0xffffu);
-    } else {
-        return v;
-    }
-}
-
 __device__ __forceinline__ uint32_t pack2h(uint16_t lo, uint16_t hi) {
     return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// Pixel u of two channels' vectors a and b, packed as (a[u], b[u]): for
+// PX >= 2 one byte permute (v_perm_b32: bytes 0-3 of its second operand,
+// 4-7 of its first) of the two 32-bit words that hold pixel u.
+template <int PX>
+__device__ __forceinline__ uint32_t pack_px(const typename PxVec<PX>::T& a, const typename PxVec<PX>::T& b, int u) {
+    if constexpr (PX == 1) {
+        return pack2h(a, b);
+    } else {
+        uint32_t da, db;
+        if constexpr (PX == 2) {
+            da = a;
+            db = b;
+        } else {
+            da = a[u >> 1];
+            db = b[u >> 1];
+        }
+        return __builtin_amdgcn_perm(db, da, (u & 1) ? 0x07060302u : 0x05040100u);
+    }
 }
 
 // Raw buffer load of PX halves at byte offset off.
@@ -443,10 +448,10 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
 #pragma unroll
                     for (int u = 0; u < PX; ++u) {
                         uint4v o;
-                        o.x = pack2h(px_half<PX>(xreg[j][0], u), px_half<PX>(xreg[j][1], u));
-                        o.y = pack2h(px_half<PX>(xreg[j][2], u), px_half<PX>(xreg[j][3], u));
-                        o.z = pack2h(px_half<PX>(xreg[j][4], u), px_half<PX>(xreg[j][5], u));
-                        o.w = pack2h(px_half<PX>(xreg[j][6], u), px_half<PX>(xreg[j][7], u));
+                        o.x = pack_px<PX>(xreg[j][0], xreg[j][1], u);
+                        o.y = pack_px<PX>(xreg[j][2], xreg[j][3], u);
+                        o.z = pack_px<PX>(xreg[j][4], xreg[j][5], u);
+                        o.w = pack_px<PX>(xreg[j][6], xreg[j][7], u);
                         *reinterpret_cast<uint4v*>(Xb + xdst[j] + u * KCS) = o;
                     }
                 }
