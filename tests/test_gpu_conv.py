@@ -165,13 +165,14 @@ def _skc_configs(w):
     return [c for c in legal_configs(w) if ct.variants()[c.variant]["name"].startswith(("f32skc", "f32skt"))]
 
 
-@pytest.mark.parametrize("misaligned", [False, True], ids=["aligned", "x_offset_4B"])
+@pytest.mark.parametrize("misaligned", ["none", "x", "y"], ids=["aligned", "x_offset_4B", "y_offset_4B"])
 @pytest.mark.parametrize("epi", [ct.CT_EPI_NONE, ct.CT_EPI_BIAS, ct.CT_EPI_EXP_BIAS_RSQRT])
 @pytest.mark.parametrize("w", SKC_LAYERS, ids=lambda w: w.name)
 def test_shape_specialised_split_k(w, epi, misaligned):
     """Every legal config of the shape-specialised kernels against the oracle:
-    conv gate, epilogue gates, and an input that is not 16-byte aligned (the
-    kernels then load the window word by word)."""
+    conv gate, epilogue gates, an input that is not 16-byte aligned (the
+    kernels then load the window word by word) and an output that is not
+    (16-byte stores fall back to words)."""
     w = w.with_(epilogue=epi)
     cfgs = _skc_configs(w)
     say(f"[conv-skc] {w.name} epi={epi} misaligned={misaligned}: {len(cfgs)} configs")
@@ -182,7 +183,7 @@ def test_shape_specialised_split_k(w, epi, misaligned):
         y, epi, inp["bias"].astype(np.float64), inp["var"].astype(np.float64), 1e-5)
     S = float(a.max())
     xd = to_dev(inp["x"], w.dtype)
-    if misaligned:
+    if misaligned == "x":
         buf = torch.empty(xd.numel() + 1, dtype=xd.dtype, device=DEV)
         buf[1:].copy_(xd.reshape(-1))
         xd = buf[1:].view(xd.shape)
@@ -191,8 +192,16 @@ def test_shape_specialised_split_k(w, epi, misaligned):
     b = torch.from_numpy(inp["bias"]).to(DEV)
     v = torch.from_numpy(inp["var"]).to(DEV)
     for cfg in cfgs:
-        got = ct.conv2d(xd, k, w.stride, w.pad, epi, b, v, 1e-5, config=cfg)
+        out = None
+        if misaligned == "y":
+            ybuf = torch.full((w.N * w.CO * w.OH * w.OW + 1,), float("nan"), device=DEV)
+            out = ybuf[1:].view(w.N, w.CO, w.OH, w.OW)
+            assert out.data_ptr() % 16 != 0
+        got = ct.conv2d(xd, k, w.stride, w.pad, epi, b, v, 1e-5, config=cfg, out=out)
         torch.cuda.synchronize()
+        if out is not None:
+            assert got.data_ptr() == out.data_ptr()
+            assert torch.isnan(ybuf[:1]).all(), "a store landed before the output"
         got = got.cpu().numpy().astype(np.float64)
         what = (ct.variants()[cfg.variant]["name"], cfg.split_k, cfg.stages, cfg.kc)
         assert np.all(np.isfinite(got)), what
