@@ -248,7 +248,7 @@ def bench_broadcast(a, name: str) -> dict:
 def main():
     a = _parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     _ensure_built()
