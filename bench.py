@@ -145,6 +145,25 @@ def cpu_baseline(w, seconds: float) -> dict:
     x = inp["x"].astype(np.float64)
     k = inp["w"].astype(np.float64)
     cores = host_threads()
+    if w.flops > 4e9:
+        # a whole pass would take minutes: time the oracle's one-output-at-a-
+        # time routine on random outputs instead, doubling the sample until
+        # about `seconds` have elapsed
+        per_point = 2 * w.CI * w.KH * w.KW
+        r = np.random.default_rng(0)
+        npts, el = 1024, 0.0
+        while True:
+            idx = np.stack([r.integers(0, d, npts) for d in (w.N, w.CO, w.OH, w.OW)], axis=1)
+            t0 = time.perf_counter()
+            O.conv2d_points(x, k, w.stride, w.pad, idx.astype(np.int64))
+            el = time.perf_counter() - t0
+            if el >= seconds / 2 or npts >= 1 << 26:
+                break
+            npts *= 2
+        return {"value": round(per_point * npts / el / 1e12, 5), "unit": "TFLOP/s", "cores": cores,
+                "kind": "oracle",
+                "sample": f"{npts} random outputs of {w.name} ({per_point} FLOP each) through the "
+                          f"fp64 oracle's per-output routine in {el:.1f} s"}
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -157,6 +176,28 @@ def cpu_baseline(w, seconds: float) -> dict:
     return {"value": round(tflops, 5), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{reps} full passes of the fp64 seven-loop oracle (OpenMP over n, f) "
                       f"on {w.name} in {el:.1f} s"}
+
+
+def cpu_baseline_gemm(g, seconds: float) -> dict:
+    """The fp64 matrix-product oracle on this host's cores, whole products of
+    the same workload repeated until about `seconds` have elapsed."""
+    from oracle import oracle as O
+    from tensor_compiler_tiling_amd import workloads as wl
+    inp = wl.gemm_inputs(g)
+    A = inp["A"].astype(np.float64)
+    B = inp["B"].astype(np.float64)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.gemm(A, B)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    # the oracle also forms sum |A||B| (a second product): count both
+    return {"value": round(2 * g.flops * reps / el / 1e12, 5), "unit": "TFLOP/s",
+            "cores": host_threads(), "kind": "oracle",
+            "sample": f"{reps} full fp64 products (C and its |A||B| scale) of {g.name} in {el:.1f} s"}
 
 
 def cpu_baseline_broadcast(bw, seconds: float) -> dict:
@@ -263,7 +304,11 @@ def main():
     if name in wl.BROADCAST_WORKLOADS:
         print(json.dumps(bench_broadcast(a, name)), flush=True)
         return
-    w = wl.CONV_WORKLOADS[name]
+    gemm = wl.GEMM_WORKLOADS.get(name)
+    # a matrix product is timed through ct_gemm_fwd; its 1x1 convolution view
+    # gives the seeded operands (A = the view's filter, B = its input) and the
+    # CPU baseline
+    w = gemm.conv_view() if gemm is not None else wl.CONV_WORKLOADS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
@@ -283,12 +328,19 @@ def main():
     tune_info = None
     if a.tune:
         t0 = time.perf_counter()
-        st, best, recs = ct.ct_conv2d_tune(*args, max_trials=a.tune_trials,
-                                           min_repeat_ms=a.tune_ms)
+        if gemm is not None:
+            st, best, recs = ct.ct_gemm_tune(gemm.M, gemm.N, gemm.K, dt, w.epilogue,
+                                             max_trials=a.tune_trials, min_repeat_ms=a.tune_ms)
+        else:
+            st, best, recs = ct.ct_conv2d_tune(*args, max_trials=a.tune_trials,
+                                               min_repeat_ms=a.tune_ms)
         ct.check(st, "tune")
         tune_info = {"trials": len(recs), "seconds": round(time.perf_counter() - t0, 2),
                      "best_us": round(best.us, 3)}
-    st, cfg, from_cache = ct.ct_conv2d_query(*args)
+    if gemm is not None:
+        st, cfg, from_cache = ct.ct_gemm_query(gemm.M, gemm.N, gemm.K, dt, w.epilogue)
+    else:
+        st, cfg, from_cache = ct.ct_conv2d_query(*args)
     ct.check(st, "query")
     vdesc = ct.variants()[cfg.variant]
 
@@ -302,8 +354,12 @@ def main():
     def step():
         # the stream current at call time: inside graph capture it is the
         # capture stream
-        st = lib.ct_conv2d_nchw_fwd(xp, kp, yp, *args, bp, vp, 1e-5,
-                                    torch.cuda.current_stream().cuda_stream)
+        if gemm is not None:
+            st = lib.ct_gemm_fwd(kp, xp, yp, gemm.M, gemm.N, gemm.K, dt, w.epilogue, bp, vp, 1e-5,
+                                 torch.cuda.current_stream().cuda_stream)
+        else:
+            st = lib.ct_conv2d_nchw_fwd(xp, kp, yp, *args, bp, vp, 1e-5,
+                                        torch.cuda.current_stream().cuda_stream)
         if st != 0:
             raise ct.ConvTileError(st, "fwd")
 
@@ -349,9 +405,14 @@ def main():
         torch.cuda.synchronize()
         eager_ms = e0.elapsed_time(e1) / a.steps
 
+    if gemm is not None:
+        metric = "matrix product TFLOP/s and % of MFMA peak"
+    elif w.dtype == "f32":
+        metric = "conv2d TFLOP/s per shape (fp32, batch 1) and % of MFMA peak"
+    else:
+        metric = "conv2d TFLOP/s per shape and % of MFMA peak"
     out = {
-        "metric": "conv2d TFLOP/s per shape (fp32, batch 1) and % of MFMA peak"
-                  if w.dtype == "f32" else "conv2d TFLOP/s per shape and % of MFMA peak",
+        "metric": metric,
         "value": round(tflops, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -365,6 +426,7 @@ def main():
         "data": "synthetic (seeded U[-1,1] inputs, He-normal weights)",
         "config": {"workload": name, "N": w.N, "CI": w.CI, "H": w.H, "W": w.W, "CO": w.CO,
                    "KH": w.KH, "KW": w.KW, "stride": w.stride, "pad": w.pad,
+                   **({"M": gemm.M, "gemm_N": gemm.N, "K": gemm.K} if gemm is not None else {}),
                    "epilogue": w.epilogue, "flops_per_step": w.flops,
                    "launch": "hip_graph" if graph is not None else "eager",
                    "kernel": vdesc["name"], "split_k": cfg.split_k, "stages": cfg.stages,
@@ -382,7 +444,8 @@ def main():
     if tune_info:
         out["tune"] = tune_info
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
+        out["cpu_baseline"] = (cpu_baseline_gemm(gemm, a.cpu_seconds) if gemm is not None
+                               else cpu_baseline(w, a.cpu_seconds))
     print(json.dumps(out), flush=True)
 
 

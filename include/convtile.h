@@ -144,6 +144,31 @@ int ct_conv2d_nchw_direct(const void* x, const void* w, float* y,
                           const float* bias, const float* var, float eps,
                           void* stream);
 
+/* ---- matrix product (the 1x1-convolution view) -----------------------
+ * The TVM tutorial notes, in its opening, that the same tiled template also
+ * serves a matrix product.  Here that is literal:
+ *
+ *   C[m][n] = sum_{k<K} A[m][k] * B[k][n]      (row-major, all contiguous)
+ *
+ * is the batch-1 convolution with a 1x1 filter, CO = M, CI = K and H*W = N:
+ * w = A as [M][K][1][1], x = B as [1][K][H][W], y = C as [1][M][H][W] (a 1x1
+ * filter sees pixels only as a flat index, so every split of N has the same
+ * layout; W is the largest divisor of N not above 256).  A and B
+ * have dtype `dtype` (CT_F32 / CT_F16 / CT_BF16), C is float.  The epilogue is
+ * per row m (bias[m], var[m]).  Tuned configs are cached under that
+ * convolution's shape, so ct_conv2d_tune and ct_gemm_tune share records.
+ * Errors: CT_ERR_INVALID_ARG for M, N or K <= 0; otherwise those of
+ * ct_conv2d_nchw_fwd / ct_conv2d_tune / ct_conv2d_query. */
+int ct_gemm_fwd(const void* A, const void* B, float* C, int M, int N, int K,
+                int dtype, int epilogue, const float* bias, const float* var,
+                float eps, void* stream);
+int ct_gemm_tune(int M, int N, int K, int dtype, int epilogue,
+                 int max_trials, float min_repeat_ms, void* stream,
+                 ct_tile_config* best_out,
+                 ct_tune_record* records, int max_records, int* n_records);
+int ct_gemm_query(int M, int N, int K, int dtype, int epilogue,
+                  ct_tile_config* cfg_out, int* from_cache);
+
 /* ---- tile-config search ----------------------------------------------
  * The space of a shape follows the TVM tutorial's template (Step 1): ordered
  * knobs, each a split (all ordered factorizations of an extent, the

@@ -17,7 +17,10 @@ What it holds:
   mixed-radix flat index of a config entity, and the shared-memory footprint
   of the tutorial's schedule template;
 * the FLOP count of a convolution (2 x multiply-accumulates, padded taps
-  included).
+  included);
+* the matrix product C = A B in fp64 (its definition, with a library matmul
+  of fp64 arrays as the one step), which the TVM tutorial's opening names as a
+  second use of its template.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` (hand-computed cases, closed forms, invariants,
@@ -134,6 +137,16 @@ def conv2d_points(x, w, stride: int, pad: int, idx) -> Tuple[np.ndarray, np.ndar
 
 
 EPI_NONE, EPI_BIAS, EPI_EXP_BIAS_RSQRT = 0, 1, 2
+
+
+def gemm(A, B) -> Tuple[np.ndarray, np.ndarray]:
+    """C[m][n] = sum_k A[m][k] * B[k][n] in fp64, and sum_k |A[m][k] * B[k][n]|
+    (the tolerance scale, as conv2d_nchw's absacc).  A [M, K], B [K, N]."""
+    a = _f64(A)
+    b = _f64(B)
+    if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("gemm: A must be [M, K] and B [K, N]")
+    return a @ b, np.abs(a) @ np.abs(b)
 
 
 def channel_epilogue(y, kind: int, b=None, v=None, eps: float = 1e-5) -> np.ndarray:

@@ -81,6 +81,10 @@ _SIGS = {
     "ct_conv2d_tune": (_I, _SHAPE + [_I, _F, _P, ctypes.POINTER(ct_tile_config),
                                      ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
     "ct_conv2d_query": (_I, _SHAPE + [ctypes.POINTER(ct_tile_config), ctypes.POINTER(_I)]),
+    "ct_gemm_fwd": (_I, [_P, _P, _P] + [_I] * 5 + [_P, _P, _F, _P]),
+    "ct_gemm_tune": (_I, [_I] * 5 + [_I, _F, _P, ctypes.POINTER(ct_tile_config),
+                                   ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
+    "ct_gemm_query": (_I, [_I] * 5 + [ctypes.POINTER(ct_tile_config), ctypes.POINTER(_I)]),
     "ct_variant_count": (_I, []),
     "ct_variant_info": (_I, [_I, ctypes.POINTER(ct_variant_desc)]),
     "ct_split_count": (_LL, [_LL, _I]),
@@ -214,6 +218,28 @@ def ct_conv2d_query(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue):
     return st, cfg, fc.value
 
 
+def ct_gemm_fwd(A, B, C, M, N, K, dtype, epilogue, bias=None, var=None, eps=1e-5, stream=None) -> int:
+    return _load().ct_gemm_fwd(_ptr(A), _ptr(B), _ptr(C), M, N, K, dtype, epilogue, _ptr(bias),
+                               _ptr(var), eps, _stream(stream))
+
+
+def ct_gemm_tune(M, N, K, dtype, epilogue, max_trials=0, min_repeat_ms=100.0, stream=None,
+                 max_records=4096):
+    best = ct_tile_config()
+    recs = (ct_tune_record * max(max_records, 1))()
+    n = _I(0)
+    st = _load().ct_gemm_tune(M, N, K, dtype, epilogue, max_trials, min_repeat_ms, _stream(stream),
+                              ctypes.byref(best), recs, max_records, ctypes.byref(n))
+    return st, best, [recs[i] for i in range(n.value)]
+
+
+def ct_gemm_query(M, N, K, dtype, epilogue):
+    cfg = ct_tile_config()
+    fc = _I(0)
+    st = _load().ct_gemm_query(M, N, K, dtype, epilogue, ctypes.byref(cfg), ctypes.byref(fc))
+    return st, cfg, fc.value
+
+
 def ct_variant_count() -> int:
     return _load().ct_variant_count()
 
@@ -318,6 +344,20 @@ def conv2d(x, w, stride: int = 1, pad: int = 0, epilogue: int = CT_EPI_NONE, bia
                                 var, eps, stream)
     check(st, "conv2d")
     return y
+
+
+def gemm(A, B, epilogue: int = CT_EPI_NONE, bias=None, var=None, eps: float = 1e-5, out=None,
+         stream=None):
+    """C = A @ B (+ per-row epilogue), fp32 output allocated with torch: A [M, K], B [K, N],
+    same dtype, contiguous."""
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or A.dtype != B.dtype:
+        raise ValueError("A and B disagree in the inner dimension or dtype")
+    C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=A.device)
+    check(ct_gemm_fwd(A, B, C, M, N, K, dtype_code(A.dtype), epilogue, bias, var, eps, stream), "gemm")
+    return C
 
 
 def broadcast(var, N: int, H: int, W: int, out_dtype=None, mode: int = CT_BC_AUTO, out=None,

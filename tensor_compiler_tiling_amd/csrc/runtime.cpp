@@ -807,6 +807,47 @@ int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y, int N, int CI, in
     return launch_tiled(s, c, x, w, y, bias, var, eps, hs);
 }
 
+// Matrix product as the batch-1 1x1 convolution: C[M][N] = A[M][K] B[K][N]
+// is y with w = A ([CO=M][CI=K][1][1]) and x = B ([1][CI=K][H][W], H*W = N:
+// a 1x1 filter sees the pixels only as a flat index, so the layout is the
+// same for every split of N).  W is the largest divisor of N not above 256,
+// which keeps the kernels' image-row windows small.
+static int gemm_args(int M, int N, int K, int* H, int* W) {
+    if (M <= 0 || N <= 0 || K <= 0) return fail(CT_ERR_INVALID_ARG, "M, N and K must be positive (got %d, %d, %d)", M, N, K);
+    for (int w = std::min(N, 256); w >= 1; --w)
+        if (N % w == 0) {
+            *W = w;
+            *H = N / w;
+            break;
+        }
+    return CT_OK;
+}
+
+int ct_gemm_fwd(const void* A, const void* B, float* C, int M, int N, int K, int dtype, int epilogue,
+                const float* bias, const float* var, float eps, void* stream) {
+    int H = 1, W = N;
+    const int st = gemm_args(M, N, K, &H, &W);
+    if (st != CT_OK) return st;
+    return ct_conv2d_nchw_fwd(B, A, C, 1, K, H, W, M, 1, 1, 1, 0, dtype, epilogue, bias, var, eps, stream);
+}
+
+int ct_gemm_tune(int M, int N, int K, int dtype, int epilogue, int max_trials, float min_repeat_ms,
+                 void* stream, ct_tile_config* best_out, ct_tune_record* records, int max_records,
+                 int* n_records) {
+    int H = 1, W = N;
+    const int st = gemm_args(M, N, K, &H, &W);
+    if (st != CT_OK) return st;
+    return ct_conv2d_tune(1, K, H, W, M, 1, 1, 1, 0, dtype, epilogue, max_trials, min_repeat_ms, stream,
+                          best_out, records, max_records, n_records);
+}
+
+int ct_gemm_query(int M, int N, int K, int dtype, int epilogue, ct_tile_config* cfg_out, int* from_cache) {
+    int H = 1, W = N;
+    const int st = gemm_args(M, N, K, &H, &W);
+    if (st != CT_OK) return st;
+    return ct_conv2d_query(1, K, H, W, M, 1, 1, 1, 0, dtype, epilogue, cfg_out, from_cache);
+}
+
 int ct_conv2d_nchw_fwd_config(const void* x, const void* w, float* y, int N, int CI, int H, int W,
                               int CO, int KH, int KW, int stride, int pad, int dtype, int epilogue,
                               const float* bias, const float* var, float eps,

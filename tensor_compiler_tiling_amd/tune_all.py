@@ -1,5 +1,5 @@
-"""Run the tile-config search over the named convolution workloads and save
-the winners as a JSON-lines tuning log.
+"""Run the tile-config search over the named convolution (and matrix-product)
+workloads and save the winners as a JSON-lines tuning log.
 
 This is the library's counterpart of the TVM tutorial's tune-then-apply flow
 (Tune the Convolution on CUDA, "Start tuning" and the history-best step): the
@@ -9,7 +9,9 @@ with ct_cache_load so that ct_conv2d_nchw_fwd dispatches to it.
 
     python -m tensor_compiler_tiling_amd.tune_all [--out PATH] [--ms MS] [names...]
 
-With no names every convolution workload is tuned and the log is rewritten;
+A matrix-product workload is tuned through ct_gemm_tune, i.e. as its 1x1
+convolution view, under which ct_gemm_fwd finds the record.
+With no names every workload is tuned and the log is rewritten;
 with names, the log's records of the other shapes are kept.  The default
 output is the log shipped with the package for gfx950 (tuned/gfx950.jsonl).
 """
@@ -37,17 +39,22 @@ def main(argv=None) -> int:
     from tensor_compiler_tiling_amd import convtile as ct
     from tensor_compiler_tiling_amd import workloads as wl
 
-    names = a.names or list(wl.CONV_WORKLOADS)
+    names = a.names or (list(wl.CONV_WORKLOADS) + list(wl.GEMM_WORKLOADS))
     ct.check(ct.ct_cache_clear(), "cache clear")
     if a.names and os.path.exists(a.out):
         # retuning some shapes: keep the log's records of the others
         ct.check(ct.ct_cache_load(a.out), "cache load")
     for name in names:
-        w = wl.CONV_WORKLOADS[name]
+        g = wl.GEMM_WORKLOADS.get(name)
+        w = g if g is not None else wl.CONV_WORKLOADS[name]
         tdt = {wl.F32: torch.float32, wl.F16: torch.float16, wl.BF16: torch.bfloat16}[w.dtype]
-        args = w.shape_args() + (ct.dtype_code(tdt), w.epilogue)
         t0 = time.perf_counter()
-        st, best, recs = ct.ct_conv2d_tune(*args, max_trials=a.trials, min_repeat_ms=a.ms)
+        if g is not None:
+            st, best, recs = ct.ct_gemm_tune(g.M, g.N, g.K, ct.dtype_code(tdt), g.epilogue,
+                                             max_trials=a.trials, min_repeat_ms=a.ms)
+        else:
+            args = w.shape_args() + (ct.dtype_code(tdt), w.epilogue)
+            st, best, recs = ct.ct_conv2d_tune(*args, max_trials=a.trials, min_repeat_ms=a.ms)
         ct.check(st, f"tune {name}")
         vname = ct.variants()[best.variant]["name"]
         print(json.dumps({"workload": name, "trials": len(recs),

@@ -105,6 +105,54 @@ CONV_WORKLOADS: Dict[str, ConvWorkload] = {w.name: w for w in [
                  EPI_EXP_BIAS_RSQRT),
 ]}
 
+def gemm_fold(N: int):
+    """(H, W) with H * W = N and W the largest divisor of N not above 256: the
+    image a row-major [K][N] operand is viewed as (the library's own split)."""
+    for w in range(min(N, 256), 0, -1):
+        if N % w == 0:
+            return N // w, w
+    raise ValueError("N must be positive")
+
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    """C[M][N] = A[M][K] B[K][N] (row-major), the batch-1 1x1 convolution with
+    CO = M, CI = K, H * W = N (A = its filter, B = its input)."""
+    name: str
+    cfg_id: int
+    M: int
+    N: int
+    K: int
+    dtype: str = F32
+    epilogue: int = EPI_NONE
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def conv_view(self) -> ConvWorkload:
+        H, W = gemm_fold(self.N)
+        return ConvWorkload(self.name, self.cfg_id, 1, self.K, H, W, self.M, 1, 1, 1, 0, self.dtype,
+                            self.epilogue)
+
+
+# Matrix products on the same kernels (the 1x1 view): a square fp16 product
+# and an fp32 one with the per-row epilogue.
+GEMM_WORKLOADS: Dict[str, GemmWorkload] = {g.name: g for g in [
+    GemmWorkload("gemm_f16_m4096_n4096_k4096", 60, 4096, 4096, 4096, F16),
+    GemmWorkload("gemm_f32_m2048_n2048_k2048_epi", 61, 2048, 2048, 2048, F32, EPI_EXP_BIAS_RSQRT),
+]}
+
+
+def gemm_inputs(g: GemmWorkload) -> dict:
+    """A [M, K] (He-normal over K) and B [K, N] (U[-1, 1]), rounded to g.dtype,
+    and the per-row bias / var: the 1x1 view's filter, input and epilogue
+    parameters, so both views see the same values."""
+    c = conv_inputs(g.conv_view())
+    return {"A": c["w"].reshape(g.M, g.K), "B": c["x"].reshape(g.K, g.N), "bias": c["bias"],
+            "var": c["var"]}
+
+
 HEADLINE = "resnet_final_c512_7x7_k3"
 SWEEP = [n for n, w in CONV_WORKLOADS.items() if w.cfg_id >= 30]
 

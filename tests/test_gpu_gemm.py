@@ -1,0 +1,152 @@
+"""GPU parity of the matrix-product entry point (the 1x1-convolution view)
+against the fp64 oracle, through the C ABI.
+
+Gates as for the convolution: max |gpu - ref| <= 1e-4 * S for fp32 operands
+and 1e-2 * S for fp16 / bf16, S = max over outputs of sum_k |A[m][k] B[k][n]|
+(the oracle's absacc); the exp-bias-rsqrt epilogue is gated relatively;
+bit-exact output for small-integer operands.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tensor_compiler_tiling_amd import convtile as ct
+from tensor_compiler_tiling_amd import workloads as wl
+
+from _gpu_helpers import CT_DT, DEV, TOL, legal_configs, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# (M, N, K): the degenerate 1x1x1, ragged sizes that fit no tile, N with no
+# divisor up to 256 (a 1-row view), N that folds into several rows, and sizes
+# that span several tiles in every dimension
+SHAPES = [(1, 1, 1), (37, 53, 29), (100, 1000, 300), (257, 130, 513), (128, 256, 64),
+          (300, 263, 70)]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU test run without a GPU"
+    torch.cuda.init()
+    ct.ct_cache_clear()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(M, N, K, dtype, seed):
+    return wl.gemm_inputs(wl.GemmWorkload(f"gemm_{M}x{N}x{K}", seed, M, N, K, dtype))
+
+
+def _ref(inp, epi):
+    C, absacc = O.gemm(inp["A"].astype(np.float64), inp["B"].astype(np.float64))
+    if epi != ct.CT_EPI_NONE:
+        # per row m: the channel of the 1x1 view
+        C = O.channel_epilogue(C.reshape(1, C.shape[0], C.shape[1], 1), epi,
+                               inp["bias"].astype(np.float64), inp["var"].astype(np.float64),
+                               1e-5).reshape(C.shape)
+    return C, absacc
+
+
+def _check(got, ref, absacc, dtype, epi, what):
+    assert got.shape == ref.shape and np.all(np.isfinite(got)), what
+    scale = float(absacc.max())
+    if epi == ct.CT_EPI_EXP_BIAS_RSQRT:
+        rel = float((np.abs(got - ref) / np.abs(ref)).max())
+        say(f"  {what}: max rel = {rel:.3e}")
+        assert rel <= TOL[dtype] * scale + 1e-5, (what, rel)
+    else:
+        err = float(np.abs(got - ref).max())
+        say(f"  {what}: max|gpu-ref| = {err:.3e} (gate {TOL[dtype] * scale:.3e})")
+        assert err <= TOL[dtype] * scale, (what, err)
+
+
+@pytest.mark.parametrize("epi", [ct.CT_EPI_NONE, ct.CT_EPI_EXP_BIAS_RSQRT])
+@pytest.mark.parametrize("dtype", [wl.F32, wl.F16, wl.BF16])
+@pytest.mark.parametrize("mnk", SHAPES, ids=lambda t: "x".join(map(str, t)))
+def test_gemm_vs_oracle(mnk, dtype, epi):
+    M, N, K = mnk
+    inp = _inputs(M, N, K, dtype, 70)
+    ref, absacc = _ref(inp, epi)
+    A, B = to_dev(inp["A"], dtype), to_dev(inp["B"], dtype)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    v = torch.from_numpy(inp["var"]).to(DEV)
+    st, cfg, _ = ct.ct_gemm_query(M, N, K, CT_DT[dtype], epi)
+    assert st == 0
+    C = ct.gemm(A, B, epi, b, v, 1e-5)
+    torch.cuda.synchronize()
+    _check(C.cpu().numpy().astype(np.float64), ref, absacc, dtype, epi,
+           f"{M}x{N}x{K} {dtype} epi={epi} {ct.variants()[cfg.variant]['name']}")
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.F16])
+def test_gemm_small_integers_bit_exact(dtype):
+    """Integer operands in [-2, 2]: every partial sum is exact in fp32, so the
+    product is exact whatever the kernel's summation order."""
+    M, N, K = 150, 300, 200
+    r = np.random.default_rng(71)
+    A = r.integers(-2, 3, (M, K)).astype(np.float32)
+    B = r.integers(-2, 3, (K, N)).astype(np.float32)
+    C = ct.gemm(to_dev(wl.to_dtype(A, dtype), dtype), to_dev(wl.to_dtype(B, dtype), dtype))
+    torch.cuda.synchronize()
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), O.gemm(A, B)[0])
+
+
+@pytest.mark.parametrize("dtype", [wl.F32, wl.F16])
+def test_gemm_view_every_legal_config(dtype):
+    """Every legal tile config of the folded 1x1 convolution (the configs the
+    matrix product chooses among) computes the same product."""
+    M, N, K = 100, 1000, 300
+    g = wl.GemmWorkload("gemm_view", 72, M, N, K, dtype)
+    w = g.conv_view()
+    inp = wl.gemm_inputs(g)
+    ref, absacc = _ref(inp, ct.CT_EPI_NONE)
+    x = to_dev(inp["B"].reshape(1, K, w.H, w.W), dtype)
+    k = to_dev(inp["A"].reshape(M, K, 1, 1), dtype)
+    cfgs = legal_configs(w)
+    say(f"[gemm-view] {M}x{N}x{K} {dtype} as 1x{K}x{w.H}x{w.W}: {len(cfgs)} legal configs")
+    assert cfgs
+    for cfg in cfgs:
+        y = ct.conv2d(x, k, 1, 0, config=cfg)
+        torch.cuda.synchronize()
+        _check(y.cpu().numpy().astype(np.float64).reshape(M, N), ref, absacc, dtype, ct.CT_EPI_NONE,
+               f"{ct.variants()[cfg.variant]['name']} S={cfg.split_k} st={cfg.stages} kc={cfg.kc}")
+
+
+def test_gemm_tune_then_query():
+    """ct_gemm_tune keeps a winner that ct_gemm_query then reports from the
+    cache, and the product through it matches the oracle."""
+    M, N, K, dtype = 256, 512, 384, wl.F16
+    st, best, recs = ct.ct_gemm_tune(M, N, K, CT_DT[dtype], ct.CT_EPI_NONE, max_trials=8,
+                                     min_repeat_ms=2.0)
+    assert st == 0 and recs
+    st, cfg, from_cache = ct.ct_gemm_query(M, N, K, CT_DT[dtype], ct.CT_EPI_NONE)
+    assert st == 0 and from_cache == 1
+    assert (cfg.variant, cfg.split_k, cfg.stages, cfg.kc) == (best.variant, best.split_k, best.stages,
+                                                             best.kc)
+    inp = _inputs(M, N, K, dtype, 73)
+    ref, absacc = _ref(inp, ct.CT_EPI_NONE)
+    C = ct.gemm(to_dev(inp["A"], dtype), to_dev(inp["B"], dtype))
+    torch.cuda.synchronize()
+    _check(C.cpu().numpy().astype(np.float64), ref, absacc, dtype, ct.CT_EPI_NONE, "after tune")
+
+
+@pytest.mark.parametrize("name", list(wl.GEMM_WORKLOADS))
+def test_gemm_full_size(name):
+    """The benchmarked products at full size, in the configuration bench.py
+    times (the shipped tuning log), every entry against the oracle (an fp64
+    product of this size takes the host seconds)."""
+    g = wl.GEMM_WORKLOADS[name]
+    cache = wl.__file__.replace("workloads.py", "tuned/gfx950.jsonl")
+    ct.check(ct.ct_cache_load(cache), "cache load")
+    inp = wl.gemm_inputs(g)
+    A, B = to_dev(inp["A"], g.dtype), to_dev(inp["B"], g.dtype)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    v = torch.from_numpy(inp["var"]).to(DEV)
+    st, cfg, from_cache = ct.ct_gemm_query(g.M, g.N, g.K, CT_DT[g.dtype], g.epilogue)
+    assert st == 0
+    C = ct.gemm(A, B, g.epilogue, b, v, 1e-5)
+    torch.cuda.synchronize()
+    ref, absacc = _ref(inp, g.epilogue)
+    _check(C.cpu().numpy().astype(np.float64), ref, absacc, g.dtype, g.epilogue,
+           f"{name} {ct.variants()[cfg.variant]['name']} (from cache: {from_cache})")

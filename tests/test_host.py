@@ -63,6 +63,35 @@ def test_invalid_shapes_rejected_before_any_hip_call(bad):
     assert ct.ct_conv2d_space_size(*args) == ct.CT_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("mnk", [(0, 4, 4), (4, 0, 4), (4, 4, 0), (-1, 4, 4)])
+def test_gemm_invalid_sizes_rejected_before_any_hip_call(mnk):
+    M, N, K = mnk
+    # fake non-null pointers: the call must fail on the sizes before touching them
+    st = ct.library().ct_gemm_fwd(16, 16, 16, M, N, K, 0, 0, 16, 16, 1e-5, None)
+    assert st == ct.CT_ERR_INVALID_ARG
+    assert "M, N and K" in ct.ct_last_error()
+    st, _, _ = ct.ct_gemm_query(M, N, K, 0, 0)
+    assert st == ct.CT_ERR_INVALID_ARG
+
+
+def test_gemm_null_and_dtype_errors():
+    assert ct.library().ct_gemm_fwd(None, 16, 16, 4, 4, 4, 0, 0, None, None, 1e-5, None) == ct.CT_ERR_INVALID_ARG
+    assert ct.library().ct_gemm_fwd(16, 16, 16, 4, 4, 4, 7, 0, None, None, 1e-5, None) == ct.CT_ERR_INVALID_ARG
+
+
+def test_gemm_query_uses_the_folded_convolution_shape():
+    """The matrix product's cached config is the 1x1 convolution's with N split as
+    H*W (W the largest divisor of N not above 256)."""
+    for M, N, K, dt in [(64, 4096, 128, ct.CT_F16), (37, 53, 29, ct.CT_F32), (8, 1000, 16, ct.CT_BF16)]:
+        H, W = wl.gemm_fold(N)
+        assert H * W == N and W <= 256
+        st, c1, fc1 = ct.ct_gemm_query(M, N, K, dt, 0)
+        st2, c2, fc2 = ct.ct_conv2d_query(1, K, H, W, M, 1, 1, 1, 0, dt, 0)
+        assert st == 0 and st2 == 0
+        assert (c1.variant, c1.split_k, c1.stages, c1.kc) == (c2.variant, c2.split_k, c2.stages, c2.kc)
+        assert ct.variants()[c1.variant]["kind"] == 1, "a tiled kernel, not the direct reference"
+
+
 def test_null_pointers_rejected():
     lib = ct.library()
     shape = (1, 4, 8, 8, 4, 3, 3, 1, 1, 0)

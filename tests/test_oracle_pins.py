@@ -274,3 +274,51 @@ def test_flop_count_reproduces_gist_gflops():
         gf = flops / t["cost"] / 1e9
         # printed to 2 decimals; the tool's own count sits ~0.12% above 2*MAC
         assert abs(gf - t["gflops"]) <= 0.005 + 1.5e-3 * t["gflops"], (t["no"], gf)
+
+
+# ---- matrix product ---------------------------------------------------------
+def test_gemm_textbook_case():
+    """[[1,2,3],[4,5,6]] x [[7,8],[9,10],[11,12]] = [[58,64],[139,154]] (worked by
+    hand: 1*7+2*9+3*11 = 58, 1*8+2*10+3*12 = 64, 4*7+5*9+6*11 = 139,
+    4*8+5*10+6*12 = 154).  A transposed operand or swapped product fails it."""
+    A = np.array([[1, 2, 3], [4, 5, 6]], dtype=np.float64)
+    B = np.array([[7, 8], [9, 10], [11, 12]], dtype=np.float64)
+    C, absacc = O.gemm(A, B)
+    assert C.tolist() == [[58, 64], [139, 154]]
+    assert absacc.tolist() == [[58, 64], [139, 154]]
+    C, absacc = O.gemm(-A, B)
+    assert C.tolist() == [[-58, -64], [-139, -154]] and absacc.tolist() == [[58, 64], [139, 154]]
+
+
+def test_gemm_brute_force_loops():
+    r = np.random.default_rng(11)
+    for M, N, K in [(1, 1, 1), (3, 5, 4), (7, 2, 9)]:
+        A, B = r.normal(size=(M, K)), r.normal(size=(K, N))
+        C, _ = O.gemm(A, B)
+        for m in range(M):
+            for n in range(N):
+                s = 0.0
+                for k in range(K):
+                    s += A[m, k] * B[k, n]
+                assert abs(C[m, n] - s) <= 1e-12 * (1 + abs(s))
+
+
+def test_gemm_identity():
+    A = np.random.default_rng(12).normal(size=(6, 6))
+    assert np.array_equal(O.gemm(A, np.eye(6))[0], A)
+    assert np.array_equal(O.gemm(np.eye(6), A)[0], A)
+
+
+@pytest.mark.parametrize("fold", [(1, 20), (4, 5), (20, 1)])
+def test_gemm_is_the_seven_loop_1x1_convolution(fold):
+    """The library's view of a matrix product: w = A as [M][K][1][1], x = B as
+    [1][K][H][W] with H*W = N, y = C.  The seven-loop convolution (independent
+    C code) gives the same numbers for every split of N; integer inputs make
+    both sums exact."""
+    r = np.random.default_rng(13)
+    M, K, N = 6, 7, 20
+    A = r.integers(-3, 4, (M, K)).astype(np.float64)
+    B = r.integers(-3, 4, (K, N)).astype(np.float64)
+    H, W = fold
+    y, _ = O.conv2d_nchw(B.reshape(1, K, H, W), A.reshape(M, K, 1, 1), 1, 0)
+    assert np.array_equal(y.reshape(M, N), O.gemm(A, B)[0])
