@@ -1,4 +1,4 @@
-// fp16 / bf16 implicit-GEMM convolution for 3x3 filters, second form
+// fp16 / bf16 implicit-GEMM convolution for 3x3 (and 1x1) filters, second form
 // (v_mfma_f32_32x32x16_f16 / _bf16, fp32 accumulation and output, as the
 // TVM tutorial "Tuning High Performance Convolution on NVIDIA GPUs", Step 1,
 // declares the output).
@@ -644,10 +644,12 @@ hipError_t h2_launch(const ConvParams& p, hipStream_t stream) {
 }
 
 // descriptor: 32x32x16 instruction, waves WM x WN x 1, reps RM x RN; kc fixed
-// at KC (kc_max = KC), 3x3 filters only
-#define CT_H2_VARIANT(NAME, DT, WM, WN, RM, RN, KC)                                              \
-    {NAME, DT, 32, 32, 16, WM, WN, 1, RM, RN, KC, &h2_lds_bytes<WM, WN, RM, RN, KC, 9>,          \
-     &h2_launch<DT, WM, WN, RM, RN, KC, 9>, &h2_aux_bytes<WM, WN, RM, RN, KC, 9>}
+// at KC (kc_max = KC); filters of T taps (3x3, and 1x1 for the matrix-product
+// view)
+#define CT_H2_VARIANT_T(NAME, DT, WM, WN, RM, RN, KC, T)                                         \
+    {NAME, DT, 32, 32, 16, WM, WN, 1, RM, RN, KC, &h2_lds_bytes<WM, WN, RM, RN, KC, T>,          \
+     &h2_launch<DT, WM, WN, RM, RN, KC, T>, &h2_aux_bytes<WM, WN, RM, RN, KC, T>}
+#define CT_H2_VARIANT(NAME, DT, WM, WN, RM, RN, KC) CT_H2_VARIANT_T(NAME, DT, WM, WN, RM, RN, KC, 9)
 
 const IgemmVariant kH2Variants[] = {
     CT_H2_VARIANT("h2f16_m128n256_w2x4_r2x2_kc16", DT_F16, 2, 4, 2, 2, 16),
@@ -658,6 +660,11 @@ const IgemmVariant kH2Variants[] = {
     CT_H2_VARIANT("h2f16_m64n128_w1x2_r2x2_kc16", DT_F16, 1, 2, 2, 2, 16),
     CT_H2_VARIANT("h2bf16_m128n256_w2x4_r2x2_kc16", DT_BF16, 2, 4, 2, 2, 16),
     CT_H2_VARIANT("h2bf16_m128n128_w2x2_r2x2_kc16", DT_BF16, 2, 2, 2, 2, 16),
+    // 1x1 filters (T = 1: the matrix-product view): 32 or 64 channels a stage
+    CT_H2_VARIANT_T("h2f16_m128n256_w2x4_r2x2_kc64_t1", DT_F16, 2, 4, 2, 2, 64, 1),
+    CT_H2_VARIANT_T("h2f16_m128n256_w2x4_r2x2_kc32_t1", DT_F16, 2, 4, 2, 2, 32, 1),
+    CT_H2_VARIANT_T("h2f16_m128n128_w2x2_r2x2_kc64_t1", DT_F16, 2, 2, 2, 2, 64, 1),
+    CT_H2_VARIANT_T("h2bf16_m128n256_w2x4_r2x2_kc64_t1", DT_BF16, 2, 4, 2, 2, 64, 1),
 };
 
 }  // namespace
