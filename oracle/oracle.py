@@ -20,7 +20,10 @@ What it holds:
   included);
 * the matrix product C = A B in fp64 (its definition, with a library matmul
   of fp64 arrays as the one step), which the TVM tutorial's opening names as a
-  second use of its template.
+  second use of its template;
+* the depthwise convolution in fp64 (the definition written out in numpy: one
+  strided slice of the zero-padded input per tap, summed in row-major tap
+  order), another operator the tutorial's opening names.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` (hand-computed cases, closed forms, invariants,
@@ -147,6 +150,35 @@ def gemm(A, B) -> Tuple[np.ndarray, np.ndarray]:
     if a.ndim != 2 or b.ndim != 2 or a.shape[1] != b.shape[0]:
         raise ValueError("gemm: A must be [M, K] and B [K, N]")
     return a @ b, np.abs(a) @ np.abs(b)
+
+
+def conv2d_depthwise(x, w, stride: int, pad: int) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 depthwise convolution: x [N, C, H, W], w [C, 1, KH, KW],
+    y[n][c][oy][ox] = sum_{ky, kx} xp[n][c][oy*s + ky][ox*s + kx] * w[c][0][ky][kx]
+    with xp = x zero-padded by `pad` on each side; the taps are summed in
+    row-major (ky, kx) order.  Returns (y, absacc), absacc the same sum of
+    |term| (the tolerance scale, as conv2d_nchw's)."""
+    x = _f64(x)
+    w = _f64(w)
+    if x.ndim != 4 or w.ndim != 4 or w.shape[0] != x.shape[1] or w.shape[1] != 1:
+        raise ValueError("conv2d_depthwise: x must be [N, C, H, W] and w [C, 1, KH, KW]")
+    N, C, H, W = x.shape
+    KH, KW = w.shape[2], w.shape[3]
+    OH, OW = out_extent(H, KH, stride, pad), out_extent(W, KW, stride, pad)
+    if OH <= 0 or OW <= 0:
+        raise ValueError("kernel larger than padded input")
+    xp = np.zeros((N, C, H + 2 * pad, W + 2 * pad), np.float64)
+    xp[:, :, pad:pad + H, pad:pad + W] = x
+    y = np.zeros((N, C, OH, OW), np.float64)
+    a = np.zeros_like(y)
+    for ky in range(KH):
+        for kx in range(KW):
+            rows = slice(ky, ky + stride * (OH - 1) + 1, stride)
+            cols = slice(kx, kx + stride * (OW - 1) + 1, stride)
+            t = xp[:, :, rows, cols] * w[:, 0, ky, kx][None, :, None, None]
+            y += t
+            a += np.abs(t)
+    return y, a
 
 
 def channel_epilogue(y, kind: int, b=None, v=None, eps: float = 1e-5) -> np.ndarray:

@@ -153,6 +153,77 @@ def gemm_inputs(g: GemmWorkload) -> dict:
             "var": c["var"]}
 
 
+@dataclass(frozen=True)
+class DepthwiseWorkload:
+    """Depthwise convolution: x [N][C][H][W], w [C][1][KH][KW], every channel
+    convolved with its own filter."""
+    name: str
+    cfg_id: int
+    N: int
+    C: int
+    H: int
+    W: int
+    KH: int
+    KW: int
+    stride: int
+    pad: int
+    dtype: str = F32
+    epilogue: int = EPI_NONE
+
+    @property
+    def OH(self) -> int:
+        return (self.H + 2 * self.pad - self.KH) // self.stride + 1
+
+    @property
+    def OW(self) -> int:
+        return (self.W + 2 * self.pad - self.KW) // self.stride + 1
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.N * self.C * self.OH * self.OW * self.KH * self.KW
+
+    def algorithmic_bytes(self) -> int:
+        """x and w read once, y (fp32) written once, plus the epilogue's
+        per-channel parameters."""
+        e = 4 if self.dtype == F32 else 2
+        b = e * (self.N * self.C * self.H * self.W + self.C * self.KH * self.KW)
+        b += 4 * self.N * self.C * self.OH * self.OW
+        if self.epilogue == EPI_BIAS:
+            b += 4 * self.C
+        elif self.epilogue == EPI_EXP_BIAS_RSQRT:
+            b += 8 * self.C
+        return b
+
+    def as_dict(self) -> dict:
+        d = asdict(self)
+        d.update(OH=self.OH, OW=self.OW, flops=self.flops)
+        return d
+
+
+# Depthwise layers of a MobileNet-style network at batch 128: a 3x3 stride-1
+# layer on 56x56 planes, a stride-2 layer on 112x112 planes, and an fp16 layer
+# on 14x14 planes (several planes a workgroup) with a bias epilogue.
+DEPTHWISE_WORKLOADS: Dict[str, DepthwiseWorkload] = {d.name: d for d in [
+    DepthwiseWorkload("dw_f32_n128_c128_56x56_k3", 70, 128, 128, 56, 56, 3, 3, 1, 1),
+    DepthwiseWorkload("dw_f32_n128_c64_112x112_k3s2", 71, 128, 64, 112, 112, 3, 3, 2, 1),
+    DepthwiseWorkload("dw_f16_n128_c512_14x14_k3_bias", 72, 128, 512, 14, 14, 3, 3, 1, 1, F16,
+                      EPI_BIAS),
+]}
+
+
+def depthwise_inputs(d: DepthwiseWorkload) -> dict:
+    """x ~ U[-1, 1] [N, C, H, W], w He-normal over fan-in KH*KW [C, 1, KH, KW]
+    (both rounded to d.dtype), bias ~ N(0, 0.1), var ~ U[0.5, 2] per channel;
+    seeds 1000 * cfg_id + {1, 2, 3, 4}."""
+    base = 1000 * d.cfg_id
+    x = np.random.default_rng(base + 1).uniform(-1.0, 1.0, (d.N, d.C, d.H, d.W))
+    w = np.random.default_rng(base + 2).normal(0.0, np.sqrt(2.0 / (d.KH * d.KW)),
+                                               (d.C, 1, d.KH, d.KW))
+    b = np.random.default_rng(base + 3).normal(0.0, 0.1, d.C).astype(np.float32)
+    v = np.random.default_rng(base + 4).uniform(0.5, 2.0, d.C).astype(np.float32)
+    return {"x": to_dtype(x, d.dtype), "w": to_dtype(w, d.dtype), "bias": b, "var": v}
+
+
 HEADLINE = "resnet_final_c512_7x7_k3"
 SWEEP = [n for n, w in CONV_WORKLOADS.items() if w.cfg_id >= 30]
 

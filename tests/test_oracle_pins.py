@@ -322,3 +322,105 @@ def test_gemm_is_the_seven_loop_1x1_convolution(fold):
     H, W = fold
     y, _ = O.conv2d_nchw(B.reshape(1, K, H, W), A.reshape(M, K, 1, 1), 1, 0)
     assert np.array_equal(y.reshape(M, N), O.gemm(A, B)[0])
+
+
+# ---- depthwise convolution --------------------------------------------------
+def test_depthwise_hand_case():
+    """Two channels worked by hand.  Channel 0: filter [[1, 0], [0, -1]], so
+    y = x[oy][ox] - x[oy+1][ox+1] (-4 everywhere on 1..9); with pad 1 and
+    stride 2 the taps fall on xp[2oy][2ox] - xp[2oy+1][2ox+1] = (0 - 1, 0 - 3,
+    0 - 7, 5 - 9).  Channel 1: filter [[2, 1], [0, 1]] on [[1, 0, -1],
+    [2, 0, -2], [0, 1, 0]] gives [[2, -3], [5, -2]] (e.g. top right:
+    2*0 + 1*(-1) + 0*0 + 1*(-2) = -3).  A flipped filter, a channel mix-up or
+    a wrong padding offset fails it."""
+    x = np.array([[[[1, 2, 3], [4, 5, 6], [7, 8, 9]],
+                   [[1, 0, -1], [2, 0, -2], [0, 1, 0]]]], np.float64)
+    w = np.array([[[[1, 0], [0, -1]]], [[[2, 1], [0, 1]]]], np.float64)
+    y, a = O.conv2d_depthwise(x, w, 1, 0)
+    assert y.tolist() == [[[[-4, -4], [-4, -4]], [[2, -3], [5, -2]]]]
+    assert a[0, 0].tolist() == [[6, 8], [12, 14]]
+    y, _ = O.conv2d_depthwise(x[:, :1], w[:1], 2, 1)
+    assert y.tolist() == [[[[-1, -3], [-7, -4]]]]
+
+
+def test_depthwise_against_torch_grouped_conv():
+    """ATen's CPU conv2d with groups = C (fp64) is an independent routine."""
+    shapes = [(1, 3, 9, 11, 3, 3, 1, 1), (2, 5, 8, 8, 3, 3, 2, 1), (1, 4, 10, 7, 5, 3, 2, 2),
+              (3, 2, 6, 6, 1, 1, 1, 0), (1, 3, 13, 13, 7, 7, 2, 3), (2, 6, 5, 9, 2, 4, 3, 0)]
+    for i, (N, C, H, W, KH, KW, s, p) in enumerate(shapes):
+        x = _rand((N, C, H, W), 400 + i)
+        w = _rand((C, 1, KH, KW), 450 + i)
+        y, _ = O.conv2d_depthwise(x, w, s, p)
+        ref = torch.nn.functional.conv2d(torch.from_numpy(x), torch.from_numpy(w), stride=s,
+                                         padding=p, groups=C).numpy()
+        assert y.shape == ref.shape
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("ints", [True, False])
+def test_depthwise_is_block_diagonal_seven_loop_convolution(ints):
+    """The seven-loop convolution (independent C code) with the filter
+    w_full[c][c'] = w[c] if c == c' else 0 gives the depthwise result: exactly
+    for integer inputs, to rounding for random ones."""
+    r = np.random.default_rng(460)
+    N, C, H, W, KH, KW, s, p = 2, 5, 11, 9, 3, 3, 2, 1
+    if ints:
+        x = r.integers(-3, 4, (N, C, H, W)).astype(np.float64)
+        w = r.integers(-3, 4, (C, 1, KH, KW)).astype(np.float64)
+    else:
+        x, w = r.normal(size=(N, C, H, W)), r.normal(size=(C, 1, KH, KW))
+    wf = np.zeros((C, C, KH, KW))
+    for c in range(C):
+        wf[c, c] = w[c, 0]
+    y, a = O.conv2d_depthwise(x, w, s, p)
+    yf, af = O.conv2d_nchw(x, wf, s, p)
+    if ints:
+        assert np.array_equal(y, yf) and np.array_equal(a, af)
+    else:
+        np.testing.assert_allclose(y, yf, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(a, af, rtol=1e-13, atol=1e-13)
+
+
+def test_depthwise_closed_forms():
+    r = np.random.default_rng(470)
+    x = r.normal(size=(2, 4, 7, 6))
+    # a 1x1 filter scales each channel
+    w1 = r.normal(size=(4, 1, 1, 1))
+    assert np.array_equal(O.conv2d_depthwise(x, w1, 1, 0)[0], x * w1[:, 0, 0, 0][None, :, None, None])
+    # a delta filter at (1, 2) of a 3x4 filter with pad 1 reads xp[oy + 1][ox + 2]
+    wd = np.zeros((4, 1, 3, 4))
+    wd[:, 0, 1, 2] = 1.0
+    y, _ = O.conv2d_depthwise(x, wd, 1, 1)
+    xp = np.pad(x, ((0, 0), (0, 0), (1, 1), (1, 1)))
+    assert np.array_equal(y, xp[:, :, 1:1 + y.shape[2], 2:2 + y.shape[3]])
+    # stride s samples the stride-1 output at multiples of s
+    w = r.normal(size=(4, 1, 3, 3))
+    y1, _ = O.conv2d_depthwise(x, w, 1, 1)
+    for s in (2, 3):
+        ys, _ = O.conv2d_depthwise(x, w, s, 1)
+        assert np.array_equal(ys, y1[:, :, ::s, ::s][:, :, :ys.shape[2], :ys.shape[3]])
+    # all ones: every output counts the taps that land inside the image
+    y, a = O.conv2d_depthwise(np.ones((1, 1, 4, 4)), np.ones((1, 1, 3, 3)), 1, 1)
+    assert y[0, 0].tolist() == [[4, 6, 6, 4], [6, 9, 9, 6], [6, 9, 9, 6], [4, 6, 6, 4]]
+    assert np.array_equal(a, y)
+
+
+def test_depthwise_channels_are_independent():
+    r = np.random.default_rng(480)
+    x = r.normal(size=(2, 5, 8, 8))
+    w = r.normal(size=(5, 1, 3, 3))
+    y0, _ = O.conv2d_depthwise(x, w, 1, 1)
+    x2 = x.copy()
+    x2[:, 3] += 1.0
+    y2, _ = O.conv2d_depthwise(x2, w, 1, 1)
+    changed = np.any(y0 != y2, axis=(0, 2, 3))
+    assert changed.tolist() == [False, False, False, True, False]
+
+
+def test_depthwise_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        O.conv2d_depthwise(np.ones((1, 2, 4, 4)), np.ones((3, 1, 3, 3)), 1, 0)
+    with pytest.raises(ValueError):
+        O.conv2d_depthwise(np.ones((1, 2, 4, 4)), np.ones((2, 2, 3, 3)), 1, 0)
+    with pytest.raises(ValueError):
+        O.conv2d_depthwise(np.ones((1, 2, 2, 2)), np.ones((2, 1, 3, 3)), 1, 0)
