@@ -44,6 +44,8 @@ def kernel_sources(kernel: str):
     """The source files a kernel (variant name, or "broadcast") is built from."""
     if kernel == "broadcast":
         main = "broadcast.hip"
+    elif kernel == "depthwise":
+        return ["conv_depthwise.hip", "ct_device.hpp"]
     elif kernel.startswith("f32skc"):
         main = "igemm_f32_skc.hip"
     elif kernel.startswith("f32skt"):
@@ -286,6 +288,109 @@ def bench_broadcast(a, name: str) -> dict:
     return out
 
 
+def cpu_baseline_depthwise(d, seconds: float) -> dict:
+    """The fp64 oracle depthwise convolution on this host, on a slice of the
+    batch repeated for about `seconds`; reported as the layer's algorithmic
+    bytes per second, scaled to the slice."""
+    from oracle import oracle as O
+    from tensor_compiler_tiling_amd import workloads as wl
+    inp = wl.depthwise_inputs(d)
+    nb = max(1, min(d.N, 8))
+    x = inp["x"][:nb].astype(np.float64)
+    w = inp["w"].astype(np.float64)
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.conv2d_depthwise(x, w, d.stride, d.pad)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(d.algorithmic_bytes() * nb / d.N * reps / el / 1e9, 3), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{reps} fp64 oracle passes (y and its |x*w| scale) over {nb} of {d.N} images "
+                      f"of {d.name} in {el:.1f} s, counted at the layer's algorithmic bytes"}
+
+
+def bench_depthwise(a, name: str) -> dict:
+    """Depthwise convolution: K launches captured in one HIP graph; inputs and
+    outputs rotate over enough buffer sets that each step's bytes come from
+    HBM, not from the 256 MB last-level cache."""
+    import torch
+    from tensor_compiler_tiling_amd import convtile as ct
+    from tensor_compiler_tiling_amd import workloads as wl
+    d = wl.DEPTHWISE_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[d.dtype]
+    inp = wl.depthwise_inputs(d)
+    nbytes = d.algorithmic_bytes()
+    nbuf = max(2, -(-300 * 2 ** 20 // nbytes))
+    xs = [torch.from_numpy(inp["x"]).to(dev).to(tdt) for _ in range(nbuf)]
+    k = torch.from_numpy(inp["w"]).to(dev).to(tdt)
+    b = torch.from_numpy(inp["bias"]).to(dev)
+    v = torch.from_numpy(inp["var"]).to(dev)
+    ys = [torch.empty((d.N, d.C, d.OH, d.OW), dtype=torch.float32, device=dev) for _ in range(nbuf)]
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    lib = ct.library()
+    dt = ct.dtype_code(tdt)
+
+    def step(i):
+        st = lib.ct_conv2d_nchw_depthwise(xs[i % nbuf].data_ptr(), k.data_ptr(), ys[i % nbuf].data_ptr(),
+                                          d.N, d.C, d.H, d.W, d.KH, d.KW, d.stride, d.pad, dt,
+                                          d.epilogue, b.data_ptr(), v.data_ptr(), 1e-5,
+                                          torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise ct.ConvTileError(st, "depthwise")
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    if a.eager:
+        e0.record(stream)
+        for i in range(a.steps):
+            step(i)
+        e1.record(stream)
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(a.steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / a.steps
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    out = {
+        "metric": "depthwise convolution, HBM GB/s of algorithmic bytes (x, w read once, y written once)",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": d.dtype,
+        "data": "synthetic (seeded: x ~ U[-1, 1], w He-normal over KH*KW, bias ~ N(0, 0.1))",
+        "config": {"workload": name, "N": d.N, "C": d.C, "H": d.H, "W": d.W, "KH": d.KH, "KW": d.KW,
+                   "stride": d.stride, "pad": d.pad, "epilogue": d.epilogue,
+                   "algorithmic_bytes_per_step": nbytes, "rotating_buffers": nbuf,
+                   "launch": "eager" if a.eager else "hip_graph"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(name, "depthwise", {})},
+        "gflops": round(d.flops / (ms * 1e-3) / 1e9, 1),
+        "wall_s": round(wall, 4),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_depthwise(d, a.cpu_seconds)
+    return out
+
+
 def main():
     a = _parse()
     if a.gpus != 1:
@@ -303,6 +408,9 @@ def main():
     name = a.workload or wl.HEADLINE
     if name in wl.BROADCAST_WORKLOADS:
         print(json.dumps(bench_broadcast(a, name)), flush=True)
+        return
+    if name in wl.DEPTHWISE_WORKLOADS:
+        print(json.dumps(bench_depthwise(a, name)), flush=True)
         return
     gemm = wl.GEMM_WORKLOADS.get(name)
     # a matrix product is timed through ct_gemm_fwd; its 1x1 convolution view

@@ -169,6 +169,28 @@ int ct_gemm_tune(int M, int N, int K, int dtype, int epilogue,
 int ct_gemm_query(int M, int N, int K, int dtype, int epilogue,
                   ct_tile_config* cfg_out, int* from_cache);
 
+/* ---- depthwise convolution -------------------------------------------
+ * The TVM tutorial names, in its opening, depthwise convolution as another
+ * operator its template covers.  Each channel is convolved with its own
+ * filter:
+ *
+ *   y[n][c][oy][ox] = sum_{ky<KH} sum_{kx<KW} xp[n][c][oy*s+ky][ox*s+kx] * w[c][0][ky][kx]
+ *
+ * x [N][C][H][W] and w [C][1][KH][KW] (contiguous, dtype `dtype`), y
+ * [N][C][OH][OW] float with OH, OW as for ct_conv2d_nchw_fwd, xp x padded with
+ * `pad` zeros, fp32 accumulation, and the per-channel epilogue (bias[c],
+ * var[c]).  No channel reduction, so no tile config: one LDS-tiled kernel.
+ * Errors: those of ct_conv2d_nchw_fwd for the arguments, and
+ * CT_ERR_UNSUPPORTED for more than 256 taps (KH*KW), N*C or H*W above 2^31 - 1, or
+ * an output row too wide for one workgroup's LDS window (about
+ * ((3*stride + KH) * ((OW-1)*stride + KW)) > 40960); CT_ERR_HIP on a launch
+ * failure.  Asynchronous on `stream`. */
+int ct_conv2d_nchw_depthwise(const void* x, const void* w, float* y,
+                             int N, int C, int H, int W, int KH, int KW,
+                             int stride, int pad, int dtype, int epilogue,
+                             const float* bias, const float* var, float eps,
+                             void* stream);
+
 /* ---- tile-config search ----------------------------------------------
  * The space of a shape follows the TVM tutorial's template (Step 1): ordered
  * knobs, each a split (all ordered factorizations of an extent, the

@@ -85,6 +85,7 @@ _SIGS = {
     "ct_gemm_tune": (_I, [_I] * 5 + [_I, _F, _P, ctypes.POINTER(ct_tile_config),
                                    ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
     "ct_gemm_query": (_I, [_I] * 5 + [ctypes.POINTER(ct_tile_config), ctypes.POINTER(_I)]),
+    "ct_conv2d_nchw_depthwise": (_I, [_P, _P, _P] + [_I] * 10 + [_P, _P, _F, _P]),
     "ct_variant_count": (_I, []),
     "ct_variant_info": (_I, [_I, ctypes.POINTER(ct_variant_desc)]),
     "ct_split_count": (_LL, [_LL, _I]),
@@ -223,6 +224,13 @@ def ct_gemm_fwd(A, B, C, M, N, K, dtype, epilogue, bias=None, var=None, eps=1e-5
                                _ptr(var), eps, _stream(stream))
 
 
+def ct_conv2d_nchw_depthwise(x, w, y, N, C, H, W, KH, KW, stride, pad, dtype, epilogue, bias=None,
+                             var=None, eps=1e-5, stream=None) -> int:
+    return _load().ct_conv2d_nchw_depthwise(_ptr(x), _ptr(w), _ptr(y), N, C, H, W, KH, KW, stride, pad,
+                                            dtype, epilogue, _ptr(bias), _ptr(var), eps,
+                                            _stream(stream))
+
+
 def ct_gemm_tune(M, N, K, dtype, epilogue, max_trials=0, min_repeat_ms=100.0, stream=None,
                  max_records=4096):
     best = ct_tile_config()
@@ -358,6 +366,24 @@ def gemm(A, B, epilogue: int = CT_EPI_NONE, bias=None, var=None, eps: float = 1e
     C = out if out is not None else torch.empty((M, N), dtype=torch.float32, device=A.device)
     check(ct_gemm_fwd(A, B, C, M, N, K, dtype_code(A.dtype), epilogue, bias, var, eps, stream), "gemm")
     return C
+
+
+def conv2d_depthwise(x, w, stride: int = 1, pad: int = 0, epilogue: int = CT_EPI_NONE, bias=None,
+                     var=None, eps: float = 1e-5, out=None, stream=None):
+    """Depthwise y[n][c] = conv2d(x[n][c], w[c][0]) (+ epilogue), fp32 output allocated with
+    torch: x [N, C, H, W], w [C, 1, KH, KW], same dtype, contiguous."""
+    import torch
+    N, C, H, W = x.shape
+    C2, one, KH, KW = w.shape
+    if C2 != C or one != 1 or w.dtype != x.dtype:
+        raise ValueError("w must be [C, 1, KH, KW] of x's channels and dtype")
+    OH, OW = out_extent(H, KH, stride, pad), out_extent(W, KW, stride, pad)
+    y = out if out is not None else torch.empty((N, C, OH, OW), dtype=torch.float32,
+                                                device=x.device)
+    st = ct_conv2d_nchw_depthwise(x, w, y, N, C, H, W, KH, KW, stride, pad, dtype_code(x.dtype),
+                                  epilogue, bias, var, eps, stream)
+    check(st, "conv2d_depthwise")
+    return y
 
 
 def broadcast(var, N: int, H: int, W: int, out_dtype=None, mode: int = CT_BC_AUTO, out=None,

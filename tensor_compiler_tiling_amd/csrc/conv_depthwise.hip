@@ -1,0 +1,401 @@
+// Depthwise NCHW convolution: every channel convolved with its own filter
+// (the TVM tutorial "Tuning High Performance Convolution on NVIDIA GPUs"
+// names depthwise convolution, in its opening, as another use of its
+// template):
+//
+//   y[n][c][oy][ox] = sum_{ky<KH} sum_{kx<KW} xp[n][c][oy*s+ky][ox*s+kx] * w[c][0][ky][kx]
+//
+// with xp the input zero-padded by `pad` (inline), fp32 accumulation and
+// output, and the per-channel epilogue of the convolution path.
+//
+// There is no reduction over channels, so nothing here is a dense
+// contraction: each input is read KH*KW times from LDS but once from HBM and
+// the kernel is bound by HBM (x read once, y written once).  The planes
+// (n, c) are contiguous in both x and y, so they are numbered pl = n*C + c.
+// One workgroup computes RB output rows (a multiple of 4) of PPW consecutive
+// planes (PPW > 1 only when a whole plane is smaller than a workgroup's work):
+//   - it stages the receptive field, RIN = (RB-1)*s + KH input rows of the
+//     padded row width per plane, in LDS as fp32, zeros outside the image, so
+//     the inner loop has no bounds tests.  The image rows a block needs are
+//     one contiguous range of x (rows of consecutive planes follow each
+//     other), read with 16-byte loads at 16-byte aligned addresses, up to
+//     eight a lane in flight at once, plus a scalar head and tail; the zero
+//     border goes to LDS words no load writes, so the two need no barrier
+//     between them;
+//   - the planes' taps follow the window in LDS;
+//   - each lane computes one output column over 4 consecutive rows, so the
+//     lanes of a wave read consecutive LDS words (no bank conflicts at
+//     stride 1) and, for the filter sizes compiled in, input rows shared by
+//     the 4 outputs are read once;
+//   - consecutive workgroups of one XCD take neighbouring row blocks, so the
+//     halo rows two blocks share come from the same L2.
+#include "ct_device.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+namespace ct {
+
+namespace {
+
+constexpr int kDwThreads = 256;
+constexpr int kDwMaxTaps = 256;         // KH*KW
+constexpr int kDwMaxLds = 160 * 1024;   // bytes of LDS per workgroup on gfx950
+constexpr int kDwPrefLds = 64 * 1024;   // plans above this only when nothing smaller fits
+constexpr int kDwTargetItems = 512;     // 4-row strips a workgroup aims at
+
+struct DwParams {
+    const void* x;
+    const void* w;
+    float* y;
+    const float* bias;
+    const float* var;
+    float eps;
+    int NC, C, H, W, KH, KW, stride, pad, OH, OW;
+    int RB;      // output rows a workgroup computes (a multiple of 4)
+    int RIN;     // input rows it stages per plane: (RB-1)*stride + KH
+    int WPAD;    // staged row width: (OW-1)*stride + KW
+    int LDSW;    // LDS row pitch (floats): WPAD rounded up to odd
+    int PPW;     // planes a workgroup computes
+    int TAPS;    // LDS word of the first tap (after the PPW windows)
+    int blocks;  // row blocks per plane: ceil(OH / RB)
+    int tiles;   // workgroups with work: blocks * ceil(NC / PPW)
+    int tiles8;  // tiles rounded up to a multiple of 8 (the grid)
+    int epilogue;
+    int vec;      // x is 16-byte aligned: vector loads
+    int rowvec;   // ... and W is a multiple of the elements of a load: one row each
+    double rW;    // 1 / W and 1 / (H*W), for the divisions of the staging loop
+    double rHW;
+};
+
+// q = n / d for 0 <= n < 2^31, d > 0, rd = 1/d rounded to double: the
+// product's error is far below one, so the truncated estimate is the
+// quotient or one off, and one correction step fixes it.
+__device__ __forceinline__ int fdiv(int n, int d, double rd) {
+    int q = (int)((double)n * rd);
+    const int r = n - q * d;
+    q += r < 0 ? -1 : (r >= d ? 1 : 0);
+    return q;
+}
+
+// Elements of one 16-byte load and their conversion to fp32.
+template <int DT> struct Vec16;
+template <> struct Vec16<DT_F32> {
+    static constexpr int N = 4;
+    static __device__ __forceinline__ float at(const uint4& u, int i) {
+        return __uint_as_float(i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w);
+    }
+};
+template <> struct Vec16<DT_F16> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ float at(const uint4& u, int i) {
+        const unsigned w = (i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w;
+        const unsigned short h = (unsigned short)((i & 1) ? (w >> 16) : (w & 0xffffu));
+        return (float)__builtin_bit_cast(_Float16, h);
+    }
+};
+template <> struct Vec16<DT_BF16> {
+    static constexpr int N = 8;
+    static __device__ __forceinline__ float at(const uint4& u, int i) {
+        const unsigned w = (i >> 1) == 0 ? u.x : (i >> 1) == 1 ? u.y : (i >> 1) == 2 ? u.z : u.w;
+        return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+};
+
+template <int DT, int KH_, int KW_, int S_>
+__global__ __launch_bounds__(kDwThreads) void conv_depthwise_kernel(DwParams p) {
+    using T = typename Elem<DT>::T;
+    extern __shared__ float lds[];  // PPW x [RIN][LDSW] windows, then PPW x KH*KW taps
+    const int tid = threadIdx.x;
+    // workgroup b runs on XCD b % 8: give each XCD a contiguous run of tiles
+    const int b = blockIdx.x;
+    const int tile = (b & 7) * (p.tiles8 >> 3) + (b >> 3);
+    if (tile >= p.tiles) return;
+    const int KH = KH_ > 0 ? KH_ : p.KH;
+    const int KW = KW_ > 0 ? KW_ : p.KW;
+    const int S = S_ > 0 ? S_ : p.stride;
+    const int blk = tile % p.blocks;
+    const int pl0 = (tile / p.blocks) * p.PPW;
+    const int np = min(p.PPW, p.NC - pl0);
+    const int oy0 = blk * p.RB;
+    const int iy0 = oy0 * S - p.pad;  // first staged input row
+    const int HW = p.H * p.W;  // < 2^31: checked by the host
+    // image rows [iy_lo, iy_hi) of each plane land in the window; in x they
+    // are the local range [lo, hi) counted from plane pl0's first element
+    const int iy_lo = min(max(iy0, 0), p.H);
+    const int iy_hi = max(min(iy0 + p.RIN, p.H), iy_lo);
+    const int drows = iy_hi - iy_lo;
+    const T* xb = static_cast<const T*>(p.x) + (long long)pl0 * HW;
+    const int lo = iy_lo * p.W;
+    const int hi = (np - 1) * HW + iy_hi * p.W;
+
+    // the zero border: rows outside the image, then the padding columns of
+    // image rows (words that no load below writes)
+    {
+        // window rows [0, zr_top) and [RIN - zr_bot, RIN) lie outside the image
+        const int zr_top = drows > 0 ? iy_lo - iy0 : p.RIN;
+        const int zr_bot = drows > 0 ? iy0 + p.RIN - iy_hi : 0;
+        const int zrows = zr_top + zr_bot;
+        const int nz = np * zrows * p.WPAD;
+        for (int e = tid; e < nz; e += kDwThreads) {
+            const int row = e / p.WPAD;
+            const int j = e - row * p.WPAD;
+            const int pp = row / zrows;
+            const int k = row - pp * zrows;
+            const int r = k < zr_top ? k : p.RIN - zr_bot + (k - zr_top);
+            lds[(pp * p.RIN + r) * p.LDSW + j] = 0.0f;
+        }
+        const int left = min(p.pad, p.WPAD);             // columns before the image
+        const int right = max(p.WPAD - p.pad - p.W, 0);  // columns past the image
+        const int pc = left + right;
+        const int nc = np * drows * pc;
+        for (int e = tid; e < nc; e += kDwThreads) {
+            const int row = e / pc;
+            const int k = e - row * pc;
+            const int pp = row / drows;
+            const int r = zr_top + (row - pp * drows);
+            const int j = k < left ? k : p.pad + p.W + (k - left);
+            lds[(pp * p.RIN + r) * p.LDSW + j] = 0.0f;
+        }
+    }
+    // local element e -> its window word, or -1 (a row or column the window
+    // does not hold: the rows between two planes' ranges, the columns that
+    // no output reads)
+    auto slot = [&](int e) -> int {
+        const int pp = fdiv(e, HW, p.rHW);
+        const int rem = e - pp * HW;
+        const int iy = fdiv(rem, p.W, p.rW);
+        const int j = rem - iy * p.W + p.pad;
+        if (iy < iy_lo || iy >= iy_hi || j >= p.WPAD) return -1;
+        return (pp * p.RIN + iy - iy0) * p.LDSW + j;
+    };
+    constexpr int VE = Vec16<DT>::N;
+    int va = 0, vb = 0, m = 0;  // vectors [va, vb); vector v holds local elements v*VE - m ..
+    if (p.vec) {
+        m = (int)(((long long)pl0 * HW) % VE);
+        va = (lo + m + VE - 1) / VE;
+        vb = (hi + m) / VE;
+        if (va > vb) va = vb = 0;
+    }
+    // scalar elements: all of [lo, hi) without vectors, else the head and tail
+    const int head_end = va < vb ? va * VE - m : hi;
+    const int tail_beg = va < vb ? vb * VE - m : hi;
+    for (int e = lo + tid; e < head_end; e += kDwThreads) {
+        const int d = slot(e);
+        if (d >= 0) lds[d] = Elem<DT>::to_f32(xb[e]);
+    }
+    for (int e = tail_beg + tid; e < hi; e += kDwThreads) {
+        const int d = slot(e);
+        if (d >= 0) lds[d] = Elem<DT>::to_f32(xb[e]);
+    }
+    const uint4* xv = reinterpret_cast<const uint4*>(xb - m);  // 16-byte aligned
+    for (int v0 = va; v0 < vb; v0 += 8 * kDwThreads) {
+        uint4 u[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int v = v0 + k * kDwThreads + tid;
+            u[k] = xv[v < vb ? v : va];
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int v = v0 + k * kDwThreads + tid;
+            if (v < vb) {
+                if (p.rowvec) {
+                    // m = 0 and the VE elements share a row: one slot, VE words
+                    const int e = v * VE;
+                    const int pp = fdiv(e, HW, p.rHW);
+                    const int rem = e - pp * HW;
+                    const int iy = fdiv(rem, p.W, p.rW);
+                    const int j = rem - iy * p.W + p.pad;
+                    if (iy >= iy_lo && iy < iy_hi) {
+                        float* dst = lds + (pp * p.RIN + iy - iy0) * p.LDSW + j;
+#pragma unroll
+                        for (int i = 0; i < VE; ++i)
+                            if (j + i < p.WPAD) dst[i] = Vec16<DT>::at(u[k], i);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < VE; ++i) {
+                        const int d = slot(v * VE - m + i);
+                        if (d >= 0) lds[d] = Vec16<DT>::at(u[k], i);
+                    }
+                }
+            }
+        }
+    }
+    const int TT = KH * KW;
+    float* tap = lds + p.TAPS;
+    const T* w = static_cast<const T*>(p.w);
+    for (int t = tid; t < np * TT; t += kDwThreads) {
+        const int pp = t / TT;
+        const int c = (pl0 + pp) % p.C;
+        tap[t] = Elem<DT>::to_f32(w[(long long)c * TT + (t - pp * TT)]);
+    }
+    __syncthreads();
+
+    // 4-row strips: item = (plane, strip g, column ox)
+    const int strips = p.RB / 4;
+    const int per_plane_items = strips * p.OW;
+    for (int item = tid; item < np * per_plane_items; item += kDwThreads) {
+        const int pp = item / per_plane_items;
+        const int rem = item - pp * per_plane_items;
+        const int g = rem / p.OW;
+        const int ox = rem - g * p.OW;
+        const float* win = lds + (pp * p.RIN + 4 * g * S) * p.LDSW + ox * S;
+        const float* tp = tap + pp * TT;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (KH_ > 0) {
+            float tr[KH_ * KW_];
+#pragma unroll
+            for (int t = 0; t < KH_ * KW_; ++t) tr[t] = tp[t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int ky = 0; ky < KH_; ++ky)
+#pragma unroll
+                    for (int kx = 0; kx < KW_; ++kx)
+                        acc[i] = __builtin_fmaf(win[(i * S_ + ky) * p.LDSW + kx], tr[ky * KW_ + kx], acc[i]);
+        } else {
+            for (int ky = 0; ky < KH; ++ky)
+                for (int kx = 0; kx < KW; ++kx) {
+                    const float wv = tp[ky * KW + kx];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc[i] = __builtin_fmaf(win[(i * S + ky) * p.LDSW + kx], wv, acc[i]);
+                }
+        }
+        const int pl = pl0 + pp;
+        float e_b = 0.0f, e_r = 1.0f;
+        if (p.epilogue != EPI_NONE) {
+            const int c = pl % p.C;
+            e_b = p.bias[c];
+            if (p.epilogue == EPI_EXP_BIAS_RSQRT) e_r = dev_rsqrt(p.var[c] + p.eps);
+        }
+        const int oy = oy0 + 4 * g;
+        float* yp = p.y + (long long)pl * p.OH * p.OW + (long long)oy * p.OW + ox;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (oy + i < p.OH) yp[(long long)i * p.OW] = apply_epilogue(p.epilogue, acc[i], e_b, e_r);
+    }
+}
+
+}  // namespace
+
+namespace {
+
+int plan_within(int NC, int OH, int OW, int KH, int KW, int stride, int budget, int* RB, int* RIN,
+                int* WPAD, int* LDSW, int* PPW, int* TAPS) {
+    *WPAD = (OW - 1) * stride + KW;
+    *LDSW = *WPAD | 1;  // odd pitch: the rows of a strip start on different banks
+    const int strips_plane = (OH + 3) / 4;
+    int g = OW >= kDwTargetItems ? 1 : kDwTargetItems / OW;
+    if (g > strips_plane) g = strips_plane;
+    int ppw = 1;
+    if (g == strips_plane) {
+        ppw = kDwTargetItems / (g * OW);
+        if (ppw < 1) ppw = 1;
+        if (ppw > NC) ppw = NC;
+    }
+    const int taps = KH * KW;
+    for (;;) {
+        const long long rin = (long long)(4 * g - 1) * stride + KH;
+        const long long words = (long long)ppw * rin * (*LDSW);
+        const long long bytes = (words + (long long)ppw * taps) * 4;
+        if (bytes <= budget) {
+            *RB = 4 * g;
+            *RIN = (int)rin;
+            *PPW = ppw;
+            *TAPS = (int)words;
+            return (int)bytes;
+        }
+        if (ppw > 1) ppw /= 2;
+        else if (g > 1) --g;
+        else return -1;
+    }
+}
+
+}  // namespace
+
+// Work split of a depthwise launch: RB rows (a multiple of 4) of PPW planes a
+// workgroup, about kDwTargetItems 4-row strips, within 64 KB of LDS (several
+// workgroups a CU) or, when four output rows of one plane need more, within
+// the 160 KB a workgroup may hold.  Returns the LDS bytes, or -1 if four
+// output rows of one plane do not fit even there.
+int depthwise_plan(int NC, int OH, int OW, int KH, int KW, int stride, int* RB, int* RIN, int* WPAD,
+                   int* LDSW, int* PPW, int* TAPS) {
+    const int b = plan_within(NC, OH, OW, KH, KW, stride, kDwPrefLds, RB, RIN, WPAD, LDSW, PPW, TAPS);
+    if (b >= 0) return b;
+    return plan_within(NC, OH, OW, KH, KW, stride, kDwMaxLds, RB, RIN, WPAD, LDSW, PPW, TAPS);
+}
+
+namespace {
+
+template <int DT, int KH_, int KW_, int S_>
+hipError_t launch_dw(const DwParams& p, int bytes, hipStream_t stream) {
+    auto kern = conv_depthwise_kernel<DT, KH_, KW_, S_>;
+    static std::atomic<int> lds_limit{65536};
+    if (bytes > lds_limit.load(std::memory_order_relaxed)) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return e;
+        }
+        lds_limit.store(bytes, std::memory_order_relaxed);
+    }
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.tiles8), dim3(kDwThreads), bytes, stream, p);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const DwParams& p, int bytes, hipStream_t stream) {
+    const int k = p.KH == p.KW ? p.KH : 0;
+    if (k == 3 && p.stride == 1) return launch_dw<DT, 3, 3, 1>(p, bytes, stream);
+    if (k == 3 && p.stride == 2) return launch_dw<DT, 3, 3, 2>(p, bytes, stream);
+    if (k == 5 && p.stride == 1) return launch_dw<DT, 5, 5, 1>(p, bytes, stream);
+    if (k == 5 && p.stride == 2) return launch_dw<DT, 5, 5, 2>(p, bytes, stream);
+    if (k == 7 && p.stride == 1) return launch_dw<DT, 7, 7, 1>(p, bytes, stream);
+    if (k == 7 && p.stride == 2) return launch_dw<DT, 7, 7, 2>(p, bytes, stream);
+    return launch_dw<DT, 0, 0, 0>(p, bytes, stream);
+}
+
+}  // namespace
+
+// Shapes are checked by the caller (positive sizes, output not empty, the
+// plan fits); this returns hipErrorInvalidValue for what it cannot launch.
+hipError_t launch_depthwise(const void* x, const void* w, float* y, int N, int C, int H, int W, int KH, int KW,
+                            int stride, int pad, int dtype, int epilogue, const float* bias, const float* var,
+                            float eps, hipStream_t stream) {
+    DwParams p{};
+    p.x = x; p.w = w; p.y = y; p.bias = bias; p.var = var; p.eps = eps;
+    p.NC = N * C; p.C = C; p.H = H; p.W = W; p.KH = KH; p.KW = KW; p.stride = stride; p.pad = pad;
+    p.OH = (H + 2 * pad - KH) / stride + 1;
+    p.OW = (W + 2 * pad - KW) / stride + 1;
+    p.epilogue = epilogue;
+    if (KH * KW > kDwMaxTaps || p.OH <= 0 || p.OW <= 0) return hipErrorInvalidValue;
+    if ((long long)H * W >= (1LL << 31)) return hipErrorInvalidValue;
+    const int bytes = depthwise_plan(p.NC, p.OH, p.OW, KH, KW, stride, &p.RB, &p.RIN, &p.WPAD, &p.LDSW,
+                                     &p.PPW, &p.TAPS);
+    if (bytes < 0) return hipErrorInvalidValue;
+    // the local element offsets of a workgroup's planes stay below 2^31
+    if ((long long)p.PPW * H * W >= (1LL << 31)) p.PPW = 1;
+    p.blocks = (p.OH + p.RB - 1) / p.RB;
+    const long long tiles = (long long)p.blocks * ((p.NC + p.PPW - 1) / p.PPW);
+    if (tiles > 0x7ffffff0LL) return hipErrorInvalidValue;
+    p.tiles = (int)tiles;
+    p.tiles8 = (p.tiles + 7) & ~7;
+    p.vec = (reinterpret_cast<uintptr_t>(x) % 16) == 0;
+    p.rowvec = p.vec && W % (dtype == DT_F32 ? 4 : 8) == 0;
+    p.rW = 1.0 / (double)W;
+    p.rHW = 1.0 / (double)((long long)H * W);
+    switch (dtype) {
+        case DT_F32: return launch_dt<DT_F32>(p, bytes, stream);
+        case DT_F16: return launch_dt<DT_F16>(p, bytes, stream);
+        case DT_BF16: return launch_dt<DT_BF16>(p, bytes, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ct

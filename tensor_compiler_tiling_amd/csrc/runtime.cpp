@@ -790,6 +790,15 @@ double now_s() {
 
 using namespace ct;
 
+// the depthwise kernel (conv_depthwise.hip)
+namespace ct {
+int depthwise_plan(int NC, int OH, int OW, int KH, int KW, int stride, int* RB, int* RIN, int* WPAD,
+                   int* LDSW, int* PPW, int* TAPS);
+hipError_t launch_depthwise(const void* x, const void* w, float* y, int N, int C, int H, int W, int KH,
+                            int KW, int stride, int pad, int dtype, int epilogue, const float* bias,
+                            const float* var, float eps, hipStream_t stream);
+}  // namespace ct
+
 // ===================================================================== ABI ==
 extern "C" {
 
@@ -966,6 +975,28 @@ int ct_broadcast_nchw(const float* var, void* out, int N, int C, int H, int W, i
     else
         e = launch_bcast_channel(var, out, N, C, (int)HW, out_dtype, hs);
     if (e != hipSuccess) return hip_fail(e, "broadcast launch");
+    return CT_OK;
+}
+
+int ct_conv2d_nchw_depthwise(const void* x, const void* w, float* y, int N, int C, int H, int W, int KH,
+                             int KW, int stride, int pad, int dtype, int epilogue, const float* bias,
+                             const float* var, float eps, void* stream) {
+    Shape s;  // the shape checks of a convolution with one input channel per group
+    int st = make_shape(N, 1, H, W, C, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    st = check_pointers(x, w, y, epilogue, bias, var);
+    if (st != CT_OK) return st;
+    if ((long long)KH * KW > 256)
+        return fail(CT_ERR_UNSUPPORTED, "depthwise filters hold at most 256 taps (got %dx%d)", KH, KW);
+    if ((long long)N * C > 0x7fffffffLL) return fail(CT_ERR_UNSUPPORTED, "N*C above 2^31 - 1");
+    if ((long long)H * W > 0x7fffffffLL) return fail(CT_ERR_UNSUPPORTED, "H*W above 2^31 - 1");
+    int rb, rin, wpad, ldsw, ppw, taps;
+    if (depthwise_plan(N * C, s.OH, s.OW, KH, KW, stride, &rb, &rin, &wpad, &ldsw, &ppw, &taps) < 0)
+        return fail(CT_ERR_UNSUPPORTED, "an output row of %d columns (stride %d, %dx%d filter) does not fit "
+                    "one workgroup's LDS window", s.OW, stride, KH, KW);
+    const hipError_t e = launch_depthwise(x, w, y, N, C, H, W, KH, KW, stride, pad, dtype, epilogue, bias,
+                                          var, eps, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "depthwise launch");
     return CT_OK;
 }
 

@@ -250,3 +250,32 @@ def test_traffic_records_point_at_summaries():
         assert os.path.exists(os.path.join(ROOT, r["summary"])), r["summary"]
         assert r["traffic_bytes_per_launch"] > 0
         assert len(r["source_sha256"]) == 64
+
+
+# ------------------------------------------------------- depthwise convolution
+@pytest.mark.parametrize("bad", [
+    dict(N=0), dict(C=0), dict(H=0), dict(KW=0), dict(stride=0), dict(pad=-1),
+    dict(KH=12),  # larger than the padded input (8 + 2)
+])
+def test_depthwise_invalid_shapes_rejected_before_any_hip_call(bad):
+    a = dict(N=1, C=4, H=8, W=8, KH=3, KW=3, stride=1, pad=1)
+    a.update(bad)
+    st = ct.library().ct_conv2d_nchw_depthwise(16, 16, 16, a["N"], a["C"], a["H"], a["W"], a["KH"],
+                                               a["KW"], a["stride"], a["pad"], 0, 0, None, None, 1e-5,
+                                               None)
+    assert st == ct.CT_ERR_INVALID_ARG, ct.ct_last_error()
+
+
+def test_depthwise_null_and_unsupported():
+    lib = ct.library()
+    shape = (1, 4, 8, 8, 3, 3, 1, 1)
+    assert lib.ct_conv2d_nchw_depthwise(None, 16, 16, *shape, 0, 0, None, None, 1e-5, None) == -1
+    assert lib.ct_conv2d_nchw_depthwise(16, 16, 16, *shape, 7, 0, None, None, 1e-5, None) == -1
+    assert lib.ct_conv2d_nchw_depthwise(16, 16, 16, *shape, 0, 1, None, None, 1e-5, None) == -1
+    assert lib.ct_conv2d_nchw_depthwise(16, 16, 16, *shape, 0, 2, 16, None, 1e-5, None) == -1
+    # more than 256 taps
+    st = lib.ct_conv2d_nchw_depthwise(16, 16, 16, 1, 2, 40, 40, 17, 17, 1, 0, 0, 0, None, None, 1e-5, None)
+    assert st == ct.CT_ERR_UNSUPPORTED and "256 taps" in ct.ct_last_error()
+    # an output row wider than one workgroup's LDS window
+    st = lib.ct_conv2d_nchw_depthwise(16, 16, 16, 1, 2, 4, 60000, 3, 3, 1, 1, 0, 0, None, None, 1e-5, None)
+    assert st == ct.CT_ERR_UNSUPPORTED and "LDS" in ct.ct_last_error()
