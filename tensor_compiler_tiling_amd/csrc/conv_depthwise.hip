@@ -27,8 +27,9 @@
 //     lanes of a wave read consecutive LDS words (no bank conflicts at
 //     stride 1) and, for the filter sizes compiled in, input rows shared by
 //     the 4 outputs are read once;
-//   - consecutive workgroups of one XCD take neighbouring row blocks, so the
-//     halo rows two blocks share come from the same L2.
+//   - a workgroup takes about 2048 strips (8192 outputs), so each has 16 to
+//     32 KB of loads in flight at once; consecutive workgroups of one XCD
+//     take neighbouring row blocks, whose halo rows then meet in one L2.
 #include "ct_device.hpp"
 
 #include <hip/hip_runtime.h>
@@ -43,7 +44,7 @@ constexpr int kDwThreads = 256;
 constexpr int kDwMaxTaps = 256;         // KH*KW
 constexpr int kDwMaxLds = 160 * 1024;   // bytes of LDS per workgroup on gfx950
 constexpr int kDwPrefLds = 64 * 1024;   // plans above this only when nothing smaller fits
-constexpr int kDwTargetItems = 512;     // 4-row strips a workgroup aims at
+constexpr int kDwTargetItems = 2048;    // 4-row strips a workgroup aims at
 
 struct DwParams {
     const void* x;
@@ -59,6 +60,7 @@ struct DwParams {
     int LDSW;    // LDS row pitch (floats): WPAD rounded up to odd
     int PPW;     // planes a workgroup computes
     int TAPS;    // LDS word of the first tap (after the PPW windows)
+    int EPIW;    // LDS word of the planes' epilogue values (after the taps)
     int blocks;  // row blocks per plane: ceil(OH / RB)
     int tiles;   // workgroups with work: blocks * ceil(NC / PPW)
     int tiles8;  // tiles rounded up to a multiple of 8 (the grid)
@@ -103,141 +105,219 @@ template <> struct Vec16<DT_BF16> {
     }
 };
 
-template <int DT, int KH_, int KW_, int S_>
-__global__ __launch_bounds__(kDwThreads) void conv_depthwise_kernel(DwParams p) {
-    using T = typename Elem<DT>::T;
-    extern __shared__ float lds[];  // PPW x [RIN][LDSW] windows, then PPW x KH*KW taps
-    const int tid = threadIdx.x;
-    // workgroup b runs on XCD b % 8: give each XCD a contiguous run of tiles
-    const int b = blockIdx.x;
-    const int tile = (b & 7) * (p.tiles8 >> 3) + (b >> 3);
-    if (tile >= p.tiles) return;
-    const int KH = KH_ > 0 ? KH_ : p.KH;
-    const int KW = KW_ > 0 ? KW_ : p.KW;
-    const int S = S_ > 0 ? S_ : p.stride;
-    const int blk = tile % p.blocks;
-    const int pl0 = (tile / p.blocks) * p.PPW;
-    const int np = min(p.PPW, p.NC - pl0);
-    const int oy0 = blk * p.RB;
-    const int iy0 = oy0 * S - p.pad;  // first staged input row
-    const int HW = p.H * p.W;  // < 2^31: checked by the host
-    // image rows [iy_lo, iy_hi) of each plane land in the window; in x they
-    // are the local range [lo, hi) counted from plane pl0's first element
-    const int iy_lo = min(max(iy0, 0), p.H);
-    const int iy_hi = max(min(iy0 + p.RIN, p.H), iy_lo);
-    const int drows = iy_hi - iy_lo;
-    const T* xb = static_cast<const T*>(p.x) + (long long)pl0 * HW;
-    const int lo = iy_lo * p.W;
-    const int hi = (np - 1) * HW + iy_hi * p.W;
+// One workgroup's share of the output: PPW planes from pl0 (np of them in
+// the last group), output rows [oy0, oy0 + RB); image rows [iy_lo, iy_hi)
+// of each plane land in the window, which in x is the local range [lo, hi)
+// counted from plane pl0's first element; 16-byte vectors [va, vb) of that
+// range, vector v holding local elements v*VE - m .. v*VE - m + VE - 1.
+struct DwTile {
+    int pl0, np, oy0, iy0, iy_lo, iy_hi, lo, hi, m, va, vb;
+};
 
-    // the zero border: rows outside the image, then the padding columns of
-    // image rows (words that no load below writes)
-    {
-        // window rows [0, zr_top) and [RIN - zr_bot, RIN) lie outside the image
-        const int zr_top = drows > 0 ? iy_lo - iy0 : p.RIN;
-        const int zr_bot = drows > 0 ? iy0 + p.RIN - iy_hi : 0;
-        const int zrows = zr_top + zr_bot;
-        const int nz = np * zrows * p.WPAD;
-        for (int e = tid; e < nz; e += kDwThreads) {
-            const int row = e / p.WPAD;
-            const int j = e - row * p.WPAD;
-            const int pp = row / zrows;
-            const int k = row - pp * zrows;
-            const int r = k < zr_top ? k : p.RIN - zr_bot + (k - zr_top);
-            lds[(pp * p.RIN + r) * p.LDSW + j] = 0.0f;
-        }
-        const int left = min(p.pad, p.WPAD);             // columns before the image
-        const int right = max(p.WPAD - p.pad - p.W, 0);  // columns past the image
-        const int pc = left + right;
-        const int nc = np * drows * pc;
-        for (int e = tid; e < nc; e += kDwThreads) {
-            const int row = e / pc;
-            const int k = e - row * pc;
-            const int pp = row / drows;
-            const int r = zr_top + (row - pp * drows);
-            const int j = k < left ? k : p.pad + p.W + (k - left);
-            lds[(pp * p.RIN + r) * p.LDSW + j] = 0.0f;
-        }
-    }
-    // local element e -> its window word, or -1 (a row or column the window
-    // does not hold: the rows between two planes' ranges, the columns that
-    // no output reads)
-    auto slot = [&](int e) -> int {
-        const int pp = fdiv(e, HW, p.rHW);
-        const int rem = e - pp * HW;
-        const int iy = fdiv(rem, p.W, p.rW);
-        const int j = rem - iy * p.W + p.pad;
-        if (iy < iy_lo || iy >= iy_hi || j >= p.WPAD) return -1;
-        return (pp * p.RIN + iy - iy0) * p.LDSW + j;
-    };
+template <int DT>
+__device__ __forceinline__ DwTile dw_tile(const DwParams& p, int tile, int S) {
     constexpr int VE = Vec16<DT>::N;
-    int va = 0, vb = 0, m = 0;  // vectors [va, vb); vector v holds local elements v*VE - m ..
+    DwTile t;
+    const int blk = tile % p.blocks;
+    t.pl0 = (tile / p.blocks) * p.PPW;
+    t.np = min(p.PPW, p.NC - t.pl0);
+    t.oy0 = blk * p.RB;
+    t.iy0 = t.oy0 * S - p.pad;
+    t.iy_lo = min(max(t.iy0, 0), p.H);
+    t.iy_hi = max(min(t.iy0 + p.RIN, p.H), t.iy_lo);
+    const int HW = p.H * p.W;  // < 2^31: checked by the host
+    t.lo = t.iy_lo * p.W;
+    t.hi = (t.np - 1) * HW + t.iy_hi * p.W;
+    t.m = 0;
+    t.va = t.vb = 0;
     if (p.vec) {
-        m = (int)(((long long)pl0 * HW) % VE);
-        va = (lo + m + VE - 1) / VE;
-        vb = (hi + m) / VE;
-        if (va > vb) va = vb = 0;
+        t.m = (int)(((long long)t.pl0 * HW) % VE);
+        t.va = (t.lo + t.m + VE - 1) / VE;
+        t.vb = (t.hi + t.m) / VE;
+        if (t.va > t.vb) t.va = t.vb = 0;
     }
-    // scalar elements: all of [lo, hi) without vectors, else the head and tail
-    const int head_end = va < vb ? va * VE - m : hi;
-    const int tail_beg = va < vb ? vb * VE - m : hi;
-    for (int e = lo + tid; e < head_end; e += kDwThreads) {
-        const int d = slot(e);
-        if (d >= 0) lds[d] = Elem<DT>::to_f32(xb[e]);
-    }
-    for (int e = tail_beg + tid; e < hi; e += kDwThreads) {
-        const int d = slot(e);
-        if (d >= 0) lds[d] = Elem<DT>::to_f32(xb[e]);
-    }
-    const uint4* xv = reinterpret_cast<const uint4*>(xb - m);  // 16-byte aligned
-    for (int v0 = va; v0 < vb; v0 += 8 * kDwThreads) {
-        uint4 u[8];
+    return t;
+}
+
+template <int DT>
+__device__ __forceinline__ const uint4* dw_vectors(const DwParams& p, const DwTile& t) {
+    using T = typename Elem<DT>::T;
+    return reinterpret_cast<const uint4*>(static_cast<const T*>(p.x) + (long long)t.pl0 * p.H * p.W - t.m);
+}
+
+// What a tile's staging reads from global memory ahead of time: the first
+// batch of 16-byte loads (vectors va + k*256 + tid, clamped to va past the
+// end: in bounds, not stored), the lane's tap (tap tid of the tile's planes)
+// and, for lanes below np, its plane's bias and var.
+struct DwPrefetch {
+    uint4 u[8];
+    float tw, eb, ev;
+};
+
+template <int DT>
+__device__ __forceinline__ void dw_issue(const DwParams& p, const DwTile& t, DwPrefetch& f, int TT, int tid) {
+    using T = typename Elem<DT>::T;
+    if (t.va < t.vb) {
+        const uint4* xv = dw_vectors<DT>(p, t);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int v = v0 + k * kDwThreads + tid;
-            u[k] = xv[v < vb ? v : va];
+            const int v = t.va + k * kDwThreads + tid;
+            f.u[k] = xv[v < t.vb ? v : t.va];
         }
+    }
+    // clamped indices: every lane loads, lanes past the end load a valid word
+    const T* w = static_cast<const T*>(p.w);
+    const int i = min(tid, t.np * TT - 1);
+    const int pp = i / TT;
+    f.tw = Elem<DT>::to_f32(w[(long long)((t.pl0 + pp) % p.C) * TT + (i - pp * TT)]);
+    // bias and var always point at C readable floats (the host substitutes
+    // what the epilogue does not read), so these loads need no branch
+    const int c = (t.pl0 + min(tid, t.np - 1)) % p.C;
+    f.eb = p.bias[c];
+    f.ev = p.var[c];
+}
+
+// Write one batch of loaded vectors (from v0) into the window.
+template <int DT>
+__device__ __forceinline__ void dw_scatter(const DwParams& p, const DwTile& t, const uint4 (&u)[8], int v0,
+                                           float* lds, int tid) {
+    constexpr int VE = Vec16<DT>::N;
+    const int HW = p.H * p.W;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int v = v0 + k * kDwThreads + tid;
-            if (v < vb) {
-                if (p.rowvec) {
-                    // m = 0 and the VE elements share a row: one slot, VE words
-                    const int e = v * VE;
+    for (int k = 0; k < 8; ++k) {
+        const int v = v0 + k * kDwThreads + tid;
+        if (v < t.vb) {
+            if (p.rowvec) {
+                // m = 0 and the VE elements share a row: one slot, VE words
+                const int e = v * VE;
+                const int pp = fdiv(e, HW, p.rHW);
+                const int rem = e - pp * HW;
+                const int iy = fdiv(rem, p.W, p.rW);
+                const int j = rem - iy * p.W + p.pad;
+                if (iy >= t.iy_lo && iy < t.iy_hi) {
+                    float* dst = lds + (pp * p.RIN + iy - t.iy0) * p.LDSW + j;
+#pragma unroll
+                    for (int i = 0; i < VE; ++i)
+                        if (j + i < p.WPAD) dst[i] = Vec16<DT>::at(u[k], i);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < VE; ++i) {
+                    const int e = v * VE - t.m + i;
                     const int pp = fdiv(e, HW, p.rHW);
                     const int rem = e - pp * HW;
                     const int iy = fdiv(rem, p.W, p.rW);
                     const int j = rem - iy * p.W + p.pad;
-                    if (iy >= iy_lo && iy < iy_hi) {
-                        float* dst = lds + (pp * p.RIN + iy - iy0) * p.LDSW + j;
-#pragma unroll
-                        for (int i = 0; i < VE; ++i)
-                            if (j + i < p.WPAD) dst[i] = Vec16<DT>::at(u[k], i);
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < VE; ++i) {
-                        const int d = slot(v * VE - m + i);
-                        if (d >= 0) lds[d] = Vec16<DT>::at(u[k], i);
-                    }
+                    if (iy >= t.iy_lo && iy < t.iy_hi && j < p.WPAD)
+                        lds[(pp * p.RIN + iy - t.iy0) * p.LDSW + j] = Vec16<DT>::at(u[k], i);
                 }
             }
         }
     }
-    const int TT = KH * KW;
-    float* tap = lds + p.TAPS;
-    const T* w = static_cast<const T*>(p.w);
-    for (int t = tid; t < np * TT; t += kDwThreads) {
-        const int pp = t / TT;
-        const int c = (pl0 + pp) % p.C;
-        tap[t] = Elem<DT>::to_f32(w[(long long)c * TT + (t - pp * TT)]);
+}
+
+// Stage a tile's windows and taps: the zero border (rows outside the image,
+// then the padding columns of image rows: words no load writes), the scalar
+// head and tail of the range (all of it without vectors), the first batch of
+// vectors from u (already in flight) and any further batches.
+template <int DT>
+__device__ __forceinline__ void dw_stage(const DwParams& p, const DwTile& t, DwPrefetch& f, int TT,
+                                         float* lds, int tid) {
+    using T = typename Elem<DT>::T;
+    constexpr int VE = Vec16<DT>::N;
+    const int HW = p.H * p.W;
+    const int drows = t.iy_hi - t.iy_lo;
+    const int zr_top = drows > 0 ? t.iy_lo - t.iy0 : p.RIN;
+    const int zr_bot = drows > 0 ? t.iy0 + p.RIN - t.iy_hi : 0;
+    const int zrows = zr_top + zr_bot;
+    const int nz = t.np * zrows * p.WPAD;
+    for (int e = tid; e < nz; e += kDwThreads) {
+        const int row = e / p.WPAD;
+        const int j = e - row * p.WPAD;
+        const int pp = row / zrows;
+        const int k = row - pp * zrows;
+        const int r = k < zr_top ? k : p.RIN - zr_bot + (k - zr_top);
+        lds[(pp * p.RIN + r) * p.LDSW + j] = 0.0f;
     }
+    const int left = min(p.pad, p.WPAD);             // columns before the image
+    const int right = max(p.WPAD - p.pad - p.W, 0);  // columns past the image
+    const int pc = left + right;
+    const int nc = t.np * drows * pc;
+    for (int e = tid; e < nc; e += kDwThreads) {
+        const int row = e / pc;
+        const int k = e - row * pc;
+        const int pp = row / drows;
+        const int r = zr_top + (row - pp * drows);
+        const int j = k < left ? k : p.pad + p.W + (k - left);
+        lds[(pp * p.RIN + r) * p.LDSW + j] = 0.0f;
+    }
+    const T* xb = static_cast<const T*>(p.x) + (long long)t.pl0 * HW;
+    const bool vecs = t.va < t.vb;
+    const int head_end = vecs ? t.va * VE - t.m : t.hi;
+    const int tail_beg = vecs ? t.vb * VE - t.m : t.hi;
+    auto put = [&](int e) {
+        const int pp = fdiv(e, HW, p.rHW);
+        const int rem = e - pp * HW;
+        const int iy = fdiv(rem, p.W, p.rW);
+        const int j = rem - iy * p.W + p.pad;
+        if (iy >= t.iy_lo && iy < t.iy_hi && j < p.WPAD)
+            lds[(pp * p.RIN + iy - t.iy0) * p.LDSW + j] = Elem<DT>::to_f32(xb[e]);
+    };
+    // the prefetched words first, then what still has to be loaded
+    float* tap = lds + p.TAPS;
+    if (tid < t.np * TT) tap[tid] = f.tw;
+    if (tid < t.np) {
+        lds[p.EPIW + 2 * tid] = p.epilogue != EPI_NONE ? f.eb : 0.0f;
+        lds[p.EPIW + 2 * tid + 1] = p.epilogue == EPI_EXP_BIAS_RSQRT ? dev_rsqrt(f.ev + p.eps) : 1.0f;
+    }
+    if (vecs) dw_scatter<DT>(p, t, f.u, t.va, lds, tid);
+    if (vecs) {
+        const uint4* xv = dw_vectors<DT>(p, t);
+        for (int v0 = t.va + 8 * kDwThreads; v0 < t.vb; v0 += 8 * kDwThreads) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int v = v0 + k * kDwThreads + tid;
+                f.u[k] = xv[v < t.vb ? v : t.va];
+            }
+            dw_scatter<DT>(p, t, f.u, v0, lds, tid);
+        }
+    }
+    for (int e = t.lo + tid; e < head_end; e += kDwThreads) put(e);
+    for (int e = tail_beg + tid; e < t.hi; e += kDwThreads) put(e);
+    const T* w = static_cast<const T*>(p.w);
+    for (int i = kDwThreads + tid; i < t.np * TT; i += kDwThreads) {
+        const int pp = i / TT;
+        const int c = (t.pl0 + pp) % p.C;
+        tap[i] = Elem<DT>::to_f32(w[(long long)c * TT + (i - pp * TT)]);
+    }
+}
+
+// One workgroup per tile.  Workgroup b runs on XCD b % 8, and XCD x takes
+// tiles [x*TX, (x+1)*TX), so neighbouring row blocks, which share halo rows,
+// meet in one L2.  The tile's loads (window vectors, taps, epilogue values)
+// are all issued before any of them is used.
+template <int DT, int KH_, int KW_, int S_>
+__global__ __launch_bounds__(kDwThreads) void conv_depthwise_kernel(DwParams p) {
+    extern __shared__ float lds[];  // PPW x [RIN][LDSW] windows, taps, epilogue values
+    const int tid = threadIdx.x;
+    const int KH = KH_ > 0 ? KH_ : p.KH;
+    const int KW = KW_ > 0 ? KW_ : p.KW;
+    const int S = S_ > 0 ? S_ : p.stride;
+    const int TT = KH * KW;
+    const int tile = (blockIdx.x & 7) * (p.tiles8 >> 3) + (blockIdx.x >> 3);
+    if (tile >= p.tiles) return;
+
+    DwPrefetch f;
+    const DwTile t = dw_tile<DT>(p, tile, S);
+    dw_issue<DT>(p, t, f, TT, tid);
+    dw_stage<DT>(p, t, f, TT, lds, tid);
     __syncthreads();
 
     // 4-row strips: item = (plane, strip g, column ox)
     const int strips = p.RB / 4;
     const int per_plane_items = strips * p.OW;
-    for (int item = tid; item < np * per_plane_items; item += kDwThreads) {
+    const float* tap = lds + p.TAPS;
+    for (int item = tid; item < t.np * per_plane_items; item += kDwThreads) {
         const int pp = item / per_plane_items;
         const int rem = item - pp * per_plane_items;
         const int g = rem / p.OW;
@@ -248,7 +328,7 @@ __global__ __launch_bounds__(kDwThreads) void conv_depthwise_kernel(DwParams p) 
         if constexpr (KH_ > 0) {
             float tr[KH_ * KW_];
 #pragma unroll
-            for (int t = 0; t < KH_ * KW_; ++t) tr[t] = tp[t];
+            for (int i = 0; i < KH_ * KW_; ++i) tr[i] = tp[i];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -265,14 +345,9 @@ __global__ __launch_bounds__(kDwThreads) void conv_depthwise_kernel(DwParams p) 
                         acc[i] = __builtin_fmaf(win[(i * S + ky) * p.LDSW + kx], wv, acc[i]);
                 }
         }
-        const int pl = pl0 + pp;
-        float e_b = 0.0f, e_r = 1.0f;
-        if (p.epilogue != EPI_NONE) {
-            const int c = pl % p.C;
-            e_b = p.bias[c];
-            if (p.epilogue == EPI_EXP_BIAS_RSQRT) e_r = dev_rsqrt(p.var[c] + p.eps);
-        }
-        const int oy = oy0 + 4 * g;
+        const int pl = t.pl0 + pp;
+        const float e_b = lds[p.EPIW + 2 * pp], e_r = lds[p.EPIW + 2 * pp + 1];
+        const int oy = t.oy0 + 4 * g;
         float* yp = p.y + (long long)pl * p.OH * p.OW + (long long)oy * p.OW + ox;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -301,7 +376,7 @@ int plan_within(int NC, int OH, int OW, int KH, int KW, int stride, int budget, 
     for (;;) {
         const long long rin = (long long)(4 * g - 1) * stride + KH;
         const long long words = (long long)ppw * rin * (*LDSW);
-        const long long bytes = (words + (long long)ppw * taps) * 4;
+        const long long bytes = (words + (long long)ppw * (taps + 2)) * 4;
         if (bytes <= budget) {
             *RB = 4 * g;
             *RIN = (int)rin;
@@ -370,6 +445,11 @@ hipError_t launch_depthwise(const void* x, const void* w, float* y, int N, int C
                             float eps, hipStream_t stream) {
     DwParams p{};
     p.x = x; p.w = w; p.y = y; p.bias = bias; p.var = var; p.eps = eps;
+    // stand-ins for the per-channel arrays the epilogue does not read: the
+    // kernel loads both unconditionally and discards them (y holds at least
+    // C floats)
+    if (epilogue == EPI_NONE) p.bias = y;
+    if (epilogue != EPI_EXP_BIAS_RSQRT) p.var = p.bias;
     p.NC = N * C; p.C = C; p.H = H; p.W = W; p.KH = KH; p.KW = KW; p.stride = stride; p.pad = pad;
     p.OH = (H + 2 * pad - KH) / stride + 1;
     p.OW = (W + 2 * pad - KW) / stride + 1;
@@ -381,6 +461,7 @@ hipError_t launch_depthwise(const void* x, const void* w, float* y, int N, int C
     if (bytes < 0) return hipErrorInvalidValue;
     // the local element offsets of a workgroup's planes stay below 2^31
     if ((long long)p.PPW * H * W >= (1LL << 31)) p.PPW = 1;
+    p.EPIW = p.TAPS + p.PPW * KH * KW;
     p.blocks = (p.OH + p.RB - 1) / p.RB;
     const long long tiles = (long long)p.blocks * ((p.NC + p.PPW - 1) / p.PPW);
     if (tiles > 0x7ffffff0LL) return hipErrorInvalidValue;
