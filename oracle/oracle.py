@@ -23,7 +23,10 @@ What it holds:
   second use of its template;
 * the depthwise convolution in fp64 (the definition written out in numpy: one
   strided slice of the zero-padded input per tap, summed in row-major tap
-  order), another operator the tutorial's opening names.
+  order), another operator the tutorial's opening names;
+* the general per-channel broadcast [1,P,1] => [B,P,B] of the Paddle PR's
+  Introduction, with a chain of div / exp / rsqrt-style steps (Performance
+  Impact), evaluated step by step in fp64 over numpy broadcasting.
 
 Parity status: every function here is pinned by tests in
 ``tests/test_oracle_pins.py`` (hand-computed cases, closed forms, invariants,
@@ -205,6 +208,64 @@ def broadcast_exp(var, N: int, H: int, W: int) -> np.ndarray:
     if rc != 0:
         raise ValueError("oracle_broadcast_exp rejected its arguments")
     return out
+
+
+def broadcast_chain(chains, outer: int, P: int, inner: int, arrays=(), x=None) -> np.ndarray:
+    """The general per-channel broadcast [1,P,1] => [B,P,B] in fp64, out of
+    shape [outer, P, inner].  chains = (c0_steps, c1_steps, v_steps); a step
+    is (op,), (op, src) or (op, "imm", value) / (op, value) with op one of
+    set add sub mul div rsub rdiv exp rsqrt sqrt and src one of imm x c0 c1
+    a0..a3.  Each chain starts from 0 and applies its steps in order:
+    c0 from immediates and arrays a_k[p]; c1 may also read c0; v may also
+    read c1 and x[o][p][i].  out = v, or c0 when the v chain is empty."""
+    arr = [None if a is None else _f64(a).reshape(1, -1, 1) for a in list(arrays) + [None] * 4][:4]
+    X = None if x is None else _f64(x).reshape(outer, P, inner)
+
+    def run(steps, regs):
+        v = np.zeros((1, 1, 1))
+        for st in steps:
+            op, rest = st[0], st[1:]
+            src, imm = "imm", 0.0
+            if len(rest) == 1:
+                if isinstance(rest[0], str):
+                    src = rest[0]
+                else:
+                    imm = float(rest[0])
+            elif len(rest) == 2:
+                src, imm = rest[0], float(rest[1])
+            if op in ("exp", "rsqrt", "sqrt"):
+                v = {"exp": np.exp, "rsqrt": lambda t: 1.0 / np.sqrt(t), "sqrt": np.sqrt}[op](v)
+                continue
+            if src == "imm":
+                a = np.float64(imm)
+            elif src in regs:
+                a = regs[src]
+            elif src.startswith("a"):
+                a = arr[int(src[1])]
+            else:
+                raise ValueError(f"source {src} not readable here")
+            if op == "set":
+                v = a + np.zeros((1, 1, 1))
+            elif op == "add":
+                v = v + a
+            elif op == "sub":
+                v = v - a
+            elif op == "mul":
+                v = v * a
+            elif op == "div":
+                v = v / a
+            elif op == "rsub":
+                v = a - v
+            elif op == "rdiv":
+                v = a / v
+            else:
+                raise ValueError(f"unknown op {op}")
+        return v
+
+    c0 = run(chains[0], {})
+    c1 = run(chains[1], {"c0": c0})
+    v = run(chains[2], {"c0": c0, "c1": c1, "x": X}) if len(chains[2]) else c0
+    return np.broadcast_to(v, (outer, P, inner)).astype(np.float64).copy()
 
 
 def conv_flops(N, CI, H, W, CO, KH, KW, stride, pad) -> int:

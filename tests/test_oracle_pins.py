@@ -424,3 +424,71 @@ def test_depthwise_rejects_bad_arguments():
         O.conv2d_depthwise(np.ones((1, 2, 4, 4)), np.ones((2, 2, 3, 3)), 1, 0)
     with pytest.raises(ValueError):
         O.conv2d_depthwise(np.ones((1, 2, 2, 2)), np.ones((2, 1, 3, 3)), 1, 0)
+
+
+# ---- general per-channel broadcast ------------------------------------------
+def test_chain_hand_case_batchnorm_form():
+    """c0 = rsqrt(a0 + 1) with a0 = [3, 8]: [1/2, 1/3]; v = (x - a1) * c0 *
+    a2 + a3 with x = 5, a1 = [1, 2], a2 = [3, 6], a3 = [-1, 0]:
+    (5-1)/2*3 - 1 = 5 and (5-2)/3*6 + 0 = 6, worked by hand."""
+    chains = ([("set", "a0"), ("add", 1.0), ("rsqrt",)], [],
+              [("set", "x"), ("sub", "a1"), ("mul", "c0"), ("mul", "a2"), ("add", "a3")])
+    arrays = [np.array([3.0, 8.0]), np.array([1.0, 2.0]), np.array([3.0, 6.0]), np.array([-1.0, 0.0])]
+    x = np.full((2, 2, 3), 5.0)
+    out = O.broadcast_chain(chains, 2, 2, 3, arrays, x)
+    np.testing.assert_allclose(out[:, 0], 5.0, rtol=1e-15)
+    np.testing.assert_allclose(out[:, 1], 6.0, rtol=1e-15)
+    # with no v chain the output is c0
+    c0 = O.broadcast_chain((chains[0], [], []), 1, 2, 1, arrays)
+    np.testing.assert_allclose(c0.reshape(-1), [0.5, 1.0 / 3.0], rtol=1e-15)
+
+
+def test_chain_exp_matches_the_c_broadcast():
+    """[1,C,1,1] => [N,C,H,W] of exp(var[c]) is the chain set(a0), exp with
+    outer = N, inner = H*W; the C oracle's broadcast is separate code."""
+    var = np.random.default_rng(490).uniform(0.5, 2.0, 6)
+    out = O.broadcast_chain(([("set", "a0"), ("exp",)], [], []), 3, 6, 20, [var])
+    ref = O.broadcast_exp(var, 3, 4, 5).reshape(3, 6, 20)
+    np.testing.assert_allclose(out, ref, rtol=1e-15)
+
+
+def test_chain_step_orientation_and_identities():
+    one = lambda steps: float(O.broadcast_chain((steps, [], []), 1, 1, 1)[0, 0, 0])
+    assert one([("set", 3.0), ("rsub", 10.0)]) == 7.0      # 10 - 3
+    assert one([("set", 3.0), ("rdiv", 12.0)]) == 4.0      # 12 / 3
+    assert one([("set", 3.0), ("sub", 10.0)]) == -7.0
+    assert one([("set", 12.0), ("div", 3.0)]) == 4.0
+    assert one([("set", 4.0), ("sqrt",)]) == 2.0
+    assert one([("set", 4.0), ("rsqrt",)]) == 0.5
+    assert one([("exp",)]) == 1.0                           # a chain starts from 0
+    assert one([("add", 2.0), ("mul", 3.0)]) == 6.0
+    assert one([]) == 0.0
+
+
+def test_chain_layout_brute_force():
+    """out[o][p][i] = a0[p] * 10 + x[o][p][i] over explicit loops: a wrong
+    axis order or a transposed broadcast fails it."""
+    outer, P, inner = 3, 4, 5
+    a0 = np.arange(P, dtype=np.float64) + 1.0
+    x = np.random.default_rng(491).normal(size=(outer, P, inner))
+    out = O.broadcast_chain(([("set", "a0"), ("mul", 10.0)], [], [("set", "x"), ("add", "c0")]),
+                            outer, P, inner, [a0], x)
+    for o in range(outer):
+        for p in range(P):
+            for i in range(inner):
+                assert out[o, p, i] == x[o, p, i] + a0[p] * 10.0
+    # without x the value depends on p only
+    out = O.broadcast_chain(([("set", "a0"), ("exp",)], [], []), outer, P, inner, [a0])
+    for p in range(P):
+        assert np.all(out[:, p, :] == out[0, p, 0])
+    assert len(set(out[0, :, 0].tolist())) == P
+
+
+def test_chain_identity_and_c1():
+    x = np.random.default_rng(492).normal(size=(2, 3, 4))
+    assert np.array_equal(O.broadcast_chain(([], [], [("set", "x")]), 2, 3, 4, x=x), x)
+    # c1 reads c0: c1 = c0 * 2, v = x * c1
+    a0 = np.array([1.0, 2.0, 3.0])
+    out = O.broadcast_chain(([("set", "a0")], [("set", "c0"), ("mul", 2.0)], [("set", "x"), ("mul", "c1")]),
+                            2, 3, 4, [a0], x)
+    assert np.array_equal(out, x * (a0 * 2.0)[None, :, None])
