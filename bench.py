@@ -46,6 +46,8 @@ def kernel_sources(kernel: str):
         main = "broadcast.hip"
     elif kernel == "depthwise":
         return ["conv_depthwise.hip", "ct_device.hpp"]
+    elif kernel == "chain":
+        return ["broadcast_chain.hip", "ct_device.hpp"]
     elif kernel.startswith("f32skc"):
         main = "igemm_f32_skc.hip"
     elif kernel.startswith("f32skt"):
@@ -391,6 +393,96 @@ def bench_depthwise(a, name: str) -> dict:
     return out
 
 
+def cpu_baseline_chain(cw, seconds: float) -> dict:
+    """The fp64 oracle's chain evaluation on this host, on whole passes of the
+    workload for about `seconds`, as algorithmic bytes per second."""
+    from oracle import oracle as O
+    from tensor_compiler_tiling_amd import workloads as wl
+    inp = wl.chain_inputs(cw)
+    x = inp["x"].astype(np.float64)
+    arrays = [v.astype(np.float64) for v in inp["arrays"]]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.broadcast_chain(wl.CHAIN_PROGRAMS[cw.program], cw.outer, cw.P, cw.inner, arrays, x)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(cw.algorithmic_bytes() * reps / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": f"{reps} full fp64 oracle passes of {cw.name} in {el:.1f} s, counted "
+                                        f"at the workload's algorithmic bytes"}
+
+
+def bench_chain(a, name: str) -> dict:
+    """The general per-channel broadcast: the channel-bound form timed (K
+    launches in one HIP graph), the flat form timed beside it; inputs and
+    outputs rotate over enough buffers to exceed the last-level cache."""
+    import torch
+    from tensor_compiler_tiling_amd import convtile as ct
+    from tensor_compiler_tiling_amd import workloads as wl
+    cw = wl.CHAIN_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = wl.chain_inputs(cw)
+    nbytes = cw.algorithmic_bytes()
+    nbuf = max(2, -(-300 * 2 ** 20 // nbytes))
+    odt = torch.float32 if cw.out_dtype == wl.F32 else torch.float16
+    xs = [torch.from_numpy(inp["x"]).to(dev) for _ in range(nbuf)]
+    outs = [torch.empty((cw.outer, cw.P, cw.inner), dtype=odt, device=dev) for _ in range(nbuf)]
+    arrays = [torch.from_numpy(v).to(dev) for v in inp["arrays"]]
+    prog = ct.make_program(*wl.CHAIN_PROGRAMS[cw.program])
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    lib = ct.library()
+    code = ct.dtype_code(odt)
+    ap = [t.data_ptr() for t in arrays]
+
+    def run(mode, i):
+        st = lib.ct_broadcast_chain(ct.ctypes.byref(prog), ap[0], ap[1], ap[2], ap[3], xs[i % nbuf].data_ptr(),
+                                    outs[i % nbuf].data_ptr(), code, cw.outer, cw.P, cw.inner, mode,
+                                    torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise ct.ConvTileError(st, "broadcast_chain")
+
+    res = {}
+    for mode, label in ((ct.CT_BC_CHANNEL, "channel"), (ct.CT_BC_FLAT, "flat")):
+        for i in range(a.warmup):
+            run(mode, i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(a.steps):
+                run(mode, i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / a.steps
+        res[label] = {"ms_per_step": round(ms, 6), "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    gbs = res["channel"]["GB/s"]
+    out = {
+        "metric": "general per-channel broadcast [1,P,1]=>[B,P,B] with a step chain, HBM GB/s of algorithmic bytes",
+        "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": res["channel"]["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cw.out_dtype,
+        "data": "synthetic (seeded x ~ U[-1, 1]; var, gamma, mean, beta per channel)",
+        "config": {"workload": name, "outer": cw.outer, "P": cw.P, "inner": cw.inner, "program": cw.program,
+                   "algorithmic_bytes_per_step": nbytes, "rotating_buffers": nbuf, "launch": "hip_graph"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic(name, "chain", {})},
+        "flat_form": res["flat"],
+        "speedup_channel_vs_flat": round(res["flat"]["ms_per_step"] / res["channel"]["ms_per_step"], 3),
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_chain(cw, a.cpu_seconds)
+    return out
+
+
 def main():
     a = _parse()
     if a.gpus != 1:
@@ -411,6 +503,9 @@ def main():
         return
     if name in wl.DEPTHWISE_WORKLOADS:
         print(json.dumps(bench_depthwise(a, name)), flush=True)
+        return
+    if name in wl.CHAIN_WORKLOADS:
+        print(json.dumps(bench_chain(a, name)), flush=True)
         return
     gemm = wl.GEMM_WORKLOADS.get(name)
     # a matrix product is timed through ct_gemm_fwd; its 1x1 convolution view

@@ -169,6 +169,73 @@ int ct_gemm_tune(int M, int N, int K, int dtype, int epilogue,
 int ct_gemm_query(int M, int N, int K, int dtype, int epilogue,
                   ct_tile_config* cfg_out, int* from_cache);
 
+/* ---- general per-channel broadcast -----------------------------------
+ * The Paddle PR's Introduction generalises its tactic, by axis fusion, to
+ * [1,P,1] => [B,P,B] with the last axis a broadcast axis, and its
+ * Performance Impact section names div / exp / rsqrt chains as the work the
+ * tactic saves.  Here: out is [outer][P][inner] (inner contiguous) and a
+ * program of three chains, each at most CT_CHAIN_MAX_OPS steps applied in
+ * order to a value that starts at 0, is evaluated in fp32 per element:
+ *
+ *   chain 0 -> c0   operands: immediates, arrays a0..a3 at [p]
+ *   chain 1 -> c1   operands: the same, and c0
+ *   chain 2 -> v    operands: the same, c0, c1, and x[o][p][i]
+ *   out[o][p][i] = v, or c0 when chain 2 is empty
+ *
+ * A step is (op, src, imm): CT_OP_SET v = a; ADD v + a; SUB v - a; MUL v * a;
+ * DIV v / a; RSUB a - v; RDIV a / v; EXP exp(v); RSQRT 1/sqrt(v); SQRT
+ * sqrt(v) (the unary steps ignore their operand); a is imm, x, c0, c1 or
+ * a_k[p] by `src`.  exp and rsqrt run on the hardware units (about 1 ulp
+ * each), division and sqrt are correctly rounded, nothing is contracted into
+ * a fused multiply-add, and fp16 output is rounded to nearest even. */
+#define CT_CHAIN_MAX_OPS 8
+#define CT_OP_SET 0
+#define CT_OP_ADD 1
+#define CT_OP_SUB 2
+#define CT_OP_MUL 3
+#define CT_OP_DIV 4
+#define CT_OP_RSUB 5
+#define CT_OP_RDIV 6
+#define CT_OP_EXP 7
+#define CT_OP_RSQRT 8
+#define CT_OP_SQRT 9
+#define CT_SRC_IMM 0
+#define CT_SRC_X 1
+#define CT_SRC_C0 2
+#define CT_SRC_C1 3
+#define CT_SRC_A0 4  /* CT_SRC_A0 + k for array a_k, k < 4 */
+
+typedef struct ct_chain_op {
+    int op;      /* CT_OP_* */
+    int src;     /* CT_SRC_* */
+    float imm;   /* the operand when src == CT_SRC_IMM */
+} ct_chain_op;
+
+typedef struct ct_bcast_program {
+    int n_ops[3];                             /* steps in chains 0, 1, 2 */
+    ct_chain_op ops[3][CT_CHAIN_MAX_OPS];
+} ct_bcast_program;
+
+/* Evaluate `prog` into out ([outer][P][inner], out_dtype CT_F32 or CT_F16).
+ * a0..a3: per-channel fp32 arrays of P floats on the device (NULL when no
+ * step reads them); x: the producer's fp32 output, same [outer][P][inner]
+ * layout (NULL when no step reads it; x == out is allowed for fp32 output,
+ * any other overlap is not).  mode: CT_BC_CHANNEL (channel-bound: c0 and c1
+ * once per block), CT_BC_FLAT (everything per element) or CT_BC_AUTO, which
+ * takes the channel-bound form when inner >= 32, each row is a whole number
+ * of 16-byte vectors of out (and x), both are 16-byte aligned and the grid
+ * fits, and the flat form otherwise.  Both forms give identical bits.
+ * Errors: CT_ERR_INVALID_ARG for a NULL prog or out, outer, P or inner < 1,
+ * more than 2^46 elements, a step count outside [0, CT_CHAIN_MAX_OPS], an
+ * unknown op or source, a source a chain may not read, a NULL array or x
+ * that a step reads, an unknown dtype or mode, or x == out with fp16 output;
+ * CT_ERR_UNSUPPORTED for CT_BC_CHANNEL when the channel-bound conditions
+ * fail; CT_ERR_HIP on a launch failure.  Asynchronous on `stream`. */
+int ct_broadcast_chain(const ct_bcast_program* prog, const float* a0, const float* a1,
+                       const float* a2, const float* a3, const float* x, void* out,
+                       int out_dtype, long long outer, int P, long long inner, int mode,
+                       void* stream);
+
 /* ---- depthwise convolution -------------------------------------------
  * The TVM tutorial names, in its opening, depthwise convolution as another
  * operator its template covers.  Each channel is convolved with its own

@@ -28,6 +28,10 @@ CT_F32, CT_F16, CT_BF16 = 0, 1, 2
 CT_EPI_NONE, CT_EPI_BIAS, CT_EPI_EXP_BIAS_RSQRT = 0, 1, 2
 CT_BC_EXP = 0
 CT_BC_AUTO, CT_BC_CHANNEL, CT_BC_FLAT = 0, 1, 2
+CT_CHAIN_MAX_OPS = 8
+CHAIN_OPS = {"set": 0, "add": 1, "sub": 2, "mul": 3, "div": 4, "rsub": 5, "rdiv": 6, "exp": 7, "rsqrt": 8,
+             "sqrt": 9}
+CHAIN_SRCS = {"imm": 0, "x": 1, "c0": 2, "c1": 3, "a0": 4, "a1": 5, "a2": 6, "a3": 7}
 CT_TRIAL_OK, CT_TRIAL_ILLEGAL, CT_TRIAL_RUNTIME, CT_TRIAL_TIMEOUT = 0, 1, 4, 6
 
 
@@ -38,6 +42,14 @@ class ct_tile_config(ctypes.Structure):
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class ct_chain_op(ctypes.Structure):
+    _fields_ = [("op", ctypes.c_int), ("src", ctypes.c_int), ("imm", ctypes.c_float)]
+
+
+class ct_bcast_program(ctypes.Structure):
+    _fields_ = [("n_ops", ctypes.c_int * 3), ("ops", (ct_chain_op * CT_CHAIN_MAX_OPS) * 3)]
 
 
 class ct_variant_desc(ctypes.Structure):
@@ -86,6 +98,7 @@ _SIGS = {
                                    ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
     "ct_gemm_query": (_I, [_I] * 5 + [ctypes.POINTER(ct_tile_config), ctypes.POINTER(_I)]),
     "ct_conv2d_nchw_depthwise": (_I, [_P, _P, _P] + [_I] * 10 + [_P, _P, _F, _P]),
+    "ct_broadcast_chain": (_I, [ctypes.POINTER(ct_bcast_program)] + [_P] * 6 + [_I, _LL, _I, _LL, _I, _P]),
     "ct_variant_count": (_I, []),
     "ct_variant_info": (_I, [_I, ctypes.POINTER(ct_variant_desc)]),
     "ct_split_count": (_LL, [_LL, _I]),
@@ -229,6 +242,12 @@ def ct_conv2d_nchw_depthwise(x, w, y, N, C, H, W, KH, KW, stride, pad, dtype, ep
     return _load().ct_conv2d_nchw_depthwise(_ptr(x), _ptr(w), _ptr(y), N, C, H, W, KH, KW, stride, pad,
                                             dtype, epilogue, _ptr(bias), _ptr(var), eps,
                                             _stream(stream))
+
+
+def ct_broadcast_chain(prog, a0, a1, a2, a3, x, out, out_dtype, outer, P, inner, mode=CT_BC_AUTO,
+                       stream=None) -> int:
+    return _load().ct_broadcast_chain(ctypes.byref(prog), _ptr(a0), _ptr(a1), _ptr(a2), _ptr(a3), _ptr(x),
+                                      _ptr(out), out_dtype, outer, P, inner, mode, _stream(stream))
 
 
 def ct_gemm_tune(M, N, K, dtype, epilogue, max_trials=0, min_repeat_ms=100.0, stream=None,
@@ -396,6 +415,48 @@ def broadcast(var, N: int, H: int, W: int, out_dtype=None, mode: int = CT_BC_AUT
     st = ct_broadcast_nchw(var, o, N, C, H, W, dtype_code(o.dtype), CT_BC_EXP, mode, stream)
     check(st, "broadcast")
     return o
+
+
+def make_program(c0=(), c1=(), v=()) -> ct_bcast_program:
+    """A broadcast program from three step lists.  A step is (op,), (op, src)
+    or (op, "imm", value) / (op, value): op a CHAIN_OPS name, src a
+    CHAIN_SRCS name, a bare number meaning an immediate."""
+    prog = ct_bcast_program()
+    for c, steps in enumerate((c0, c1, v)):
+        steps = list(steps)
+        if len(steps) > CT_CHAIN_MAX_OPS:
+            raise ValueError(f"chain {c} has {len(steps)} steps (at most {CT_CHAIN_MAX_OPS})")
+        prog.n_ops[c] = len(steps)
+        for k, st in enumerate(steps):
+            op, rest = st[0], st[1:]
+            src, imm = "imm", 0.0
+            if len(rest) == 1:
+                if isinstance(rest[0], str):
+                    src = rest[0]
+                else:
+                    imm = float(rest[0])
+            elif len(rest) == 2:
+                src, imm = rest[0], float(rest[1])
+            prog.ops[c][k].op = CHAIN_OPS[op]
+            prog.ops[c][k].src = CHAIN_SRCS[src]
+            prog.ops[c][k].imm = imm
+    return prog
+
+
+def broadcast_chain(prog: ct_bcast_program, outer: int, P: int, inner: int, arrays=(), x=None,
+                    out_dtype=None, mode: int = CT_BC_AUTO, out=None, stream=None):
+    """out[o][p][i] = the program's value ([outer][P][inner], torch-allocated
+    unless `out` is given); arrays: up to four per-channel fp32 tensors of P
+    floats; x: the producer's fp32 tensor of the output's size, or None."""
+    import torch
+    arrays = list(arrays) + [None] * (4 - len(arrays))
+    dev = next((t.device for t in arrays + [x, out] if t is not None), None)
+    if out is None:
+        out = torch.empty((outer, P, inner), dtype=out_dtype or torch.float32, device=dev)
+    st = ct_broadcast_chain(prog, arrays[0], arrays[1], arrays[2], arrays[3], x, out,
+                            dtype_code(out.dtype), outer, P, inner, mode, stream)
+    check(st, "broadcast_chain")
+    return out
 
 
 def make_config(variant, split_k: int, stages: int, kc: int) -> ct_tile_config:

@@ -797,6 +797,11 @@ int depthwise_plan(int NC, int OH, int OW, int KH, int KW, int stride, int* RB, 
 hipError_t launch_depthwise(const void* x, const void* w, float* y, int N, int C, int H, int W, int KH,
                             int KW, int stride, int pad, int dtype, int epilogue, const float* bias,
                             const float* var, float eps, hipStream_t stream);
+// the general broadcast (broadcast_chain.hip)
+bool chain_channel_ok(long long outer, int P, long long inner, int out_dtype, const void* out, const void* x);
+hipError_t launch_broadcast_chain(const ct_bcast_program* prog, const float* const a[4], const float* x,
+                                  void* out, int out_dtype, long long outer, int P, long long inner,
+                                  bool channel, hipStream_t stream);
 }  // namespace ct
 
 // ===================================================================== ABI ==
@@ -997,6 +1002,54 @@ int ct_conv2d_nchw_depthwise(const void* x, const void* w, float* y, int N, int 
     const hipError_t e = launch_depthwise(x, w, y, N, C, H, W, KH, KW, stride, pad, dtype, epilogue, bias,
                                           var, eps, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "depthwise launch");
+    return CT_OK;
+}
+
+int ct_broadcast_chain(const ct_bcast_program* prog, const float* a0, const float* a1, const float* a2,
+                       const float* a3, const float* x, void* out, int out_dtype, long long outer, int P,
+                       long long inner, int mode, void* stream) {
+    if (!prog || !out) return fail(CT_ERR_INVALID_ARG, "prog and out must not be NULL");
+    if (outer < 1 || P < 1 || inner < 1) return fail(CT_ERR_INVALID_ARG, "outer, P and inner must be positive");
+    if ((double)outer * P * inner > (double)(1LL << 46)) return fail(CT_ERR_INVALID_ARG, "output too large");
+    if (out_dtype != CT_F32 && out_dtype != CT_F16)
+        return fail(CT_ERR_INVALID_ARG, "out_dtype must be CT_F32 or CT_F16");
+    if (mode != CT_BC_AUTO && mode != CT_BC_CHANNEL && mode != CT_BC_FLAT)
+        return fail(CT_ERR_INVALID_ARG, "unknown mode %d", mode);
+    const float* arrays[4] = {a0, a1, a2, a3};
+    bool reads_x = false;
+    for (int c = 0; c < 3; ++c) {
+        const int n = prog->n_ops[c];
+        if (n < 0 || n > CT_CHAIN_MAX_OPS)
+            return fail(CT_ERR_INVALID_ARG, "chain %d has %d steps (0..%d)", c, n, CT_CHAIN_MAX_OPS);
+        for (int k = 0; k < n; ++k) {
+            const ct_chain_op& o = prog->ops[c][k];
+            if (o.op < CT_OP_SET || o.op > CT_OP_SQRT)
+                return fail(CT_ERR_INVALID_ARG, "chain %d step %d: unknown op %d", c, k, o.op);
+            if (o.src < CT_SRC_IMM || o.src > CT_SRC_A0 + 3)
+                return fail(CT_ERR_INVALID_ARG, "chain %d step %d: unknown source %d", c, k, o.src);
+            // the unary steps ignore their operand
+            if (o.op == CT_OP_EXP || o.op == CT_OP_RSQRT || o.op == CT_OP_SQRT) continue;
+            const bool allowed = o.src == CT_SRC_IMM || o.src >= CT_SRC_A0 || (o.src == CT_SRC_C0 && c >= 1) ||
+                                 (c == 2 && (o.src == CT_SRC_C1 || o.src == CT_SRC_X));
+            if (!allowed) return fail(CT_ERR_INVALID_ARG, "chain %d step %d may not read source %d", c, k, o.src);
+            if (o.src >= CT_SRC_A0 && !arrays[o.src - CT_SRC_A0])
+                return fail(CT_ERR_INVALID_ARG, "chain %d step %d reads array a%d, which is NULL", c, k,
+                            o.src - CT_SRC_A0);
+            if (o.src == CT_SRC_X) reads_x = true;
+        }
+    }
+    if (reads_x && !x) return fail(CT_ERR_INVALID_ARG, "a step reads x, which is NULL");
+    const float* xr = reads_x ? x : nullptr;
+    if (xr && (const void*)xr == out && out_dtype != CT_F32)
+        return fail(CT_ERR_INVALID_ARG, "x == out needs fp32 output");
+    const bool ok = chain_channel_ok(outer, P, inner, out_dtype, out, xr);
+    if (mode == CT_BC_CHANNEL && !ok)
+        return fail(CT_ERR_UNSUPPORTED, "channel-bound broadcast needs inner >= 32, whole 16-byte vectors per "
+                                        "row, 16-byte aligned out and x, and a grid that fits");
+    const bool channel = mode == CT_BC_CHANNEL || (mode == CT_BC_AUTO && ok);
+    const hipError_t e = launch_broadcast_chain(prog, arrays, xr, out, out_dtype, outer, P, inner, channel,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "broadcast chain launch");
     return CT_OK;
 }
 

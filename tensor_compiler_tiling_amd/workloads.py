@@ -224,6 +224,52 @@ def depthwise_inputs(d: DepthwiseWorkload) -> dict:
     return {"x": to_dtype(x, d.dtype), "w": to_dtype(w, d.dtype), "bias": b, "var": v}
 
 
+@dataclass(frozen=True)
+class ChainWorkload:
+    """The general per-channel broadcast on [outer][P][inner]: `program` names
+    a step-chain recipe (batch-norm inference on a producer's fp32 output)."""
+    name: str
+    cfg_id: int
+    outer: int
+    P: int
+    inner: int
+    program: str
+    out_dtype: str = F32
+
+    def algorithmic_bytes(self) -> int:
+        """The producer's fp32 elements read once, the output written once, the
+        four per-channel arrays read once."""
+        n = self.outer * self.P * self.inner
+        return 4 * n + (4 if self.out_dtype == F32 else 2) * n + 16 * self.P
+
+
+# Batch-norm inference applied to a 128x256x32x32 fp32 activation:
+# out = (x - mean[c]) * gamma[c] / sqrt(var[c] + eps) + beta[c], as
+# c0 = gamma * rsqrt(var + eps), c1 = beta - mean * c0, out = x * c0 + c1.
+CHAIN_PROGRAMS = {
+    "batchnorm": ([("set", "a0"), ("add", 1e-5), ("rsqrt",), ("mul", "a1")],
+                  [("set", "a2"), ("mul", "c0"), ("rsub", "a3")],
+                  [("set", "x"), ("mul", "c0"), ("add", "c1")]),
+}
+
+CHAIN_WORKLOADS: Dict[str, ChainWorkload] = {c.name: c for c in [
+    ChainWorkload("bn_apply_f32_128x256x32x32", 80, 128, 256, 32 * 32, "batchnorm"),
+]}
+
+
+def chain_inputs(cw: ChainWorkload) -> dict:
+    """x ~ U[-1, 1] [outer, P, inner] (fp32); arrays a0 = var ~ U[0.5, 2],
+    a1 = gamma ~ U[0.5, 1.5], a2 = mean ~ N(0, 0.5), a3 = beta ~ N(0, 0.5);
+    seeds 1000 * cfg_id + {1, ..., 5}."""
+    base = 1000 * cw.cfg_id
+    x = np.random.default_rng(base + 1).uniform(-1.0, 1.0, (cw.outer, cw.P, cw.inner)).astype(np.float32)
+    a = [np.random.default_rng(base + 2).uniform(0.5, 2.0, cw.P),
+         np.random.default_rng(base + 3).uniform(0.5, 1.5, cw.P),
+         np.random.default_rng(base + 4).normal(0.0, 0.5, cw.P),
+         np.random.default_rng(base + 5).normal(0.0, 0.5, cw.P)]
+    return {"x": x, "arrays": [v.astype(np.float32) for v in a]}
+
+
 HEADLINE = "resnet_final_c512_7x7_k3"
 SWEEP = [n for n, w in CONV_WORKLOADS.items() if w.cfg_id >= 30]
 

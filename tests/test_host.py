@@ -2,6 +2,7 @@
 include/convtile.h declares, argument checking, the tile-config space (against
 the oracle's plain enumerator and the gist's printed space), the legality
 check, the default config, and the JSON-lines cache."""
+import ctypes
 import json
 import os
 import re
@@ -279,3 +280,73 @@ def test_depthwise_null_and_unsupported():
     # an output row wider than one workgroup's LDS window
     st = lib.ct_conv2d_nchw_depthwise(16, 16, 16, 1, 2, 4, 60000, 3, 3, 1, 1, 0, 0, None, None, 1e-5, None)
     assert st == ct.CT_ERR_UNSUPPORTED and "LDS" in ct.ct_last_error()
+
+
+# ------------------------------------------------------ general broadcast chain
+def test_chain_program_layout_matches_the_header():
+    """ct_bcast_program as ctypes sees it: 3 ints, then 3 x 8 steps of
+    (int, int, float)."""
+    assert ctypes.sizeof(ct.ct_chain_op) == 12
+    assert ctypes.sizeof(ct.ct_bcast_program) == 12 + 3 * 8 * 12
+    p = ct.make_program([("set", "a0"), ("add", 1e-5), ("rsqrt",)], [], [("set", "x"), ("mul", "c0")])
+    assert list(p.n_ops) == [3, 0, 2]
+    assert (p.ops[0][1].op, p.ops[0][1].src) == (ct.CHAIN_OPS["add"], ct.CHAIN_SRCS["imm"])
+    assert abs(p.ops[0][1].imm - 1e-5) < 1e-12
+    assert (p.ops[2][1].op, p.ops[2][1].src) == (ct.CHAIN_OPS["mul"], ct.CHAIN_SRCS["c0"])
+
+
+@pytest.mark.parametrize("case", [
+    "null_prog", "null_out", "zero_outer", "zero_P", "zero_inner", "dtype", "mode", "too_many_steps",
+    "bad_op", "bad_src", "c0_reads_x", "c0_reads_c1", "c1_reads_c1", "array_null", "x_null", "inplace_f16",
+])
+def test_chain_invalid_arguments_rejected_before_any_hip_call(case):
+    lib = ct.library()
+    prog = ct.make_program([("set", "a0")], [], [("set", "x"), ("mul", "c0")])
+    a = dict(prog=ctypes.byref(prog), a0=16, x=32, out=64, dt=ct.CT_F32, outer=2, P=3, inner=64, mode=0)
+    if case == "null_prog":
+        a["prog"] = None
+    elif case == "null_out":
+        a["out"] = None
+    elif case == "zero_outer":
+        a["outer"] = 0
+    elif case == "zero_P":
+        a["P"] = 0
+    elif case == "zero_inner":
+        a["inner"] = 0
+    elif case == "dtype":
+        a["dt"] = ct.CT_BF16
+    elif case == "mode":
+        a["mode"] = 7
+    elif case == "too_many_steps":
+        prog.n_ops[1] = 9
+    elif case == "bad_op":
+        prog.ops[0][0].op = 42
+    elif case == "bad_src":
+        prog.ops[0][0].src = 8
+    elif case == "c0_reads_x":
+        prog.ops[0][0].src = ct.CHAIN_SRCS["x"]
+    elif case == "c0_reads_c1":
+        prog.ops[0][0].src = ct.CHAIN_SRCS["c1"]
+    elif case == "c1_reads_c1":
+        prog.n_ops[1] = 1
+        prog.ops[1][0].op, prog.ops[1][0].src = ct.CHAIN_OPS["set"], ct.CHAIN_SRCS["c1"]
+    elif case == "array_null":
+        a["a0"] = None
+    elif case == "x_null":
+        a["x"] = None
+    elif case == "inplace_f16":
+        a["dt"], a["out"] = ct.CT_F16, a["x"]
+    st = lib.ct_broadcast_chain(a["prog"], a["a0"], None, None, None, a["x"], a["out"], a["dt"], a["outer"],
+                                a["P"], a["inner"], a["mode"], None)
+    assert st == ct.CT_ERR_INVALID_ARG, (case, ct.ct_last_error())
+
+
+def test_chain_channel_mode_unsupported_shapes():
+    """CT_BC_CHANNEL where the channel-bound conditions fail: an error before
+    any launch (inner < 32, rows not whole 16-byte vectors, misaligned out)."""
+    lib = ct.library()
+    prog = ct.make_program([("set", 1.0)], [], [])
+    for inner, out, dt in [(16, 256, ct.CT_F32), (34, 256, ct.CT_F32), (36, 256, ct.CT_F16), (64, 260, ct.CT_F32)]:
+        st = lib.ct_broadcast_chain(ctypes.byref(prog), None, None, None, None, None, out, dt, 4, 3, inner,
+                                    ct.CT_BC_CHANNEL, None)
+        assert st == ct.CT_ERR_UNSUPPORTED, (inner, out, dt, ct.ct_last_error())
