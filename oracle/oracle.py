@@ -24,6 +24,8 @@ What it holds:
 * the depthwise convolution in fp64 (the definition written out in numpy: one
   strided slice of the zero-padded input per tap, summed in row-major tap
   order), another operator the tutorial's opening names;
+* the ridge regression that the guided tile-config search fits as its cost
+  model (the normal equations, one library solve);
 * the general per-channel broadcast [1,P,1] => [B,P,B] of the Paddle PR's
   Introduction, with a chain of div / exp / rsqrt-style steps (Performance
   Impact), evaluated step by step in fp64 over numpy broadcasting.
@@ -266,6 +268,15 @@ def broadcast_chain(chains, outer: int, P: int, inner: int, arrays=(), x=None) -
     c1 = run(chains[1], {"c0": c0})
     v = run(chains[2], {"c0": c0, "c1": c1, "x": X}) if len(chains[2]) else c0
     return np.broadcast_to(v, (outer, P, inner)).astype(np.float64).copy()
+
+
+def ridge_fit(X, y, lam: float) -> np.ndarray:
+    """The ridge regression the guided search fits (its cost model): w
+    minimising |X w - y|^2 + lam |w|^2, from the normal equations
+    (X^T X + lam I) w = X^T y solved by a library routine."""
+    X = _f64(X)
+    y = _f64(y)
+    return np.linalg.solve(X.T @ X + lam * np.eye(X.shape[1]), X.T @ y)
 
 
 def conv_flops(N, CI, H, W, CO, KH, KW, stride, pad) -> int:

@@ -492,3 +492,22 @@ def test_chain_identity_and_c1():
     out = O.broadcast_chain(([("set", "a0")], [("set", "c0"), ("mul", 2.0)], [("set", "x"), ("mul", "c1")]),
                             2, 3, 4, [a0], x)
     assert np.array_equal(out, x * (a0 * 2.0)[None, :, None])
+
+
+# ---- the guided search's cost model -----------------------------------------
+def test_ridge_recovers_an_exact_linear_model():
+    """y = X w exactly and lam = 0: the fit returns w (a closed form)."""
+    r = np.random.default_rng(500)
+    X = np.column_stack([np.ones(30), r.normal(size=(30, 4))])
+    w = np.array([0.5, -1.0, 2.0, 0.25, 3.0])
+    np.testing.assert_allclose(O.ridge_fit(X, X @ w, 0.0), w, rtol=1e-10, atol=1e-12)
+
+
+def test_ridge_hand_case_and_shrinkage():
+    """One feature x = (1, 2), y = (2, 4): w = sum(xy) / (sum(x^2) + lam) =
+    10 / (5 + lam), worked by hand; a huge lam shrinks w to 0."""
+    X = np.array([[1.0], [2.0]])
+    y = np.array([2.0, 4.0])
+    assert abs(O.ridge_fit(X, y, 0.0)[0] - 2.0) < 1e-15
+    assert abs(O.ridge_fit(X, y, 5.0)[0] - 1.0) < 1e-15
+    assert abs(O.ridge_fit(X, y, 1e12)[0]) < 1e-10
