@@ -296,6 +296,36 @@ int ct_conv2d_tune(int N, int CI, int H, int W, int CO, int KH, int KW,
                    ct_tile_config* best_out,
                    ct_tune_record* records, int max_records, int* n_records);
 
+/* Guided search for spaces too large to time exhaustively (the role of the
+ * TVM tutorial's cost-model tuner, XGBTuner, in Step 2).  Times at most
+ * `max_trials` legal configs (0 = all), `batch` at a time: the first batch
+ * drawn uniformly (SplitMix64 on `seed`), each later one the lowest
+ * predictions of a ridge regression of log(time) on 11 features of a config
+ * (ct_ridge_fit, lambda 1e-3, refitted after every batch) plus max(1,
+ * batch/4) uniform draws among the untimed configs.  Trials, records, the
+ * cache entry and errors as ct_conv2d_tune; CT_ERR_INVALID_ARG also for
+ * batch < 1. */
+int ct_conv2d_tune_guided(int N, int CI, int H, int W, int CO, int KH, int KW,
+                          int stride, int pad, int dtype, int epilogue,
+                          int max_trials, int batch, unsigned long long seed,
+                          float min_repeat_ms, void* stream,
+                          ct_tile_config* best_out,
+                          ct_tune_record* records, int max_records, int* n_records);
+
+/* The guided search's parts on host data (no device): ct_ridge_fit solves
+ * min |X w - y|^2 + lambda |w|^2 (X row-major n x d, 1 <= d <= 64) by a
+ * Cholesky factorisation, CT_ERR_INVALID_ARG when X^T X + lambda I is
+ * singular; ct_guided_search_table runs the search of ct_conv2d_tune_guided
+ * over n points with features feats (n x d) whose costs are given (cost <= 0
+ * or not finite = a failed trial, left out of the fit), with n_explore
+ * draws a batch after the first, and writes the order in which it would time
+ * them (at most max_trials) to order_out, their count to *n_order. */
+int ct_ridge_fit(const double* X, const double* y, int n, int d, double lambda, double* w);
+int ct_guided_search_table(const double* feats, const double* costs, int n, int d,
+                           int max_trials, int batch, int n_explore,
+                           unsigned long long seed, double lambda,
+                           int* order_out, int* n_order);
+
 /* The config ct_conv2d_nchw_fwd would use for this shape; *from_cache = 1
  * when it came from a tuning record, 0 when it is the built-in default. */
 int ct_conv2d_query(int N, int CI, int H, int W, int CO, int KH, int KW,

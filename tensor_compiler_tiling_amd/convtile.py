@@ -93,6 +93,10 @@ _SIGS = {
     "ct_conv2d_tune": (_I, _SHAPE + [_I, _F, _P, ctypes.POINTER(ct_tile_config),
                                      ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
     "ct_conv2d_query": (_I, _SHAPE + [ctypes.POINTER(ct_tile_config), ctypes.POINTER(_I)]),
+    "ct_conv2d_tune_guided": (_I, _SHAPE + [_I, _I, ctypes.c_ulonglong, _F, _P, ctypes.POINTER(ct_tile_config),
+                                            ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
+    "ct_ridge_fit": (_I, [_P, _P, _I, _I, ctypes.c_double, _P]),
+    "ct_guided_search_table": (_I, [_P, _P, _I, _I, _I, _I, _I, ctypes.c_ulonglong, ctypes.c_double, _P, _P]),
     "ct_gemm_fwd": (_I, [_P, _P, _P] + [_I] * 5 + [_P, _P, _F, _P]),
     "ct_gemm_tune": (_I, [_I] * 5 + [_I, _F, _P, ctypes.POINTER(ct_tile_config),
                                    ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
@@ -248,6 +252,41 @@ def ct_broadcast_chain(prog, a0, a1, a2, a3, x, out, out_dtype, outer, P, inner,
                        stream=None) -> int:
     return _load().ct_broadcast_chain(ctypes.byref(prog), _ptr(a0), _ptr(a1), _ptr(a2), _ptr(a3), _ptr(x),
                                       _ptr(out), out_dtype, outer, P, inner, mode, _stream(stream))
+
+
+def ct_conv2d_tune_guided(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials=64, batch=8,
+                          seed=0, min_repeat_ms=100.0, stream=None, max_records=4096):
+    best = ct_tile_config()
+    recs = (ct_tune_record * max(max_records, 1))()
+    n = _I(0)
+    st = _load().ct_conv2d_tune_guided(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials, batch,
+                                       seed, min_repeat_ms, _stream(stream), ctypes.byref(best), recs, max_records,
+                                       ctypes.byref(n))
+    return st, best, [recs[i] for i in range(n.value)]
+
+
+def ct_ridge_fit(X, y, lam=0.0):
+    """numpy in, numpy out: (status, w)."""
+    import numpy as np
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    n, d = X.shape
+    w = np.zeros(d, np.float64)
+    st = _load().ct_ridge_fit(X.ctypes.data, y.ctypes.data, n, d, float(lam), w.ctypes.data)
+    return st, w
+
+
+def ct_guided_search_table(feats, costs, max_trials, batch, n_explore, seed=0, lam=1e-3):
+    """numpy in: (status, order of the points the search would time)."""
+    import numpy as np
+    F = np.ascontiguousarray(feats, dtype=np.float64)
+    c = np.ascontiguousarray(costs, dtype=np.float64)
+    n, d = F.shape
+    order = np.zeros(max(max_trials, 1), np.int32)
+    cnt = _I(0)
+    st = _load().ct_guided_search_table(F.ctypes.data, c.ctypes.data, n, d, max_trials, batch, n_explore, seed,
+                                        float(lam), order.ctypes.data, ctypes.addressof(cnt))
+    return st, order[:cnt.value].tolist()
 
 
 def ct_gemm_tune(M, N, K, dtype, epilogue, max_trials=0, min_repeat_ms=100.0, stream=None,

@@ -22,6 +22,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <fstream>
+#include <functional>
 #include <map>
 #include <mutex>
 #include <sstream>
@@ -1159,88 +1160,71 @@ std::map<long long, int> injected_errors() {
     return m;
 }
 
-}  // namespace
-
-int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad, int dtype,
-              int epilogue, int max_trials, float min_repeat_ms, void* stream,
-              ct_tile_config* best_out, ct_tune_record* records, int max_records, int* n_records) {
+// Device-side state of a search: scratch inputs filled on the device, the
+// direct kernel's reference output, events; trial() times one candidate the
+// way the TVM tutorial's runner does (a check of the output, then `repeat`
+// measurements of at least min_repeat_ms each, a per-trial time limit).
+struct TuneBench {
     Shape s;
-    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
-    if (st != CT_OK) return st;
-    if (!best_out) return fail(CT_ERR_INVALID_ARG, "best_out must not be NULL");
-    if (max_trials < 0) return fail(CT_ERR_INVALID_ARG, "max_trials must be >= 0");
-    if (!(min_repeat_ms >= 0.0f)) return fail(CT_ERR_INVALID_ARG, "min_repeat_ms must be >= 0");
-    if (max_records < 0 || (max_records > 0 && !records))
-        return fail(CT_ERR_INVALID_ARG, "records / max_records mismatch");
-    if (n_records) *n_records = 0;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    const double kTimeout = 4.0;  // seconds per trial
-    const int kRepeat = 3;
-
-    // search order: legal points by predicted time, then illegal points
-    Space sp = space_of(s);
-    std::vector<std::pair<double, long long>> order;
-    std::vector<long long> illegal;
-    for (long long i = 0; i < sp.size(); ++i) {
-        ct_tile_config c;
-        decode(sp, i, &c);
-        Resolved r;
-        if (legal(s, c, &r, nullptr))
-            order.push_back({predict_us(s, c, r), i});
-        else
-            illegal.push_back(i);
-    }
-    std::stable_sort(order.begin(), order.end());
-    std::vector<long long> trials;
-    for (auto& o : order) trials.push_back(o.second);
-    for (long long i : illegal) trials.push_back(i);
-    if (max_trials > 0 && (long long)trials.size() > max_trials) trials.resize(max_trials);
-
-    // scratch inputs, filled on the device
+    Space sp;
+    hipStream_t hs = nullptr;
     Scratch sc;
-    const size_t esz = dtype == CT_F32 ? 4 : 2;
-    const long long nx = (long long)N * CI * H * W, nw = (long long)CO * s.K;
-    const long long ny = s.P * CO;
-    hipError_t e;
-    if ((e = hipMalloc(&sc.x, nx * esz)) != hipSuccess ||
-        (e = hipMalloc(&sc.w, nw * esz)) != hipSuccess ||
-        (e = hipMalloc((void**)&sc.y, ny * 4)) != hipSuccess ||
-        (e = hipMalloc((void**)&sc.y_ref, ny * 4)) != hipSuccess ||
-        (e = hipMalloc((void**)&sc.bias, CO * 4)) != hipSuccess ||
-        (e = hipMalloc((void**)&sc.var, CO * 4)) != hipSuccess ||
-        (e = hipMalloc((void**)&sc.bad, 4)) != hipSuccess)
-        return fail(CT_ERR_NO_MEMORY, "tuning scratch: %s", hipGetErrorString(e));
-    const float wa = std::sqrt(6.0f / (float)s.K);
-    if ((e = launch_fill_uniform(sc.x, nx, dtype, -1.0f, 1.0f, 11u, hs)) != hipSuccess ||
-        (e = launch_fill_uniform(sc.w, nw, dtype, -wa, wa, 12u, hs)) != hipSuccess ||
-        (e = launch_fill_uniform(sc.bias, CO, CT_F32, -0.2f, 0.2f, 13u, hs)) != hipSuccess ||
-        (e = launch_fill_uniform(sc.var, CO, CT_F32, 0.5f, 2.0f, 14u, hs)) != hipSuccess)
-        return hip_fail(e, "tuning scratch fill");
-    const float eps = 1e-5f;
-    st = launch_direct(s, sc.x, sc.w, sc.y_ref, sc.bias, sc.var, eps, hs);
-    if (st != CT_OK) return st;
-    if ((e = hipStreamSynchronize(hs)) != hipSuccess) return hip_fail(e, "reference run");
-    // expected sum |x w| is about K * E|x| * E|w| = K * wa / 4; allow 1e-4 of twice that
-    const float atol = 1e-4f * (float)s.K * wa * 0.5f;
-    const float rtol = epilogue == CT_EPI_EXP_BIAS_RSQRT ? atol + 1e-5f : 1e-5f;
+    hipEvent_t ev0 = nullptr, ev1 = nullptr;
+    float atol = 0, rtol = 0, eps = 1e-5f;
+    float min_repeat_ms = 0;
+    long long ny = 0;
+    std::map<long long, int> inject;
+    static constexpr double kTimeout = 4.0;  // seconds per trial
+    static constexpr int kRepeat = 3;
 
-    hipEvent_t ev0, ev1;
-    if ((e = hipEventCreate(&ev0)) != hipSuccess) return hip_fail(e, "hipEventCreate");
-    if ((e = hipEventCreate(&ev1)) != hipSuccess) {
-        (void)hipEventDestroy(ev0);
-        return hip_fail(e, "hipEventCreate");
+    ~TuneBench() {
+        if (ev0) (void)hipEventDestroy(ev0);
+        if (ev1) (void)hipEventDestroy(ev1);
     }
-    const auto inject = injected_errors();
-    ct_tile_config best{};
-    best.variant = -1;
-    double best_mean = 1e300;
-    int nrec = 0;
-    for (long long idx : trials) {
+
+    int init(const Shape& shape, void* stream, float repeat_ms) {
+        s = shape;
+        sp = space_of(s);
+        hs = static_cast<hipStream_t>(stream);
+        min_repeat_ms = repeat_ms;
+        const size_t esz = s.dtype == CT_F32 ? 4 : 2;
+        const long long nx = (long long)s.N * s.CI * s.H * s.W, nw = (long long)s.CO * s.K;
+        ny = s.P * s.CO;
+        hipError_t e;
+        if ((e = hipMalloc(&sc.x, nx * esz)) != hipSuccess || (e = hipMalloc(&sc.w, nw * esz)) != hipSuccess ||
+            (e = hipMalloc((void**)&sc.y, ny * 4)) != hipSuccess ||
+            (e = hipMalloc((void**)&sc.y_ref, ny * 4)) != hipSuccess ||
+            (e = hipMalloc((void**)&sc.bias, s.CO * 4)) != hipSuccess ||
+            (e = hipMalloc((void**)&sc.var, s.CO * 4)) != hipSuccess ||
+            (e = hipMalloc((void**)&sc.bad, 4)) != hipSuccess)
+            return fail(CT_ERR_NO_MEMORY, "tuning scratch: %s", hipGetErrorString(e));
+        const float wa = std::sqrt(6.0f / (float)s.K);
+        if ((e = launch_fill_uniform(sc.x, nx, s.dtype, -1.0f, 1.0f, 11u, hs)) != hipSuccess ||
+            (e = launch_fill_uniform(sc.w, nw, s.dtype, -wa, wa, 12u, hs)) != hipSuccess ||
+            (e = launch_fill_uniform(sc.bias, s.CO, CT_F32, -0.2f, 0.2f, 13u, hs)) != hipSuccess ||
+            (e = launch_fill_uniform(sc.var, s.CO, CT_F32, 0.5f, 2.0f, 14u, hs)) != hipSuccess)
+            return hip_fail(e, "tuning scratch fill");
+        const int st = launch_direct(s, sc.x, sc.w, sc.y_ref, sc.bias, sc.var, eps, hs);
+        if (st != CT_OK) return st;
+        if ((e = hipStreamSynchronize(hs)) != hipSuccess) return hip_fail(e, "reference run");
+        // expected sum |x w| is about K * E|x| * E|w| = K * wa / 4; allow 1e-4 of twice that
+        atol = 1e-4f * (float)s.K * wa * 0.5f;
+        rtol = s.epilogue == CT_EPI_EXP_BIAS_RSQRT ? atol + 1e-5f : 1e-5f;
+        if ((e = hipEventCreate(&ev0)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+        if ((e = hipEventCreate(&ev1)) != hipSuccess) return hip_fail(e, "hipEventCreate");
+        inject = injected_errors();
+        return CT_OK;
+    }
+
+    // Time candidate idx; fills *rec (cfg, costs, error_no, wall time).
+    void trial(long long idx, ct_tune_record* rec) {
         const auto t_start = std::chrono::steady_clock::now();
         ct_tile_config c;
         decode(sp, idx, &c);
-        ct_tune_record rec{};
+        *rec = ct_tune_record{};
         int err = CT_TRIAL_OK;
+        int st = CT_OK;
+        hipError_t e;
         auto inj = inject.find(idx);
         Resolved r;
         if (inj != inject.end()) {
@@ -1250,8 +1234,7 @@ int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, i
         } else {
             // poison the output so a kernel that writes nothing cannot pass
             e = hipMemsetAsync(sc.y, 0xff, ny * 4, hs);
-            st = (e == hipSuccess) ? launch_tiled(s, c, sc.x, sc.w, sc.y, sc.bias, sc.var, eps, hs)
-                                   : CT_ERR_HIP;
+            st = (e == hipSuccess) ? launch_tiled(s, c, sc.x, sc.w, sc.y, sc.bias, sc.var, eps, hs) : CT_ERR_HIP;
             if (st == CT_OK && (e = hipStreamSynchronize(hs)) != hipSuccess) st = CT_ERR_HIP;
             if (st == CT_OK) {
                 unsigned bad = 0;
@@ -1277,8 +1260,8 @@ int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, i
                         break;
                     }
                     (void)hipEventElapsedTime(&ms, ev0, ev1);
-                    const double wall = std::chrono::duration<double>(
-                                            std::chrono::steady_clock::now() - t_start).count();
+                    const double wall =
+                        std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
                     if (wall > kTimeout) {
                         err = CT_TRIAL_TIMEOUT;
                         break;
@@ -1298,47 +1281,46 @@ int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, i
                         break;
                     }
                     (void)hipEventElapsedTime(&ms, ev0, ev1);
-                    rec.costs_us[rep] = 1000.0f * ms / (float)number;
-                    rec.n_costs = rep + 1;
-                    const double wall = std::chrono::duration<double>(
-                                            std::chrono::steady_clock::now() - t_start).count();
+                    rec->costs_us[rep] = 1000.0f * ms / (float)number;
+                    rec->n_costs = rep + 1;
+                    const double wall =
+                        std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
                     if (wall > kTimeout) err = CT_TRIAL_TIMEOUT;
                 }
             }
         }
-        rec.error_no = err;
-        rec.all_cost_s =
-            std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
-        rec.timestamp = now_s();
+        rec->error_no = err;
+        rec->all_cost_s = std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+        rec->timestamp = now_s();
         c.error_no = err;
-        if (err == CT_TRIAL_OK && rec.n_costs == kRepeat) {
+        c.us = 0.0f;
+        if (err == CT_TRIAL_OK && rec->n_costs == kRepeat) {
             double mean = 0;
-            for (int i = 0; i < kRepeat; ++i) mean += rec.costs_us[i];
-            mean /= kRepeat;
-            c.us = (float)mean;
-            if (mean < best_mean || (mean == best_mean && idx < best.index)) {
-                best_mean = mean;
-                best = c;
-            }
+            for (int i = 0; i < kRepeat; ++i) mean += rec->costs_us[i];
+            c.us = (float)(mean / kRepeat);
         }
-        rec.cfg = c;
-        if (nrec < max_records) records[nrec] = rec;
-        ++nrec;
-        if (log_debug())
-            fprintf(stderr, "[convtile tune] No: %d index %lld %s S=%d stages=%d kc=%d  %.3f us  "
-                            "error_no=%d all_cost=%.3fs\n",
-                    nrec, idx, variants()[c.variant].desc.name, c.split_k, c.stages, c.kc,
-                    (double)c.us, err, rec.all_cost_s);
+        rec->cfg = c;
     }
-    (void)hipEventDestroy(ev0);
-    (void)hipEventDestroy(ev1);
-    if (n_records) *n_records = std::min(nrec, max_records);
+};
+
+// Keep the best of the timed records and store the winner in the cache (and
+// in the file named by CT_CACHE_PATH).
+int tune_finish(const Shape& s, const std::vector<ct_tune_record>& recs, ct_tile_config* best_out,
+                ct_tune_record* records, int max_records, int* n_records) {
+    ct_tile_config best{};
+    best.variant = -1;
+    for (size_t k = 0; k < recs.size(); ++k) {
+        const ct_tune_record& r = recs[k];
+        if ((int)k < max_records) records[k] = r;
+        if (r.error_no != CT_TRIAL_OK || r.n_costs != TuneBench::kRepeat) continue;
+        if (best.variant < 0 || r.cfg.us < best.us || (r.cfg.us == best.us && r.cfg.index < best.index))
+            best = r.cfg;
+    }
+    if (n_records) *n_records = std::min((int)recs.size(), max_records);
     if (best.variant < 0) return fail(CT_ERR_TUNE_FAILED, "no candidate ran correctly");
     *best_out = best;
-    // record the winner: in memory, and in the file named by CT_CACHE_PATH
     float costs[1] = {best.us};
-    const std::string line = json_record(s, best, variants()[best.variant].desc.name, costs, 1,
-                                         0.0, now_s());
+    const std::string line = json_record(s, best, variants()[best.variant].desc.name, costs, 1, 0.0, now_s());
     {
         std::lock_guard<std::mutex> lk(g_cache_mu);
         g_cache[s.key()] = CacheEntry{variants()[best.variant].desc.name, best, line};
@@ -1352,7 +1334,293 @@ int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, i
     return CT_OK;
 }
 
+int tune_args(int max_trials, float min_repeat_ms, ct_tile_config* best_out, ct_tune_record* records,
+              int max_records, int* n_records) {
+    if (!best_out) return fail(CT_ERR_INVALID_ARG, "best_out must not be NULL");
+    if (max_trials < 0) return fail(CT_ERR_INVALID_ARG, "max_trials must be >= 0");
+    if (!(min_repeat_ms >= 0.0f)) return fail(CT_ERR_INVALID_ARG, "min_repeat_ms must be >= 0");
+    if (max_records < 0 || (max_records > 0 && !records))
+        return fail(CT_ERR_INVALID_ARG, "records / max_records mismatch");
+    if (n_records) *n_records = 0;
+    return CT_OK;
+}
+
+void log_trial(int no, const ct_tune_record& rec) {
+    if (log_debug())
+        fprintf(stderr, "[convtile tune] No: %d index %lld %s S=%d stages=%d kc=%d  %.3f us  error_no=%d all_cost=%.3fs\n",
+                no, rec.cfg.index, variants()[rec.cfg.variant].desc.name, rec.cfg.split_k, rec.cfg.stages,
+                rec.cfg.kc, (double)rec.cfg.us, rec.error_no, rec.all_cost_s);
+}
+
+}  // namespace
+
+int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad, int dtype,
+              int epilogue, int max_trials, float min_repeat_ms, void* stream,
+              ct_tile_config* best_out, ct_tune_record* records, int max_records, int* n_records) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    st = tune_args(max_trials, min_repeat_ms, best_out, records, max_records, n_records);
+    if (st != CT_OK) return st;
+
+    // search order: legal points by predicted time, then illegal points
+    Space sp = space_of(s);
+    std::vector<std::pair<double, long long>> order;
+    std::vector<long long> illegal;
+    for (long long i = 0; i < sp.size(); ++i) {
+        ct_tile_config c;
+        decode(sp, i, &c);
+        Resolved r;
+        if (legal(s, c, &r, nullptr))
+            order.push_back({predict_us(s, c, r), i});
+        else
+            illegal.push_back(i);
+    }
+    std::stable_sort(order.begin(), order.end());
+    std::vector<long long> trials;
+    for (auto& o : order) trials.push_back(o.second);
+    for (long long i : illegal) trials.push_back(i);
+    if (max_trials > 0 && (long long)trials.size() > max_trials) trials.resize(max_trials);
+
+    TuneBench tb;
+    st = tb.init(s, stream, min_repeat_ms);
+    if (st != CT_OK) return st;
+    std::vector<ct_tune_record> recs;
+    for (long long idx : trials) {
+        ct_tune_record rec;
+        tb.trial(idx, &rec);
+        recs.push_back(rec);
+        log_trial((int)recs.size(), rec);
+    }
+    return tune_finish(s, recs, best_out, records, max_records, n_records);
+}
+
+// ------------------------------------------------------- guided search --
+// The TVM tutorial tunes with a cost-model-guided tuner (XGBTuner, Step 2):
+// fit a model on the configs measured so far and measure next the ones it
+// ranks best.  Here the model is a ridge regression of log(time) on a few
+// features of a config, refitted after every batch; each batch is the
+// model's lowest predictions among the untimed points plus a few uniform
+// draws (exploration); the first batch is all draws.
+
+namespace {
+
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", 2014): the generator's output function on a counter.
+uint64_t splitmix64(uint64_t x) {
+    x += 0x9e3779b97f4a7c15ULL;
+    x = (x ^ (x >> 30)) * 0xbf58476d1ce4e5b9ULL;
+    x = (x ^ (x >> 27)) * 0x94d049bb133111ebULL;
+    return x ^ (x >> 31);
+}
+
+// Minimise |X w - y|^2 + lambda |w|^2 (X row-major n x d) by a Cholesky
+// factorisation of X^T X + lambda I.  False if that matrix is not positive
+// definite (lambda = 0 and X rank-deficient).
+bool ridge(const double* X, const double* y, int n, int d, double lambda, double* w) {
+    std::vector<double> A((size_t)d * d, 0.0), b(d, 0.0);
+    for (int i = 0; i < n; ++i)
+        for (int j = 0; j < d; ++j) {
+            b[j] += X[(size_t)i * d + j] * y[i];
+            for (int k = 0; k <= j; ++k) A[(size_t)j * d + k] += X[(size_t)i * d + j] * X[(size_t)i * d + k];
+        }
+    for (int j = 0; j < d; ++j) A[(size_t)j * d + j] += lambda;
+    // A = L L^T, lower triangle in place
+    for (int j = 0; j < d; ++j) {
+        double v = A[(size_t)j * d + j];
+        for (int k = 0; k < j; ++k) v -= A[(size_t)j * d + k] * A[(size_t)j * d + k];
+        if (!(v > 1e-300)) return false;
+        const double l = std::sqrt(v);
+        A[(size_t)j * d + j] = l;
+        for (int i = j + 1; i < d; ++i) {
+            double u = A[(size_t)i * d + j];
+            for (int k = 0; k < j; ++k) u -= A[(size_t)i * d + k] * A[(size_t)j * d + k];
+            A[(size_t)i * d + j] = u / l;
+        }
+    }
+    // L z = b, then L^T w = z
+    std::vector<double> z(d);
+    for (int i = 0; i < d; ++i) {
+        double u = b[i];
+        for (int k = 0; k < i; ++k) u -= A[(size_t)i * d + k] * z[k];
+        z[i] = u / A[(size_t)i * d + i];
+    }
+    for (int i = d - 1; i >= 0; --i) {
+        double u = z[i];
+        for (int k = i + 1; k < d; ++k) u -= A[(size_t)k * d + i] * w[k];
+        w[i] = u / A[(size_t)i * d + i];
+    }
+    return true;
+}
+
+// The next batch: up to `batch` untimed points, the lowest `batch -
+// n_explore` by pred (ties by index; none when pred is null) and the rest
+// drawn uniformly from the untimed points left, draw k of round r taking
+// splitmix64(seed ^ (r << 32) ^ k) modulo the count.
+std::vector<int> guided_select(const double* pred, int n, const std::vector<char>& timed, int batch, int n_explore,
+                               uint64_t seed, int round) {
+    std::vector<int> out;
+    std::vector<char> taken(timed.begin(), timed.end());
+    if (pred) {
+        std::vector<int> cand;
+        for (int i = 0; i < n; ++i)
+            if (!taken[i]) cand.push_back(i);
+        std::stable_sort(cand.begin(), cand.end(), [&](int a, int b) { return pred[a] < pred[b]; });
+        for (int i : cand) {
+            if ((int)out.size() >= batch - n_explore) break;
+            out.push_back(i);
+            taken[i] = 1;
+        }
+    }
+    std::vector<int> rest;
+    for (int i = 0; i < n; ++i)
+        if (!taken[i]) rest.push_back(i);
+    for (uint64_t k = 0; (int)out.size() < batch && !rest.empty(); ++k) {
+        const uint64_t r = splitmix64(seed ^ ((uint64_t)round << 32) ^ k);
+        const size_t j = (size_t)(r % rest.size());
+        out.push_back(rest[j]);
+        rest[j] = rest.back();
+        rest.pop_back();
+    }
+    return out;
+}
+
+// The search: measure(i) returns the cost of point i (> 0), or <= 0 / not
+// finite for a failed trial, which is left out of the fit.  Returns the
+// points in the order they were measured (at most max_trials of them).
+std::vector<int> guided_search(int n, int d, const double* feats, int max_trials, int batch, int n_explore,
+                               uint64_t seed, double lambda, const std::function<double(int)>& measure) {
+    std::vector<int> order;
+    std::vector<char> timed(n, 0);
+    std::vector<double> X, y;
+    std::vector<double> w(d), pred(n);
+    const int budget = std::min(max_trials, n);
+    bool have_model = false;
+    for (int round = 0; (int)order.size() < budget; ++round) {
+        const int want = std::min(batch, budget - (int)order.size());
+        const auto next = guided_select(have_model ? pred.data() : nullptr, n, timed, want,
+                                        have_model ? std::min(n_explore, want) : want, seed, round);
+        if (next.empty()) break;
+        for (int i : next) {
+            timed[i] = 1;
+            order.push_back(i);
+            const double c = measure(i);
+            if (c > 0.0 && std::isfinite(c)) {
+                X.insert(X.end(), feats + (size_t)i * d, feats + (size_t)(i + 1) * d);
+                y.push_back(std::log(c));
+            }
+        }
+        have_model = !y.empty() && ridge(X.data(), y.data(), (int)y.size(), d, lambda, w.data());
+        if (have_model)
+            for (int i = 0; i < n; ++i) {
+                double v = 0.0;
+                for (int j = 0; j < d; ++j) v += feats[(size_t)i * d + j] * w[j];
+                pred[i] = v;
+            }
+    }
+    return order;
+}
+
+constexpr int kFeatures = 11;
+
+// Features of a legal config: an intercept, the analytic time estimate,
+// and log sizes of the split, the stages, the channels a stage, the tile,
+// the workgroup, the grid, the grid's shortfall from one workgroup per CU,
+// and the LDS a workgroup holds.
+void config_features(const Shape& s, const ct_tile_config& c, const Resolved& r, double* f) {
+    const auto& d = r.v->desc;
+    const double lg = std::log2(std::max<double>((double)r.grid, 1.0));
+    f[0] = 1.0;
+    f[1] = std::log2(std::max(predict_us(s, c, r), 1e-3));
+    f[2] = std::log2((double)c.split_k);
+    f[3] = std::log2((double)c.stages);
+    f[4] = std::log2((double)c.kc);
+    f[5] = std::log2((double)std::max(d.tile_m, 1));
+    f[6] = std::log2((double)std::max(d.tile_n, 1));
+    f[7] = std::log2((double)std::max(d.threads, 1));
+    f[8] = lg;
+    f[9] = std::max(0.0, std::log2((double)kNumCU) - lg);
+    f[10] = std::log2(1.0 + (double)r.lds);
+}
+
+}  // namespace
+
+int tune_guided_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad, int dtype,
+                     int epilogue, int max_trials, int batch, unsigned long long seed, float min_repeat_ms,
+                     void* stream, ct_tile_config* best_out, ct_tune_record* records, int max_records,
+                     int* n_records) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    st = tune_args(max_trials, min_repeat_ms, best_out, records, max_records, n_records);
+    if (st != CT_OK) return st;
+    if (batch < 1) return fail(CT_ERR_INVALID_ARG, "batch must be >= 1");
+    Space sp = space_of(s);
+    std::vector<long long> idx;
+    std::vector<double> feats;
+    for (long long i = 0; i < sp.size(); ++i) {
+        ct_tile_config c;
+        decode(sp, i, &c);
+        Resolved r;
+        if (!legal(s, c, &r, nullptr)) continue;
+        idx.push_back(i);
+        feats.resize(feats.size() + kFeatures);
+        config_features(s, c, r, feats.data() + feats.size() - kFeatures);
+    }
+    if (idx.empty()) return fail(CT_ERR_TUNE_FAILED, "no legal config for this shape");
+    TuneBench tb;
+    st = tb.init(s, stream, min_repeat_ms);
+    if (st != CT_OK) return st;
+    std::vector<ct_tune_record> recs;
+    const int n = (int)idx.size();
+    const int budget = max_trials == 0 ? n : std::min(max_trials, n);
+    (void)guided_search(n, kFeatures, feats.data(), budget, batch, std::max(1, batch / 4), seed, 1e-3,
+                        [&](int i) -> double {
+                            ct_tune_record rec;
+                            tb.trial(idx[i], &rec);
+                            recs.push_back(rec);
+                            log_trial((int)recs.size(), rec);
+                            return rec.error_no == CT_TRIAL_OK ? (double)rec.cfg.us : -1.0;
+                        });
+    return tune_finish(s, recs, best_out, records, max_records, n_records);
+}
+
 }  // namespace ct
+
+extern "C" {
+
+int ct_ridge_fit(const double* X, const double* y, int n, int d, double lambda, double* w) {
+    if (!X || !y || !w) return fail(CT_ERR_INVALID_ARG, "X, y and w must not be NULL");
+    if (n < 1 || d < 1 || d > 64) return fail(CT_ERR_INVALID_ARG, "need n >= 1 and 1 <= d <= 64");
+    if (!(lambda >= 0.0)) return fail(CT_ERR_INVALID_ARG, "lambda must be >= 0");
+    if (!ct::ridge(X, y, n, d, lambda, w)) return fail(CT_ERR_INVALID_ARG, "X^T X + lambda I is singular");
+    return CT_OK;
+}
+
+int ct_guided_search_table(const double* feats, const double* costs, int n, int d, int max_trials, int batch,
+                           int n_explore, unsigned long long seed, double lambda, int* order_out, int* n_order) {
+    if (!feats || !costs || !order_out || !n_order)
+        return fail(CT_ERR_INVALID_ARG, "feats, costs, order_out and n_order must not be NULL");
+    if (n < 1 || d < 1 || d > 64) return fail(CT_ERR_INVALID_ARG, "need n >= 1 and 1 <= d <= 64");
+    if (max_trials < 1 || batch < 1 || n_explore < 0 || n_explore > batch)
+        return fail(CT_ERR_INVALID_ARG, "need max_trials >= 1, batch >= 1 and 0 <= n_explore <= batch");
+    if (!(lambda >= 0.0)) return fail(CT_ERR_INVALID_ARG, "lambda must be >= 0");
+    const auto order = ct::guided_search(n, d, feats, max_trials, batch, n_explore, seed, lambda,
+                                         [&](int i) { return costs[i]; });
+    for (size_t k = 0; k < order.size(); ++k) order_out[k] = order[k];
+    *n_order = (int)order.size();
+    return CT_OK;
+}
+
+int ct_conv2d_tune_guided(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad, int dtype,
+                          int epilogue, int max_trials, int batch, unsigned long long seed, float min_repeat_ms,
+                          void* stream, ct_tile_config* best_out, ct_tune_record* records, int max_records,
+                          int* n_records) {
+    return ct::tune_guided_impl(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials, batch, seed,
+                                min_repeat_ms, stream, best_out, records, max_records, n_records);
+}
+
+}  // extern "C"
 
 extern "C" int ct_conv2d_tune(int N, int CI, int H, int W, int CO, int KH, int KW, int stride,
                               int pad, int dtype, int epilogue, int max_trials, float min_repeat_ms,

@@ -7,6 +7,7 @@ import json
 import os
 import re
 
+import numpy as np
 import pytest
 
 from oracle import oracle as O
@@ -350,3 +351,84 @@ def test_chain_channel_mode_unsupported_shapes():
         st = lib.ct_broadcast_chain(ctypes.byref(prog), None, None, None, None, None, out, dt, 4, 3, inner,
                                     ct.CT_BC_CHANNEL, None)
         assert st == ct.CT_ERR_UNSUPPORTED, (inner, out, dt, ct.ct_last_error())
+
+
+# ------------------------------------------------------------- guided search
+@pytest.mark.parametrize("lam", [0.0, 1e-3, 2.5])
+def test_ridge_fit_matches_the_oracle(lam):
+    r = np.random.default_rng(510)
+    X = np.column_stack([np.ones(40), r.normal(size=(40, 7))])
+    y = r.normal(size=40)
+    st, w = ct.ct_ridge_fit(X, y, lam)
+    assert st == ct.CT_OK
+    np.testing.assert_allclose(w, O.ridge_fit(X, y, lam), rtol=1e-9, atol=1e-12)
+
+
+def test_ridge_fit_errors():
+    X = np.ones((3, 2))  # rank 1: singular without shrinkage
+    assert ct.ct_ridge_fit(X, np.ones(3), 0.0)[0] == ct.CT_ERR_INVALID_ARG
+    assert ct.ct_ridge_fit(X, np.ones(3), 1e-3)[0] == ct.CT_OK
+    assert ct.ct_ridge_fit(X, np.ones(3), -1.0)[0] == ct.CT_ERR_INVALID_ARG
+
+
+def _landscape(n, d, seed):
+    """Features with an intercept and costs exactly exp(features . w_true)."""
+    r = np.random.default_rng(seed)
+    F = np.column_stack([np.ones(n), r.normal(size=(n, d - 1))])
+    w = r.normal(size=d)
+    return F, np.exp(F @ w)
+
+
+def test_guided_search_order_is_a_deterministic_prefix_without_repeats():
+    F, c = _landscape(300, 6, 520)
+    st, a = ct.ct_guided_search_table(F, c, 40, 8, 2, seed=7)
+    st2, b = ct.ct_guided_search_table(F, c, 40, 8, 2, seed=7)
+    st3, e = ct.ct_guided_search_table(F, c, 40, 8, 2, seed=8)
+    assert st == st2 == st3 == ct.CT_OK
+    assert a == b and len(a) == 40 and len(set(a)) == 40 and all(0 <= i < 300 for i in a)
+    assert a[:8] != e[:8]  # the first batch is the seed's draw
+
+
+def test_guided_search_times_everything_when_the_budget_allows():
+    F, c = _landscape(50, 4, 521)
+    st, order = ct.ct_guided_search_table(F, c, 1000, 8, 2)
+    assert st == ct.CT_OK and sorted(order) == list(range(50))
+
+
+def test_guided_search_finds_the_optimum_of_a_log_linear_landscape():
+    """Costs exactly log-linear in the features: once the first batch has
+    more points than features, the fit is exact and the next batch's model
+    picks are the true best untimed points, so the optimum is timed in the
+    second batch -- where uniform draws of the same budget would miss it."""
+    F, c = _landscape(2000, 6, 522)
+    st, order = ct.ct_guided_search_table(F, c, 16, 8, 2, seed=3)
+    assert st == ct.CT_OK
+    assert int(np.argmin(c)) in order[8:16]
+    best_found = min(c[i] for i in order)
+    assert best_found == c.min()
+
+
+def test_guided_search_skips_failed_trials_in_the_fit():
+    """Points whose trial fails (cost <= 0) are timed once and never refit; the
+    search still reaches the optimum among the rest."""
+    F, c = _landscape(500, 5, 523)
+    c = c.copy()
+    worst = np.argsort(c)[-100:]
+    c[worst] = -1.0
+    st, order = ct.ct_guided_search_table(F, c, 24, 8, 2, seed=4)
+    assert st == ct.CT_OK and len(set(order)) == 24
+    ok = c > 0
+    assert min(c[i] for i in order if ok[i]) == c[ok].min()
+
+
+def test_guided_search_errors():
+    F, c = _landscape(10, 3, 524)
+    for kw in [dict(max_trials=0, batch=4, n_explore=1), dict(max_trials=5, batch=0, n_explore=0),
+               dict(max_trials=5, batch=4, n_explore=5)]:
+        assert ct.ct_guided_search_table(F, c, kw["max_trials"], kw["batch"], kw["n_explore"])[0] == \
+            ct.CT_ERR_INVALID_ARG
+    best = ct.ct_tile_config()
+    # batch < 1 is refused before any HIP call
+    st = ct.library().ct_conv2d_tune_guided(1, 8, 8, 8, 8, 3, 3, 1, 1, 0, 0, 4, 0, 0, 1.0, None,
+                                            ctypes.byref(best), None, 0, None)
+    assert st == ct.CT_ERR_INVALID_ARG and "batch" in ct.ct_last_error()
