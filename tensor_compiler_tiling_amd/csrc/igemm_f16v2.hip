@@ -178,16 +178,33 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     float* e_bias = reinterpret_cast<float*>(hs + 2 * C::WB + 2 * XB);
     float* e_rs = e_bias + TM;
 
-    // workgroup -> (split, tile); when the column tiles come in multiples of
-    // 8, the row tiles of one column tile (readers of the same window) share
-    // blockIdx % 8, i.e. one XCD under round-robin placement
+    // workgroup -> (split, tile).  When the column tiles come in multiples
+    // of 8, workgroup b runs on XCD x = b % 8 (round-robin placement) and the
+    // XCDs split the tile grid into ga row groups x 8/ga column groups: XCD x
+    // takes one rectangle, row tiles fastest (the readers of one window run
+    // together).  Each filter row block is then read by 8/ga XCDs and each
+    // window by ga, and ga minimises the estimate of the bytes they fetch,
+    // (8/ga) * tiles_m*TM*K + ga * tiles_n*TN*CI: 1 for convolutions (small
+    // filters), 2 or 4 for large matrix products.
     const int tiles = p.tiles_m * p.tiles_n;
     const int split = blockIdx.x / tiles;
     const int b = blockIdx.x - split * tiles;
     int tm, tn;
     if ((p.tiles_n & 7) == 0) {
-        tm = (b >> 3) % p.tiles_m;
-        tn = (b / (8 * p.tiles_m)) * 8 + (b & 7);
+        const double wbytes = (double)p.tiles_m * TM * p.K, xbytes = (double)p.tiles_n * TN * p.CI;
+        int ga = 1;
+        double best = 8.0 * wbytes + xbytes;
+        for (int g = 2; g <= 8; g *= 2) {
+            const double cost = (8 / g) * wbytes + g * xbytes;
+            if (p.tiles_m % g == 0 && p.tiles_n % (8 / g) == 0 && cost < best) {
+                best = cost;
+                ga = g;
+            }
+        }
+        const int x = b & 7, l = b >> 3;
+        const int rm = p.tiles_m / ga, rn = p.tiles_n / (8 / ga);
+        tm = (x / (8 / ga)) * rm + l % rm;
+        tn = (x % (8 / ga)) * rn + l / rm;
     } else {
         tm = b % p.tiles_m;
         tn = b / p.tiles_m;
