@@ -69,6 +69,8 @@ struct DwParams {
     int rowvec;   // ... and W is a multiple of the elements of a load: one row each
     double rW;    // 1 / W and 1 / (H*W), for the divisions of the staging loop
     double rHW;
+    double rOW;   // 1 / OW and 1 / (RB/4 * OW), for the strip index of an item
+    double rPPI;
 };
 
 // q = n / d for 0 <= n < 2^31, d > 0, rd = 1/d rounded to double: the
@@ -201,15 +203,25 @@ __device__ __forceinline__ void dw_scatter(const DwParams& p, const DwTile& t, c
                         if (j + i < p.WPAD) dst[i] = Vec16<DT>::at(u[k], i);
                 }
             } else {
+                // the first element's (plane, row, column), then one step at a
+                // time with carries (a vector may cross rows and planes)
+                const int e = v * VE - t.m;
+                int pp = fdiv(e, HW, p.rHW);
+                const int rem = e - pp * HW;
+                int iy = fdiv(rem, p.W, p.rW);
+                int ix = rem - iy * p.W;
 #pragma unroll
                 for (int i = 0; i < VE; ++i) {
-                    const int e = v * VE - t.m + i;
-                    const int pp = fdiv(e, HW, p.rHW);
-                    const int rem = e - pp * HW;
-                    const int iy = fdiv(rem, p.W, p.rW);
-                    const int j = rem - iy * p.W + p.pad;
+                    const int j = ix + p.pad;
                     if (iy >= t.iy_lo && iy < t.iy_hi && j < p.WPAD)
                         lds[(pp * p.RIN + iy - t.iy0) * p.LDSW + j] = Vec16<DT>::at(u[k], i);
+                    if (++ix == p.W) {
+                        ix = 0;
+                        if (++iy == p.H) {
+                            iy = 0;
+                            ++pp;
+                        }
+                    }
                 }
             }
         }
@@ -231,10 +243,11 @@ __device__ __forceinline__ void dw_stage(const DwParams& p, const DwTile& t, DwP
     const int zr_bot = drows > 0 ? t.iy0 + p.RIN - t.iy_hi : 0;
     const int zrows = zr_top + zr_bot;
     const int nz = t.np * zrows * p.WPAD;
+    const double rWPAD = 1.0 / (double)p.WPAD, rZ = 1.0 / (double)max(zrows, 1);
     for (int e = tid; e < nz; e += kDwThreads) {
-        const int row = e / p.WPAD;
+        const int row = fdiv(e, p.WPAD, rWPAD);
         const int j = e - row * p.WPAD;
-        const int pp = row / zrows;
+        const int pp = fdiv(row, zrows, rZ);
         const int k = row - pp * zrows;
         const int r = k < zr_top ? k : p.RIN - zr_bot + (k - zr_top);
         lds[(pp * p.RIN + r) * p.LDSW + j] = 0.0f;
@@ -243,10 +256,11 @@ __device__ __forceinline__ void dw_stage(const DwParams& p, const DwTile& t, DwP
     const int right = max(p.WPAD - p.pad - p.W, 0);  // columns past the image
     const int pc = left + right;
     const int nc = t.np * drows * pc;
+    const double rPC = 1.0 / (double)max(pc, 1), rD = 1.0 / (double)max(drows, 1);
     for (int e = tid; e < nc; e += kDwThreads) {
-        const int row = e / pc;
+        const int row = fdiv(e, pc, rPC);
         const int k = e - row * pc;
-        const int pp = row / drows;
+        const int pp = fdiv(row, drows, rD);
         const int r = zr_top + (row - pp * drows);
         const int j = k < left ? k : p.pad + p.W + (k - left);
         lds[(pp * p.RIN + r) * p.LDSW + j] = 0.0f;
@@ -318,9 +332,9 @@ __global__ __launch_bounds__(kDwThreads) void conv_depthwise_kernel(DwParams p) 
     const int per_plane_items = strips * p.OW;
     const float* tap = lds + p.TAPS;
     for (int item = tid; item < t.np * per_plane_items; item += kDwThreads) {
-        const int pp = item / per_plane_items;
+        const int pp = fdiv(item, per_plane_items, p.rPPI);
         const int rem = item - pp * per_plane_items;
-        const int g = rem / p.OW;
+        const int g = fdiv(rem, p.OW, p.rOW);
         const int ox = rem - g * p.OW;
         const float* win = lds + (pp * p.RIN + 4 * g * S) * p.LDSW + ox * S;
         const float* tp = tap + pp * TT;
@@ -471,6 +485,8 @@ hipError_t launch_depthwise(const void* x, const void* w, float* y, int N, int C
     p.rowvec = p.vec && W % (dtype == DT_F32 ? 4 : 8) == 0;
     p.rW = 1.0 / (double)W;
     p.rHW = 1.0 / (double)((long long)H * W);
+    p.rOW = 1.0 / (double)p.OW;
+    p.rPPI = 1.0 / (double)((long long)(p.RB / 4) * p.OW);
     switch (dtype) {
         case DT_F32: return launch_dt<DT_F32>(p, bytes, stream);
         case DT_F16: return launch_dt<DT_F16>(p, bytes, stream);
