@@ -43,7 +43,7 @@ namespace {
 constexpr int kDwThreads = 256;
 constexpr int kDwMaxTaps = 256;         // KH*KW
 constexpr int kDwMaxLds = 160 * 1024;   // bytes of LDS per workgroup on gfx950
-constexpr int kDwPrefLds = 64 * 1024;   // plans above this only when nothing smaller fits
+constexpr int kDwPrefLds = 32 * 1024;   // plans above this only when nothing smaller fits (5 workgroups a CU)
 constexpr int kDwTargetItems = 2048;    // 4-row strips a workgroup aims at
 
 struct DwParams {
@@ -407,10 +407,11 @@ int plan_within(int NC, int OH, int OW, int KH, int KW, int stride, int budget, 
 }  // namespace
 
 // Work split of a depthwise launch: RB rows (a multiple of 4) of PPW planes a
-// workgroup, about kDwTargetItems 4-row strips, within 64 KB of LDS (several
-// workgroups a CU) or, when four output rows of one plane need more, within
-// the 160 KB a workgroup may hold.  Returns the LDS bytes, or -1 if four
-// output rows of one plane do not fit even there.
+// workgroup, about kDwTargetItems 4-row strips, within 32 KB of LDS (five
+// workgroups a CU, as many as the registers allow) or, when four output rows
+// of one plane need more, within the 160 KB a workgroup may hold.  Returns
+// the LDS bytes, or -1 if four output rows of one plane do not fit even
+// there.
 int depthwise_plan(int NC, int OH, int OW, int KH, int KW, int stride, int* RB, int* RIN, int* WPAD,
                    int* LDSW, int* PPW, int* TAPS) {
     const int b = plan_within(NC, OH, OW, KH, KW, stride, kDwPrefLds, RB, RIN, WPAD, LDSW, PPW, TAPS);
