@@ -22,14 +22,16 @@
 //     eight a lane in flight at once, plus a scalar head and tail; the zero
 //     border goes to LDS words no load writes, so the two need no barrier
 //     between them;
-//   - the planes' taps follow the window in LDS;
+//   - the planes' taps and epilogue values follow the windows in LDS, loaded
+//     together with the window (no load waits on another);
 //   - each lane computes one output column over 4 consecutive rows, so the
 //     lanes of a wave read consecutive LDS words (no bank conflicts at
 //     stride 1) and, for the filter sizes compiled in, input rows shared by
 //     the 4 outputs are read once;
-//   - a workgroup takes about 2048 strips (8192 outputs), so each has 16 to
-//     32 KB of loads in flight at once; consecutive workgroups of one XCD
-//     take neighbouring row blocks, whose halo rows then meet in one L2.
+//   - a workgroup takes up to about 2048 strips (8192 outputs) within 32 KB
+//     of LDS, so that five fit a CU with all of their loads in flight;
+//     consecutive workgroups of one XCD take neighbouring row blocks, whose
+//     halo rows then meet in one L2.
 #include "ct_device.hpp"
 
 #include <hip/hip_runtime.h>
