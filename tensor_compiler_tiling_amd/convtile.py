@@ -386,11 +386,24 @@ def variant_id(name: str) -> int:
     raise KeyError(name)
 
 
+def _on_gpu(**tensors) -> None:
+    """The C ABI takes raw device pointers: every tensor handed to it must live
+    on a GPU and be contiguous (None is skipped)."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
 def conv2d(x, w, stride: int = 1, pad: int = 0, epilogue: int = CT_EPI_NONE, bias=None, var=None,
            eps: float = 1e-5, config: Optional[ct_tile_config] = None, out=None, stream=None,
            direct: bool = False):
     """y = conv2d_nchw(x, w) (+ epilogue), fp32 output allocated with torch."""
     import torch
+    _on_gpu(x=x, w=w, bias=bias, var=var, out=out)
     N, CI, H, W = x.shape
     CO, CI2, KH, KW = w.shape
     if CI2 != CI or w.dtype != x.dtype:
@@ -417,6 +430,7 @@ def gemm(A, B, epilogue: int = CT_EPI_NONE, bias=None, var=None, eps: float = 1e
     """C = A @ B (+ per-row epilogue), fp32 output allocated with torch: A [M, K], B [K, N],
     same dtype, contiguous."""
     import torch
+    _on_gpu(A=A, B=B, bias=bias, var=var, out=out)
     M, K = A.shape
     K2, N = B.shape
     if K2 != K or A.dtype != B.dtype:
@@ -431,6 +445,7 @@ def conv2d_depthwise(x, w, stride: int = 1, pad: int = 0, epilogue: int = CT_EPI
     """Depthwise y[n][c] = conv2d(x[n][c], w[c][0]) (+ epilogue), fp32 output allocated with
     torch: x [N, C, H, W], w [C, 1, KH, KW], same dtype, contiguous."""
     import torch
+    _on_gpu(x=x, w=w, bias=bias, var=var, out=out)
     N, C, H, W = x.shape
     C2, one, KH, KW = w.shape
     if C2 != C or one != 1 or w.dtype != x.dtype:
@@ -448,6 +463,7 @@ def broadcast(var, N: int, H: int, W: int, out_dtype=None, mode: int = CT_BC_AUT
               stream=None):
     """[1,C,1,1] -> [N,C,H,W] of exp(var[c])."""
     import torch
+    _on_gpu(var=var, out=out)
     out_dtype = out_dtype or torch.float16
     C = var.numel()
     o = out if out is not None else torch.empty((N, C, H, W), dtype=out_dtype, device=var.device)
@@ -489,7 +505,10 @@ def broadcast_chain(prog: ct_bcast_program, outer: int, P: int, inner: int, arra
     floats; x: the producer's fp32 tensor of the output's size, or None."""
     import torch
     arrays = list(arrays) + [None] * (4 - len(arrays))
+    _on_gpu(a0=arrays[0], a1=arrays[1], a2=arrays[2], a3=arrays[3], x=x, out=out)
     dev = next((t.device for t in arrays + [x, out] if t is not None), None)
+    if dev is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
     if out is None:
         out = torch.empty((outer, P, inner), dtype=out_dtype or torch.float32, device=dev)
     st = ct_broadcast_chain(prog, arrays[0], arrays[1], arrays[2], arrays[3], x, out,

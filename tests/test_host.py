@@ -432,3 +432,20 @@ def test_guided_search_errors():
     st = ct.library().ct_conv2d_tune_guided(1, 8, 8, 8, 8, 3, 3, 1, 1, 0, 0, 4, 0, 0, 1.0, None,
                                             ctypes.byref(best), None, 0, None)
     assert st == ct.CT_ERR_INVALID_ARG and "batch" in ct.ct_last_error()
+
+
+def test_tensor_helpers_reject_host_and_strided_tensors():
+    """The helpers hand raw pointers to the C ABI: a CPU tensor (or a
+    non-contiguous view) is refused before any call."""
+    import torch
+    x = torch.ones(1, 2, 6, 6)
+    with pytest.raises(ValueError, match="GPU"):
+        ct.conv2d(x, torch.ones(3, 2, 3, 3))
+    with pytest.raises(ValueError, match="GPU"):
+        ct.conv2d_depthwise(x, torch.ones(2, 1, 3, 3))
+    with pytest.raises(ValueError, match="GPU"):
+        ct.gemm(torch.ones(4, 5), torch.ones(5, 6))
+    with pytest.raises(ValueError, match="GPU"):
+        ct.broadcast(torch.ones(4), 2, 3, 3)
+    with pytest.raises(ValueError, match="GPU"):
+        ct.broadcast_chain(ct.make_program([("set", 1.0)]), 2, 3, 4, arrays=[torch.ones(3)])
