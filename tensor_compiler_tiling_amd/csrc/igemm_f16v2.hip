@@ -153,6 +153,10 @@ template <> struct BufLoad<1> {
 };
 
 // Divisors: fd_kw = KW.
+// Column tiles of the grid: tiles_n rounded up to a multiple of 8, so that
+// every XCD (workgroup b runs on XCD b % 8) takes a block of whole columns.
+__host__ __device__ inline int h2_col_tiles(int tiles_n) { return (tiles_n + 7) & ~7; }
+
 template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
 __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     fetch_kernargs(p);
@@ -185,8 +189,12 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     // together).  Each filter row block is then read by 8/ga XCDs and each
     // window by ga, and ga minimises the estimate of the bytes they fetch,
     // (8/ga) * tiles_m*TM*K + ga * tiles_n*TN*CI: 1 for convolutions (small
-    // filters), 2 or 4 for large matrix products.
-    const int tiles = p.tiles_m * p.tiles_n;
+    // filters), 2 or 4 for large matrix products.  Otherwise the grid holds
+    // column tiles rounded up to a multiple of 8 (h2_col_tiles) and each XCD
+    // takes a block of whole columns (ga = 1); workgroups past the last
+    // column exit at once.
+    const int cols = h2_col_tiles(p.tiles_n);
+    const int tiles = p.tiles_m * cols;
     const int split = blockIdx.x / tiles;
     const int b = blockIdx.x - split * tiles;
     int tm, tn;
@@ -206,8 +214,10 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
         tm = (x / (8 / ga)) * rm + l % rm;
         tn = (x % (8 / ga)) * rn + l / rm;
     } else {
-        tm = b % p.tiles_m;
-        tn = b / p.tiles_m;
+        const int x = b & 7, l = b >> 3;
+        tm = l % p.tiles_m;
+        tn = x * (cols >> 3) + l / p.tiles_m;
+        if (tn >= p.tiles_n) return;  // padding of the grid: uniform over the workgroup
     }
     const int tile = tm + tn * p.tiles_m;
     const int co0 = tm * TM;
@@ -620,7 +630,7 @@ hipError_t h2_launch_px(const ConvParams& q, int bytes, hipStream_t stream) {
         }
         lds_limit.store(bytes, std::memory_order_relaxed);
     }
-    const long long grid = (long long)q.tiles_m * q.tiles_n * q.S;
+    const long long grid = (long long)q.tiles_m * h2_col_tiles(q.tiles_n) * q.S;
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(C::NT), bytes, stream, q);
     return hipGetLastError();
