@@ -47,13 +47,6 @@ constexpr int kSpaceVersion = 1;
 // ---------------------------------------------------------------- errors --
 thread_local char g_last_error[512] = "";
 
-void set_error(const char* fmt, ...) {
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
-    va_end(ap);
-}
-
 int fail(int status, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
