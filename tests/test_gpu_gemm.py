@@ -1,8 +1,8 @@
 """GPU parity of the matrix-product entry point (the 1x1-convolution view)
 against the fp64 oracle, through the C ABI.
 
-Gates as for the convolution: max |gpu - ref| <= 1e-4 * S for fp32 operands
-and 1e-2 * S for fp16 / bf16, S = max over outputs of sum_k |A[m][k] B[k][n]|
+Gates as for the convolution: max |gpu - ref| <= 1e-4 * S for every operand
+dtype (half-precision products are exact in fp32), S = max over outputs of sum_k |A[m][k] B[k][n]|
 (the oracle's absacc); the exp-bias-rsqrt epilogue is gated relatively;
 bit-exact output for small-integer operands.
 """
