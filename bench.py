@@ -1,11 +1,15 @@
 #!/usr/bin/env python3
 """Throughput of the convolution hot path on one MI355X.
 
-A step is one forward convolution through the C ABI (host dispatch ->
-implicit-GEMM kernel: padded-window gather, LDS staging, fp32 MFMA, split
-reduction, epilogue, store) on the 1x512x7x7 -> 512, 3x3, stride 1, pad 1
-fp32 layer (the final ResNet layer of the TVM tutorial's tuning example),
-with seeded synthetic inputs already resident in HBM.
+A step is one forward convolution through the C ABI (implicit-GEMM kernel:
+padded-window gather, LDS staging, fp32 MFMA, split reduction, epilogue,
+store) on the 1x512x7x7 -> 512, 3x3, stride 1, pad 1 fp32 layer (the final
+ResNet layer of the TVM tutorial's tuning example), with seeded synthetic
+inputs already resident in HBM.  In the default mode the K steps are
+dispatched once, into a HIP graph, and the timed region is the graph's
+replay: the device time of K back-to-back launches, host dispatch excluded.
+`eager_ms_per_step` times the same K steps dispatched one by one from the
+host through the C ABI (host dispatch included).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
                     [--tune] [--cache PATH | --no-cache] [--no-cpu-baseline]

@@ -34,13 +34,22 @@
  *     last failure on the calling thread.
  *   - Argument errors are reported with CT_ERR_INVALID_ARG before any HIP call.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Launch calls are
- *     asynchronous on that stream and never synchronise.
+ *     asynchronous on that stream.  Once a device is set up (ct_init, or the
+ *     first launch on it) and a stream's workspace has grown to what a shape
+ *     needs (the first split-reduction launch of that size on the stream),
+ *     a launch neither synchronises nor allocates, so it may be captured into
+ *     a HIP graph.  A launch that would need either step while its stream is
+ *     capturing returns CT_ERR_UNSUPPORTED and captures nothing.
  *   - The library owns: the compiled kernels, a process-wide tile-config cache
- *     (mutex-protected), and per-(device, stream) split-reduction workspaces
- *     (grow-only; allocated with hipMalloc on first need, never freed before
- *     ct_release()).  Two launches that use split reduction on the same stream
+ *     (mutex-protected), a launch plan per (device, shape) derived from it,
+ *     and per-(device, stream) split-reduction workspaces.  A workspace grows
+ *     by allocating a larger buffer; the buffer it replaces stays allocated
+ *     until ct_release(), because a graph captured earlier on that stream may
+ *     still use it.  Two launches that use split reduction on the same stream
  *     are ordered by the stream; launches on different streams get different
- *     workspaces.
+ *     workspaces.  A captured launch keeps the workspace of the stream it was
+ *     captured on: replays of such graphs must not overlap one another or
+ *     other launches on that stream.
  */
 #ifndef CONVTILE_H
 #define CONVTILE_H
@@ -118,6 +127,8 @@ typedef struct ct_tune_record {
  * used only by CT_EPI_EXP_BIAS_RSQRT.  Errors: CT_ERR_INVALID_ARG for any
  * dimension <= 0, stride <= 0, pad < 0, OH or OW <= 0, NULL x/w/y, unknown
  * dtype/epilogue, or bias/var missing when the epilogue reads them;
+ * CT_ERR_UNSUPPORTED when the device is not set up or the stream's workspace
+ * must grow while the stream is capturing (see Conventions);
  * CT_ERR_NO_MEMORY if the split workspace cannot grow; CT_ERR_HIP on a launch
  * failure. */
 int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y,
@@ -327,7 +338,11 @@ int ct_guided_search_table(const double* feats, const double* costs, int n, int 
                            int* order_out, int* n_order);
 
 /* The config ct_conv2d_nchw_fwd would use for this shape; *from_cache = 1
- * when it came from a tuning record, 0 when it is the built-in default. */
+ * when it came from a tuning record, 0 when it is the built-in default.  The
+ * TVM tutorial's closing step looks the tuned config of a workload up in its
+ * log this way (apply_history_best, then query of the best record) before it
+ * builds the kernel.  Errors: those of ct_conv2d_space_size, CT_ERR_INVALID_ARG
+ * for a NULL cfg_out. */
 int ct_conv2d_query(int N, int CI, int H, int W, int CO, int KH, int KW,
                     int stride, int pad, int dtype, int epilogue,
                     ct_tile_config* cfg_out, int* from_cache);
@@ -354,16 +369,38 @@ int ct_broadcast_nchw(const float* var, void* out, int N, int C, int H, int W,
 
 /* ---- cache, lifetime, errors ----------------------------------------- */
 
-/* Append-only JSON-lines cache of tuning winners (one record per line).
- * load merges the file into memory (lines that do not parse are skipped);
- * save appends every in-memory record to the file.  CT_ERR_IO on failure. */
+/* Append-only JSON-lines tuning log: the TVM tutorial's Step 2 writes every
+ * measure record to a log file (log_to_file), and its closing step picks the
+ * best record per workload from that log (apply_history_best).  Here a record
+ * is one line with the shape key, the config, its costs, error_no and a
+ * timestamp.  load merges the file into memory, keeping per shape the fastest
+ * successful record (lines that do not parse, name an unknown variant or are
+ * not legal for their shape are skipped); save appends every in-memory
+ * winner to the file.  CT_ERR_INVALID_ARG for a NULL path, CT_ERR_IO when the
+ * file cannot be opened or written.  clear empties the in-memory cache; size
+ * is its number of shapes. */
 int ct_cache_load(const char* path);
 int ct_cache_save(const char* path);
 int ct_cache_clear(void);
 int ct_cache_size(void);
 
-/* Free the library's device workspaces (all devices, all streams). */
+/* Free the library's device workspaces, and every buffer a workspace
+ * outgrew (all devices, all streams).  Synchronises each stream that owns a
+ * workspace first.  No graph that captured a launch may be replayed after
+ * this. */
 int ct_release(void);
+
+/* Set up `device` for launches: the zero page's device address and the
+ * workgroup-placement probe of the XCD-local variants (which launches and
+ * synchronises a private stream).  Idempotent.  Call it before capturing
+ * the first launch on a device into a HIP graph.  CT_ERR_INVALID_ARG for a
+ * device that does not exist, CT_ERR_HIP when a HIP call fails. */
+int ct_init(int device);
+
+/* How many times ct_conv2d_nchw_fwd resolved a launch plan (a first call for
+ * a (device, shape), or the first after the config cache changed); every
+ * other call reused a plan.  For tests and diagnostics. */
+long long ct_plan_misses(void);
 
 const char* ct_status_string(int status);
 const char* ct_last_error(void);

@@ -113,6 +113,8 @@ _SIGS = {
     "ct_cache_clear": (_I, []),
     "ct_cache_size": (_I, []),
     "ct_release": (_I, []),
+    "ct_init": (_I, [_I]),
+    "ct_plan_misses": (_LL, []),
     "ct_status_string": (ctypes.c_char_p, [_I]),
     "ct_last_error": (ctypes.c_char_p, []),
     "ct_version": (ctypes.c_char_p, []),
@@ -358,6 +360,14 @@ def ct_status_string(st: int) -> str:
 
 def ct_last_error() -> str:
     return _load().ct_last_error().decode(errors="replace")
+
+
+def ct_init(device: int = 0) -> int:
+    return _load().ct_init(device)
+
+
+def ct_plan_misses() -> int:
+    return _load().ct_plan_misses()
 
 
 def ct_version() -> str:

@@ -109,6 +109,9 @@ hipError_t launch_xcc_probe(int* out, int blocks, hipStream_t stream);
 hipError_t launch_fill_uniform(void* dst, long long n, int dtype, float lo, float hi,
                                unsigned seed, hipStream_t stream);
 
+// dst[0..n) = v, as a kernel on `stream`.
+hipError_t launch_fill_u32(unsigned* dst, long long n, unsigned v, hipStream_t stream);
+
 // max over i of |a[i] - b[i]| / (atol + rtol * |b[i]|) > 1 ?  writes a flag.
 hipError_t launch_compare(const float* a, const float* b, long long n, float atol,
                           float rtol, unsigned* bad_count, hipStream_t stream);

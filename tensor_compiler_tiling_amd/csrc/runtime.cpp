@@ -28,6 +28,7 @@
 #include <sstream>
 #include <string>
 #include <tuple>
+#include <unordered_map>
 #include <vector>
 
 #include "../../include/convtile.h"
@@ -324,42 +325,104 @@ struct Resolved {
     long long grid, ws_bytes, aux_bytes;
 };
 
-// Whether workgroup b of a launch runs on XCD b % 8 on the current device:
-// observed once per device with a probe launch of 4096 workgroups (false if
-// the probe fails).  On a host with no device nothing can launch, and the
-// tuning log's XCD-local records are taken as they were measured; any
-// launch happens on a device, where the probe decides.
+// ------------------------------------------------------- device set-up --
+// Once per device: the address of the zero page (a device global, so no
+// allocation) and the workgroup-placement probe that gates the XCD-local
+// variants.  The probe launches and synchronises on a private stream, so it
+// cannot run inside stream capture: ct_init(device) does it up front, and a
+// first launch on a device that finds its stream capturing is refused.
+
+// 256 zero bytes: the source address of every padded tap in the direct-to-LDS
+// loads (never written).
+static __device__ __align__(256) float g_zero_page[64];
+// The probe's output: the XCD of each of its workgroups.
+constexpr int kProbeBlocks = 4096;
+static __device__ int g_probe_out[kProbeBlocks];
+
+struct DeviceState {
+    bool ready = false;
+    bool xcd_rr = false;          // workgroup b runs on XCD b % 8
+    const void* zero = nullptr;   // device address of g_zero_page
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+DeviceState g_dev[kMaxDevices];
+std::atomic<bool> g_dev_ready[kMaxDevices];
+
+// Set up device `dev` (current).  Not under capture: the caller checks.
+int device_setup_locked(int dev) {
+    DeviceState& d = g_dev[dev];
+    if (d.ready) return CT_OK;
+    void* z = nullptr;
+    hipError_t e = hipGetSymbolAddress(&z, HIP_SYMBOL(g_zero_page));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(zero page)");
+    int* probe = nullptr;
+    e = hipGetSymbolAddress((void**)&probe, HIP_SYMBOL(g_probe_out));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(probe buffer)");
+    hipStream_t ps = nullptr;
+    e = hipStreamCreateWithFlags(&ps, hipStreamNonBlocking);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+    std::vector<int> h(kProbeBlocks, -1);
+    bool rr = false;
+    if (launch_xcc_probe(probe, kProbeBlocks, ps) == hipSuccess &&
+        hipMemcpyAsync(h.data(), probe, kProbeBlocks * sizeof(int), hipMemcpyDeviceToHost, ps) == hipSuccess &&
+        hipStreamSynchronize(ps) == hipSuccess) {
+        rr = true;
+        for (int b = 0; b < kProbeBlocks; ++b) rr = rr && h[b] == b % 8;
+    }
+    (void)hipStreamDestroy(ps);
+    (void)hipGetLastError();
+    d.zero = z;
+    d.xcd_rr = rr;
+    d.ready = true;
+    g_dev_ready[dev].store(true, std::memory_order_release);
+    return CT_OK;
+}
+
+// Set up the current device if that has not happened yet.  `stream` is the
+// stream of the launch that needs it: if it is capturing, set-up cannot run
+// and the launch is refused.
+int ensure_device(hipStream_t stream, int* dev_out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(CT_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    *dev_out = dev;
+    if (g_dev_ready[dev].load(std::memory_order_acquire)) return CT_OK;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(CT_ERR_UNSUPPORTED,
+                    "first launch on device %d during stream capture: call ct_init(%d) (or launch once "
+                    "eagerly) before capturing",
+                    dev, dev);
+    std::lock_guard<std::mutex> lk(g_dev_mu);
+    return device_setup_locked(dev);
+}
+
+// Whether workgroup b of a launch runs on XCD b % 8 on the current device
+// (false if the probe failed).  On a host with no device nothing can launch,
+// and the tuning log's XCD-local records are taken as they were measured;
+// any launch happens on a device, where the probe decides.
 bool xcd_round_robin() {
-    static std::mutex mu;
-    static std::map<int, bool> seen;
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev == 0) {
         (void)hipGetLastError();
         return true;
     }
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
         (void)hipGetLastError();
         return false;
     }
-    std::lock_guard<std::mutex> lk(mu);
-    auto it = seen.find(dev);
-    if (it != seen.end()) return it->second;
-    constexpr int kBlocks = 4096;
-    bool ok = false;
-    int* d = nullptr;
-    if (hipMalloc((void**)&d, kBlocks * sizeof(int)) == hipSuccess) {
-        std::vector<int> h(kBlocks, -1);
-        if (launch_xcc_probe(d, kBlocks, nullptr) == hipSuccess && hipDeviceSynchronize() == hipSuccess &&
-            hipMemcpy(h.data(), d, kBlocks * sizeof(int), hipMemcpyDeviceToHost) == hipSuccess) {
-            ok = true;
-            for (int b = 0; b < kBlocks; ++b) ok = ok && h[b] == b % 8;
-        }
-        (void)hipFree(d);
+    if (!g_dev_ready[dev].load(std::memory_order_acquire)) {
+        // host-side calls (space, query, tune) set the device up on demand
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        if (device_setup_locked(dev) != CT_OK) return false;
     }
-    (void)hipGetLastError();
-    seen[dev] = ok;
-    return ok;
+    return g_dev[dev].xcd_rr;
 }
 
 // Legality of a tile config for a shape; launches nothing except, once per
@@ -452,6 +515,8 @@ struct CacheEntry {
 std::mutex g_cache_mu;
 std::map<std::string, CacheEntry> g_cache;
 std::map<std::string, ct_tile_config> g_default_memo;
+// bumped by every change to g_cache (the launch plans built on it go stale)
+std::atomic<unsigned> g_cache_gen{1};
 
 std::string json_record(const Shape& s, const ct_tile_config& c, const char* vname,
                         const float* costs, int ncost, double all_cost, double ts) {
@@ -563,6 +628,7 @@ bool cache_insert_line(const std::string& line) {
     auto it = g_cache.find(key);
     if (it != g_cache.end() && it->second.cfg.us > 0 && it->second.cfg.us <= c.us) return true;
     g_cache[key] = CacheEntry{kv["variant"], c, line};
+    g_cache_gen.fetch_add(1, std::memory_order_acq_rel);
     return true;
 }
 
@@ -578,87 +644,62 @@ struct Workspace {
 
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+// Buffers a workspace outgrew.  They stay allocated until ct_release(): a
+// graph captured earlier on that stream, or a launch still in flight, may use
+// them.
+std::vector<std::pair<int, void*>> g_retired;
 
-int get_workspace(hipStream_t stream, long long ws_bytes, long long n_tickets, long long aux_bytes,
+int get_workspace(int dev, hipStream_t stream, long long ws_bytes, long long n_tickets, long long aux_bytes,
                   Workspace* out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lk(g_ws_mu);
     Workspace& w = g_ws[{dev, stream}];
     if (w.ws_bytes < ws_bytes || w.n_tickets < n_tickets || w.aux_bytes < aux_bytes) {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-        e = hipStreamIsCapturing(stream, &cs);
+        hipError_t e = hipStreamIsCapturing(stream, &cs);
         if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
         if (cs != hipStreamCaptureStatusNone)
             return fail(CT_ERR_UNSUPPORTED,
                         "the workspace of this stream must grow, which cannot happen during "
                         "stream capture: run the same convolution once on the stream first");
-        // in-flight launches on this stream may still use the old buffers
-        e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     }
+    hipError_t e;
     if (w.ws_bytes < ws_bytes) {
-        if (w.ws) (void)hipFree(w.ws);
-        w.ws = nullptr;
-        w.ws_bytes = 0;
         const long long b = std::max<long long>(ws_bytes, 1 << 20);
-        e = hipMalloc((void**)&w.ws, (size_t)b);
+        float* nw = nullptr;
+        e = hipMalloc((void**)&nw, (size_t)b);
         if (e != hipSuccess) return fail(CT_ERR_NO_MEMORY, "split workspace of %lld bytes: %s", b,
                                          hipGetErrorString(e));
+        if (w.ws) g_retired.push_back({dev, w.ws});
+        w.ws = nw;
         w.ws_bytes = b;
     }
     if (w.n_tickets < n_tickets) {
-        if (w.tickets) (void)hipFree(w.tickets);
-        w.tickets = nullptr;
-        w.n_tickets = 0;
         const long long n = std::max<long long>(n_tickets, 4096);
-        e = hipMalloc((void**)&w.tickets, (size_t)n * sizeof(unsigned));
+        unsigned* nt = nullptr;
+        e = hipMalloc((void**)&nt, (size_t)n * sizeof(unsigned));
         if (e != hipSuccess) return fail(CT_ERR_NO_MEMORY, "ticket array: %s", hipGetErrorString(e));
-        // zero once; every launch leaves the counters it used at zero again
-        e = hipMemset(w.tickets, 0, (size_t)n * sizeof(unsigned));
-        if (e != hipSuccess) return hip_fail(e, "hipMemset");
-        e = hipDeviceSynchronize();
-        if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+        // zeroed once, in stream order before the launch that needs them;
+        // every launch leaves the counters it used at zero again
+        e = launch_fill_u32(nt, n, 0u, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(nt);
+            return hip_fail(e, "ticket fill");
+        }
+        if (w.tickets) g_retired.push_back({dev, w.tickets});
+        w.tickets = nt;
         w.n_tickets = n;
     }
     if (w.aux_bytes < aux_bytes) {
-        if (w.aux) (void)hipFree(w.aux);
-        w.aux = nullptr;
-        w.aux_bytes = 0;
         const long long b = std::max<long long>(aux_bytes, 1 << 20);
-        e = hipMalloc(&w.aux, (size_t)b);
+        void* na = nullptr;
+        e = hipMalloc(&na, (size_t)b);
         if (e != hipSuccess) return fail(CT_ERR_NO_MEMORY, "filter scratch of %lld bytes: %s", b,
                                          hipGetErrorString(e));
+        if (w.aux) g_retired.push_back({dev, w.aux});
+        w.aux = na;
         w.aux_bytes = b;
     }
     *out = w;
-    return CT_OK;
-}
-
-// One zeroed 256-byte block per device: the source address of every padded
-// tap in the direct-to-LDS loads.
-std::mutex g_zero_mu;
-std::map<int, void*> g_zero;
-
-int zero_page(const void** out) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-    std::lock_guard<std::mutex> lk(g_zero_mu);
-    auto it = g_zero.find(dev);
-    if (it != g_zero.end()) {
-        *out = it->second;
-        return CT_OK;
-    }
-    void* z = nullptr;
-    e = hipMalloc(&z, 256);
-    if (e != hipSuccess) return fail(CT_ERR_NO_MEMORY, "zero page: %s", hipGetErrorString(e));
-    e = hipMemset(z, 0, 256);
-    if (e == hipSuccess) e = hipDeviceSynchronize();
-    if (e != hipSuccess) return hip_fail(e, "zero page");
-    g_zero[dev] = z;
-    *out = z;
     return CT_OK;
 }
 
@@ -684,12 +725,19 @@ int launch_direct(const Shape& s, const void* x, const void* w, float* y, const 
     return CT_OK;
 }
 
-int launch_tiled(const Shape& s, const ct_tile_config& c, const void* x, const void* w, float* y,
-                 const float* bias, const float* var, float eps, hipStream_t stream) {
-    Resolved r;
-    std::string why;
-    if (!legal(s, c, &r, &why))
-        return fail(CT_ERR_UNSUPPORTED, "tile config not legal for this shape: %s", why.c_str());
+// Scratch of one launch: the split partials, their arrival counters and a
+// variant's own buffer (the reordered filter).
+struct LaunchScratch {
+    float* ws = nullptr;
+    unsigned* tickets = nullptr;
+    void* aux = nullptr;
+};
+
+// Launch config c, already resolved (r) and checked legal for s, on device
+// dev (set up) with the given scratch.
+int launch_resolved(int dev, const Shape& s, const ct_tile_config& c, const Resolved& r, const LaunchScratch& sc,
+                    const void* x, const void* w, float* y, const float* bias, const float* var, float eps,
+                    hipStream_t stream) {
     ConvParams p = base_params(s, x, w, y, bias, var, eps);
     p.kc = c.kc;
     p.stages = c.stages;
@@ -697,22 +745,47 @@ int launch_tiled(const Shape& s, const ct_tile_config& c, const void* x, const v
     p.tiles_m = r.tiles_m;
     p.tiles_n = r.tiles_n;
     p.R = r.R;
-    int zst = zero_page(&p.zero);
-    if (zst != CT_OK) return zst;
-    if (c.split_k > 1 || r.aux_bytes > 0) {
-        Workspace ws;
-        const long long nt = c.split_k > 1 ? (long long)r.tiles_m * r.tiles_n * kTicketStride : 0;
-        int st = get_workspace(stream, r.ws_bytes, nt, r.aux_bytes, &ws);
-        if (st != CT_OK) return st;
-        if (c.split_k > 1) {
-            p.ws = ws.ws;
-            p.tickets = ws.tickets;
-        }
-        p.aux = ws.aux;
+    p.zero = g_dev[dev].zero;
+    if (c.split_k > 1) {
+        p.ws = sc.ws;
+        p.tickets = sc.tickets;
     }
+    p.aux = sc.aux;
     hipError_t e = r.v->ig->launch(p, stream);
     if (e != hipSuccess) return hip_fail(e, r.v->desc.name);
     return CT_OK;
+}
+
+long long tickets_needed(const ct_tile_config& c, const Resolved& r) {
+    return c.split_k > 1 ? (long long)r.tiles_m * r.tiles_n * kTicketStride : 0;
+}
+
+// The stream's workspace (grown if needed) as a launch's scratch.
+int stream_scratch(int dev, const ct_tile_config& c, const Resolved& r, hipStream_t stream, LaunchScratch* out) {
+    *out = LaunchScratch{};
+    if (c.split_k <= 1 && r.aux_bytes <= 0) return CT_OK;
+    Workspace ws;
+    const int st = get_workspace(dev, stream, r.ws_bytes, tickets_needed(c, r), r.aux_bytes, &ws);
+    if (st != CT_OK) return st;
+    out->ws = ws.ws;
+    out->tickets = ws.tickets;
+    out->aux = ws.aux;
+    return CT_OK;
+}
+
+int launch_tiled(const Shape& s, const ct_tile_config& c, const void* x, const void* w, float* y,
+                 const float* bias, const float* var, float eps, hipStream_t stream) {
+    int dev = 0;
+    int st = ensure_device(stream, &dev);
+    if (st != CT_OK) return st;
+    Resolved r;
+    std::string why;
+    if (!legal(s, c, &r, &why))
+        return fail(CT_ERR_UNSUPPORTED, "tile config not legal for this shape: %s", why.c_str());
+    LaunchScratch sc;
+    st = stream_scratch(dev, c, r, stream, &sc);
+    if (st != CT_OK) return st;
+    return launch_resolved(dev, s, c, r, sc, x, w, y, bias, var, eps, stream);
 }
 
 // Built-in default: the legal point with the smallest predicted time.
@@ -774,6 +847,69 @@ ct_tile_config choose(const Shape& s, int* from_cache) {
     return c;
 }
 
+// ------------------------------------------------------------ launch plans --
+// The resolved launch of fwd per (device, shape): the config it uses, with
+// the legality check's resolution (grid, window rows, LDS and scratch
+// sizes), so that a repeated fwd skips the string key, the cache lookup and
+// the legality check.  Any change to the config cache bumps g_cache_gen,
+// which retires every plan.
+
+struct PlanKey {
+    int v[12];
+    bool operator==(const PlanKey& o) const { return memcmp(v, o.v, sizeof v) == 0; }
+};
+
+struct PlanKeyHash {
+    size_t operator()(const PlanKey& k) const {
+        uint64_t h = 1469598103934665603ULL;  // FNV-1a over the words
+        for (int x : k.v) {
+            h ^= (uint32_t)x;
+            h *= 1099511628211ULL;
+        }
+        return (size_t)h;
+    }
+};
+
+struct Plan {
+    unsigned gen = 0;
+    bool direct = false;
+    int from_cache = 0;
+    ct_tile_config cfg{};
+    Resolved r{};
+};
+
+std::mutex g_plan_mu;
+std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
+std::atomic<long long> g_plan_misses{0};
+
+// The plan of fwd for shape s on device dev (set up).
+int get_plan(int dev, const Shape& s, Plan* out) {
+    const PlanKey k{{dev, s.N, s.CI, s.H, s.W, s.CO, s.KH, s.KW, s.stride, s.pad, s.dtype, s.epilogue}};
+    const unsigned gen = g_cache_gen.load(std::memory_order_acquire);
+    {
+        std::lock_guard<std::mutex> lk(g_plan_mu);
+        auto it = g_plans.find(k);
+        if (it != g_plans.end() && it->second.gen == gen) {
+            *out = it->second;
+            return CT_OK;
+        }
+    }
+    g_plan_misses.fetch_add(1, std::memory_order_relaxed);
+    Plan pl;
+    pl.gen = gen;
+    pl.cfg = choose(s, &pl.from_cache);
+    pl.direct = !variants()[pl.cfg.variant].ig;
+    if (!pl.direct) {
+        std::string why;
+        if (!legal(s, pl.cfg, &pl.r, &why))
+            return fail(CT_ERR_UNSUPPORTED, "the chosen tile config is not legal: %s", why.c_str());
+    }
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    g_plans[k] = pl;
+    *out = pl;
+    return CT_OK;
+}
+
 double now_s() {
     return std::chrono::duration<double>(std::chrono::system_clock::now().time_since_epoch())
         .count();
@@ -809,10 +945,18 @@ int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y, int N, int CI, in
     if (st != CT_OK) return st;
     st = check_pointers(x, w, y, epilogue, bias, var);
     if (st != CT_OK) return st;
-    ct_tile_config c = choose(s, nullptr);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (!variants()[c.variant].ig) return launch_direct(s, x, w, y, bias, var, eps, hs);
-    return launch_tiled(s, c, x, w, y, bias, var, eps, hs);
+    int dev = 0;
+    st = ensure_device(hs, &dev);
+    if (st != CT_OK) return st;
+    Plan pl;
+    st = get_plan(dev, s, &pl);
+    if (st != CT_OK) return st;
+    if (pl.direct) return launch_direct(s, x, w, y, bias, var, eps, hs);
+    LaunchScratch sc;
+    st = stream_scratch(dev, pl.cfg, pl.r, hs, &sc);
+    if (st != CT_OK) return st;
+    return launch_resolved(dev, s, pl.cfg, pl.r, sc, x, w, y, bias, var, eps, hs);
 }
 
 // Matrix product as the batch-1 1x1 convolution: C[M][N] = A[M][K] B[K][N]
@@ -1074,6 +1218,7 @@ int ct_cache_save(const char* path) {
 int ct_cache_clear(void) {
     std::lock_guard<std::mutex> lk(g_cache_mu);
     g_cache.clear();
+    g_cache_gen.fetch_add(1, std::memory_order_acq_rel);
     return CT_OK;
 }
 
@@ -1084,20 +1229,46 @@ int ct_cache_size(void) {
 
 int ct_release(void) {
     std::lock_guard<std::mutex> lk(g_ws_mu);
-    int st = CT_OK;
+    int cur = 0;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
     for (auto& kv : g_ws) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess) st = CT_ERR_HIP;
         (void)hipSetDevice(kv.first.first);
         (void)hipStreamSynchronize(kv.first.second);
         if (kv.second.ws) (void)hipFree(kv.second.ws);
         if (kv.second.tickets) (void)hipFree(kv.second.tickets);
         if (kv.second.aux) (void)hipFree(kv.second.aux);
-        (void)hipSetDevice(dev);
     }
+    for (auto& r : g_retired) {
+        (void)hipSetDevice(r.first);
+        (void)hipFree(r.second);
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+    (void)hipGetLastError();
     g_ws.clear();
+    g_retired.clear();
+    return have_cur ? CT_OK : CT_ERR_HIP;
+}
+
+int ct_init(int device) {
+    int count = 0;
+    hipError_t e = hipGetDeviceCount(&count);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceCount");
+    if (device < 0 || device >= count || device >= kMaxDevices)
+        return fail(CT_ERR_INVALID_ARG, "device %d: %d devices visible", device, count);
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    int st;
+    {
+        std::lock_guard<std::mutex> lk(g_dev_mu);
+        st = device_setup_locked(device);
+    }
+    if (cur != device) (void)hipSetDevice(cur);
     return st;
 }
+
+long long ct_plan_misses(void) { return g_plan_misses.load(std::memory_order_relaxed); }
 
 const char* ct_status_string(int status) {
     switch (status) {
@@ -1317,6 +1488,7 @@ int tune_finish(const Shape& s, const std::vector<ct_tune_record>& recs, ct_tile
     {
         std::lock_guard<std::mutex> lk(g_cache_mu);
         g_cache[s.key()] = CacheEntry{variants()[best.variant].desc.name, best, line};
+        g_cache_gen.fetch_add(1, std::memory_order_acq_rel);
     }
     const char* path = getenv("CT_CACHE_PATH");
     if (path && *path) {

@@ -1,5 +1,6 @@
-// Small device utilities for the tile-config search: deterministic scratch
-// fills and an on-device output comparison.
+// Small device utilities: deterministic scratch fills and an on-device output
+// comparison for the tile-config search, a word fill (kernel, not a memset, so
+// it may sit in a captured graph), and the workgroup-placement probe.
 #include "ct_device.hpp"
 #include "ct_kernels.hpp"
 
@@ -50,6 +51,11 @@ __global__ __launch_bounds__(256) void compare_kernel(const float* a, const floa
     if (local) atomicAdd(bad, local);
 }
 
+__global__ __launch_bounds__(256) void fill_u32_kernel(unsigned* dst, long long n, unsigned v) {
+    const long long stride = (long long)gridDim.x * blockDim.x;
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = v;
+}
+
 // Which XCD (accelerator complex die) each workgroup ran on: the XCC_ID
 // hardware register (id 20), bits 3:0.
 __global__ __launch_bounds__(64) void xcc_probe_kernel(int* out) {
@@ -89,6 +95,15 @@ hipError_t launch_fill_uniform(void* dst, long long n, int dtype, float lo, floa
         default:
             return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(unsigned* dst, long long n, unsigned v, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    long long blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dst, n, v);
     return hipGetLastError();
 }
 
