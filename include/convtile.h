@@ -137,6 +137,27 @@ int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y,
                        const float* bias, const float* var, float eps,
                        void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * convolution as ct_conv2d_nchw_fwd (same arguments, config, kernel and
+ * bits), but a launch's scratch -- the split partials, their arrival
+ * counters and the half-precision kernels' reordered filter -- lives in a
+ * fixed array inside the library instead of a per-stream workspace:
+ * CT_NOALLOC_SCRATCH_BYTES for partials plus filter and 16384 counters (at
+ * most 512 split tiles), held by every device the library runs on until the
+ * process ends.  Never calls hipMalloc or hipFree.  Errors: those of
+ * ct_conv2d_nchw_fwd, and CT_ERR_UNSUPPORTED when the config needs more
+ * scratch than that (the message says how much).  Every call on a device
+ * shares that device's array, which keeps the last call's contents: calls
+ * that overlap in time on one device (launches on different streams, or
+ * concurrent graph replays) race and give wrong results. */
+#define CT_NOALLOC_SCRATCH_BYTES (16LL << 20)
+int ct_conv2d_nchw_fwd_noalloc(const void* x, const void* w, float* y,
+                               int N, int CI, int H, int W, int CO, int KH, int KW,
+                               int stride, int pad, int dtype, int epilogue,
+                               const float* bias, const float* var, float eps,
+                               void* stream);
+
 /* The same with an explicit tile config (cfg->variant, split_k, stages, kc);
  * cfg->index is ignored.  Returns CT_ERR_UNSUPPORTED when the config is not
  * legal for the shape (the check of ct_conv2d_space_entity). */

@@ -84,6 +84,7 @@ _SHAPE = [_I] * 11  # N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue
 
 _SIGS = {
     "ct_conv2d_nchw_fwd": (_I, [_P, _P, _P] + [_I] * 11 + [_P, _P, _F, _P]),
+    "ct_conv2d_nchw_fwd_noalloc": (_I, [_P, _P, _P] + [_I] * 11 + [_P, _P, _F, _P]),
     "ct_conv2d_nchw_fwd_config": (_I, [_P, _P, _P] + [_I] * 11 +
                                   [_P, _P, _F, ctypes.POINTER(ct_tile_config), _P]),
     "ct_conv2d_nchw_direct": (_I, [_P, _P, _P] + [_I] * 11 + [_P, _P, _F, _P]),
@@ -190,6 +191,13 @@ def ct_conv2d_nchw_fwd(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dtype, epi
     return _load().ct_conv2d_nchw_fwd(_ptr(x), _ptr(w), _ptr(y), N, CI, H, W, CO, KH, KW, stride,
                                       pad, dtype, epilogue, _ptr(bias), _ptr(var), eps,
                                       _stream(stream))
+
+
+def ct_conv2d_nchw_fwd_noalloc(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,
+                               bias=None, var=None, eps=1e-5, stream=None) -> int:
+    return _load().ct_conv2d_nchw_fwd_noalloc(_ptr(x), _ptr(w), _ptr(y), N, CI, H, W, CO, KH, KW, stride,
+                                              pad, dtype, epilogue, _ptr(bias), _ptr(var), eps,
+                                              _stream(stream))
 
 
 def ct_conv2d_nchw_fwd_config(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,

@@ -350,6 +350,8 @@ std::mutex g_dev_mu;
 DeviceState g_dev[kMaxDevices];
 std::atomic<bool> g_dev_ready[kMaxDevices];
 
+int noalloc_setup(int dev, hipStream_t setup_stream);  // the no-allocation entry point's scratch
+
 // Set up device `dev` (current).  Not under capture: the caller checks.
 int device_setup_locked(int dev) {
     DeviceState& d = g_dev[dev];
@@ -363,6 +365,11 @@ int device_setup_locked(int dev) {
     hipStream_t ps = nullptr;
     e = hipStreamCreateWithFlags(&ps, hipStreamNonBlocking);
     if (e != hipSuccess) return hip_fail(e, "hipStreamCreateWithFlags");
+    const int st = noalloc_setup(dev, ps);
+    if (st != CT_OK) {
+        (void)hipStreamDestroy(ps);
+        return st;
+    }
     std::vector<int> h(kProbeBlocks, -1);
     bool rr = false;
     if (launch_xcc_probe(probe, kProbeBlocks, ps) == hipSuccess &&
@@ -703,6 +710,66 @@ int get_workspace(int dev, hipStream_t stream, long long ws_bytes, long long n_t
     return CT_OK;
 }
 
+// Scratch of one launch: the split partials, their arrival counters and a
+// variant's own buffer (the reordered filter).
+struct LaunchScratch {
+    float* ws = nullptr;
+    unsigned* tickets = nullptr;
+    void* aux = nullptr;
+};
+
+// ------------------------------------------------ no-allocation scratch --
+// ct_conv2d_nchw_fwd_noalloc keeps a launch's scratch in this array instead
+// of a per-stream workspace, for callers that cannot allocate.  Layout: the
+// split arrival counters first (16384 of them), then the split partials,
+// then a variant's own buffer (the reordered half-precision filter), each
+// 256-byte aligned.  Each device that loads the library holds its own copy
+// until the process ends.  In host code the array's name is only a host-side
+// stand-in: device set-up takes its device address per device with
+// hipGetSymbolAddress, and everything else uses that address.
+constexpr long long kScratchTicketBytes = 64LL << 10;
+constexpr long long kScratchDataBytes = CT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchTicketBytes + kScratchDataBytes];
+unsigned char* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device
+
+// Called once per device from device set-up (device current, under
+// g_dev_mu, not during capture).  The counters must start at zero: they are
+// cleared here, and every launch leaves the counters it used at zero again.
+int noalloc_setup(int dev, hipStream_t setup_stream) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    e = launch_fill_u32(static_cast<unsigned*>(ptr), kScratchTicketBytes / 4, 0u, setup_stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(setup_stream);
+    if (e != hipSuccess) return hip_fail(e, "clearing the no-allocation scratch");
+    g_scratch_ptr[dev] = static_cast<unsigned char*>(ptr);
+    return CT_OK;
+}
+
+// A launch's scratch carved from the array, or CT_ERR_UNSUPPORTED when it
+// does not fit.
+int array_scratch(int dev, const ct_tile_config& c, const Resolved& r, LaunchScratch* out) {
+    *out = LaunchScratch{};
+    const long long nt = c.split_k > 1 ? (long long)r.tiles_m * r.tiles_n * kTicketStride : 0;
+    const long long ws = c.split_k > 1 ? (r.ws_bytes + 255) / 256 * 256 : 0;
+    const long long aux = r.aux_bytes > 0 ? r.aux_bytes : 0;
+    if (nt * (long long)sizeof(unsigned) > kScratchTicketBytes)
+        return fail(CT_ERR_UNSUPPORTED,
+                    "%lld split tiles exceed the %lld arrival counters of the no-allocation scratch",
+                    nt / kTicketStride, kScratchTicketBytes / (long long)sizeof(unsigned) / kTicketStride);
+    if (ws + aux > kScratchDataBytes)
+        return fail(CT_ERR_UNSUPPORTED,
+                    "this shape's config needs %lld bytes of scratch (partials %lld, filter %lld), above the "
+                    "%lld-byte limit of the no-allocation entry point",
+                    ws + aux, ws, aux, kScratchDataBytes);
+    unsigned char* base = g_scratch_ptr[dev];
+    if (!base) return fail(CT_ERR_HIP, "no-allocation scratch of device %d not set up", dev);
+    out->tickets = reinterpret_cast<unsigned*>(base);
+    out->ws = reinterpret_cast<float*>(base + kScratchTicketBytes);
+    out->aux = aux > 0 ? base + kScratchTicketBytes + ws : nullptr;
+    return CT_OK;
+}
+
 // ------------------------------------------------------------- launches ---
 ConvParams base_params(const Shape& s, const void* x, const void* w, float* y, const float* bias,
                        const float* var, float eps) {
@@ -724,14 +791,6 @@ int launch_direct(const Shape& s, const void* x, const void* w, float* y, const 
     if (e != hipSuccess) return hip_fail(e, "direct convolution launch");
     return CT_OK;
 }
-
-// Scratch of one launch: the split partials, their arrival counters and a
-// variant's own buffer (the reordered filter).
-struct LaunchScratch {
-    float* ws = nullptr;
-    unsigned* tickets = nullptr;
-    void* aux = nullptr;
-};
 
 // Launch config c, already resolved (r) and checked legal for s, on device
 // dev (set up) with the given scratch.
@@ -955,6 +1014,28 @@ int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y, int N, int CI, in
     if (pl.direct) return launch_direct(s, x, w, y, bias, var, eps, hs);
     LaunchScratch sc;
     st = stream_scratch(dev, pl.cfg, pl.r, hs, &sc);
+    if (st != CT_OK) return st;
+    return launch_resolved(dev, s, pl.cfg, pl.r, sc, x, w, y, bias, var, eps, hs);
+}
+
+int ct_conv2d_nchw_fwd_noalloc(const void* x, const void* w, float* y, int N, int CI, int H, int W, int CO,
+                               int KH, int KW, int stride, int pad, int dtype, int epilogue,
+                               const float* bias, const float* var, float eps, void* stream) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    st = check_pointers(x, w, y, epilogue, bias, var);
+    if (st != CT_OK) return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    st = ensure_device(hs, &dev);
+    if (st != CT_OK) return st;
+    Plan pl;
+    st = get_plan(dev, s, &pl);
+    if (st != CT_OK) return st;
+    if (pl.direct) return launch_direct(s, x, w, y, bias, var, eps, hs);
+    LaunchScratch sc;
+    st = array_scratch(dev, pl.cfg, pl.r, &sc);
     if (st != CT_OK) return st;
     return launch_resolved(dev, s, pl.cfg, pl.r, sc, x, w, y, bias, var, eps, hs);
 }
