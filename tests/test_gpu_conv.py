@@ -165,17 +165,19 @@ SKC_LAYERS = [
 
 
 def _skc_configs(w):
-    return [c for c in legal_configs(w) if ct.variants()[c.variant]["name"].startswith(("f32skc", "f32skt"))]
+    return [c for c in legal_configs(w)
+            if ct.variants()[c.variant]["name"].startswith(("f32skc", "f32skt"))]
 
 
-@pytest.mark.parametrize("misaligned", ["none", "x", "y"], ids=["aligned", "x_offset_4B", "y_offset_4B"])
+@pytest.mark.parametrize("misaligned", ["none", "x", "w", "y"],
+                         ids=["aligned", "x_offset_4B", "w_offset_4B", "y_offset_4B"])
 @pytest.mark.parametrize("epi", [ct.CT_EPI_NONE, ct.CT_EPI_BIAS, ct.CT_EPI_EXP_BIAS_RSQRT])
 @pytest.mark.parametrize("w", SKC_LAYERS, ids=lambda w: w.name)
 def test_shape_specialised_split_k(w, epi, misaligned):
     """Every legal config of the shape-specialised kernels against the oracle:
     conv gate, epilogue gates, an input that is not 16-byte aligned (the
-    kernels then load the window word by word) and an output that is not
-    (16-byte stores fall back to words)."""
+    kernels then load the window word by word), a filter that is not, and an
+    output that is not (16-byte stores fall back to words)."""
     w = w.with_(epilogue=epi)
     cfgs = _skc_configs(w)
     say(f"[conv-skc] {w.name} epi={epi} misaligned={misaligned}: {len(cfgs)} configs")
@@ -192,6 +194,11 @@ def test_shape_specialised_split_k(w, epi, misaligned):
         xd = buf[1:].view(xd.shape)
         assert xd.data_ptr() % 16 != 0
     k = to_dev(inp["w"], w.dtype)
+    if misaligned == "w":
+        buf = torch.empty(k.numel() + 1, dtype=k.dtype, device=DEV)
+        buf[1:].copy_(k.reshape(-1))
+        k = buf[1:].view(k.shape)
+        assert k.data_ptr() % 16 != 0
     b = torch.from_numpy(inp["bias"]).to(DEV)
     v = torch.from_numpy(inp["var"]).to(DEV)
     for cfg in cfgs:
