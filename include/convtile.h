@@ -137,6 +137,34 @@ int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y,
                        const float* bias, const float* var, float eps,
                        void* stream);
 
+/* Half-precision filters in the layout the kernels stage from.  The
+ * half-precision kernels read the filter as 16-byte records of 8 input
+ * channels at one tap:
+ *
+ *   wp[co][g][t][j] = w[co][8g + j][t]   (t = ky*KW + kx; 0 when 8g + j >= CI)
+ *
+ * wp is [CO][ceil(CI/8)][KH*KW][8] halves, ct_conv2d_filter_prepared_bytes
+ * bytes.  ct_conv2d_nchw_fwd reorders the caller's filter into its scratch
+ * on every call (one small kernel before the convolution); a caller whose
+ * filter does not change between calls (inference) prepares it once with
+ * ct_conv2d_prepare_filter (asynchronous on `stream`, wp caller-owned device
+ * memory, 16-byte aligned) and calls ct_conv2d_nchw_fwd_prepared, which
+ * takes the same arguments as ct_conv2d_nchw_fwd with wp in place of w and
+ * gives the same bits, without the reorder.  The prepared entry point uses
+ * the cached tile config when its variant reads a prepared filter, else the
+ * best such default.  Errors: CT_ERR_INVALID_ARG for dtype CT_F32 (fp32
+ * kernels read the caller's layout directly) or a NULL pointer, and those of
+ * ct_conv2d_nchw_fwd; CT_ERR_UNSUPPORTED when no tile config of the shape
+ * reads a prepared filter. */
+long long ct_conv2d_filter_prepared_bytes(int CO, int CI, int KH, int KW, int dtype);
+int ct_conv2d_prepare_filter(const void* w, void* wp, int CO, int CI, int KH, int KW, int dtype,
+                             void* stream);
+int ct_conv2d_nchw_fwd_prepared(const void* x, const void* wp, float* y,
+                                int N, int CI, int H, int W, int CO, int KH, int KW,
+                                int stride, int pad, int dtype, int epilogue,
+                                const float* bias, const float* var, float eps,
+                                void* stream);
+
 /* For callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
  * convolution as ct_conv2d_nchw_fwd (same arguments, config, kernel and

@@ -85,6 +85,9 @@ _SHAPE = [_I] * 11  # N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue
 _SIGS = {
     "ct_conv2d_nchw_fwd": (_I, [_P, _P, _P] + [_I] * 11 + [_P, _P, _F, _P]),
     "ct_conv2d_nchw_fwd_noalloc": (_I, [_P, _P, _P] + [_I] * 11 + [_P, _P, _F, _P]),
+    "ct_conv2d_nchw_fwd_prepared": (_I, [_P, _P, _P] + [_I] * 11 + [_P, _P, _F, _P]),
+    "ct_conv2d_filter_prepared_bytes": (_LL, [_I] * 5),
+    "ct_conv2d_prepare_filter": (_I, [_P, _P] + [_I] * 5 + [_P]),
     "ct_conv2d_nchw_fwd_config": (_I, [_P, _P, _P] + [_I] * 11 +
                                   [_P, _P, _F, ctypes.POINTER(ct_tile_config), _P]),
     "ct_conv2d_nchw_direct": (_I, [_P, _P, _P] + [_I] * 11 + [_P, _P, _F, _P]),
@@ -198,6 +201,35 @@ def ct_conv2d_nchw_fwd_noalloc(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dt
     return _load().ct_conv2d_nchw_fwd_noalloc(_ptr(x), _ptr(w), _ptr(y), N, CI, H, W, CO, KH, KW, stride,
                                               pad, dtype, epilogue, _ptr(bias), _ptr(var), eps,
                                               _stream(stream))
+
+
+def ct_conv2d_nchw_fwd_prepared(x, wp, y, N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,
+                                bias=None, var=None, eps=1e-5, stream=None) -> int:
+    return _load().ct_conv2d_nchw_fwd_prepared(_ptr(x), _ptr(wp), _ptr(y), N, CI, H, W, CO, KH, KW, stride,
+                                               pad, dtype, epilogue, _ptr(bias), _ptr(var), eps,
+                                               _stream(stream))
+
+
+def ct_conv2d_filter_prepared_bytes(CO, CI, KH, KW, dtype) -> int:
+    return _load().ct_conv2d_filter_prepared_bytes(CO, CI, KH, KW, dtype)
+
+
+def ct_conv2d_prepare_filter(w, wp, CO, CI, KH, KW, dtype, stream=None) -> int:
+    return _load().ct_conv2d_prepare_filter(_ptr(w), _ptr(wp), CO, CI, KH, KW, dtype, _stream(stream))
+
+
+def prepare_filter(w, stream=None):
+    """The prepared (regrouped) copy of a half-precision filter w [CO, CI, KH, KW]
+    as a flat torch tensor of the same dtype."""
+    import torch
+    _on_gpu(w=w)
+    CO, CI, KH, KW = w.shape
+    dt = dtype_code(w.dtype)
+    nbytes = ct_conv2d_filter_prepared_bytes(CO, CI, KH, KW, dt)
+    check(nbytes if nbytes < 0 else 0, "prepare_filter")
+    wp = torch.empty(nbytes // 2, dtype=w.dtype, device=w.device)
+    check(ct_conv2d_prepare_filter(w, wp, CO, CI, KH, KW, dt, stream), "prepare_filter")
+    return wp
 
 
 def ct_conv2d_nchw_fwd_config(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue,
@@ -440,6 +472,24 @@ def conv2d(x, w, stride: int = 1, pad: int = 0, epilogue: int = CT_EPI_NONE, bia
         st = ct_conv2d_nchw_fwd(x, w, y, N, CI, H, W, CO, KH, KW, stride, pad, dt, epilogue, bias,
                                 var, eps, stream)
     check(st, "conv2d")
+    return y
+
+
+def conv2d_prepared(x, wp, filter_shape, stride: int = 1, pad: int = 0, epilogue: int = CT_EPI_NONE,
+                    bias=None, var=None, eps: float = 1e-5, out=None, stream=None):
+    """conv2d with a half-precision filter already prepared by prepare_filter;
+    filter_shape = (CO, CI, KH, KW) of the original filter."""
+    import torch
+    _on_gpu(x=x, wp=wp, bias=bias, var=var, out=out)
+    N, CI, H, W = x.shape
+    CO, CI2, KH, KW = filter_shape
+    if CI2 != CI or wp.dtype != x.dtype:
+        raise ValueError("x and the prepared filter disagree in channels or dtype")
+    OH, OW = out_extent(H, KH, stride, pad), out_extent(W, KW, stride, pad)
+    y = out if out is not None else torch.empty((N, CO, OH, OW), dtype=torch.float32, device=x.device)
+    st = ct_conv2d_nchw_fwd_prepared(x, wp, y, N, CI, H, W, CO, KH, KW, stride, pad, dtype_code(x.dtype),
+                                     epilogue, bias, var, eps, stream)
+    check(st, "conv2d_prepared")
     return y
 
 

@@ -56,6 +56,7 @@ struct ConvParams {
     FastDiv fd_ow, fd_t, fd_kw;
     FastDiv fd_w, fd_hw;                    // W, H*W (register-staged windows)
     void* aux;          // variant-specific scratch (a reordered filter copy), or null
+    int w_prepared;     // 1: w is already in the prepared layout of the variant (prepared_filter)
 };
 
 // Static description of one compiled implicit-GEMM instantiation.
@@ -70,7 +71,8 @@ struct IgemmVariant {
     // plus kc, stages, S and R filled in); > 163840 means "cannot run".
     int (*lds_bytes)(const ConvParams& p);
     hipError_t (*launch)(const ConvParams& p, hipStream_t stream);
-    // bytes of ConvParams::aux the launch needs (null: none)
+    // bytes of ConvParams::aux the launch needs (null: none); p.w may be
+    // null (the legality check), then the bytes for a 16-byte aligned w
     long long (*aux_bytes)(const ConvParams& p);
     // nonzero: the variant keeps each tile's split reduction inside one XCD,
     // relying on workgroup b running on XCD b % 8; legal only where the
@@ -79,6 +81,9 @@ struct IgemmVariant {
     // nonzero: the width (output pixels) of the variant's column tiles, when
     // it is not waves_n * reps_n * mfma_n
     int tile_n;
+    // nonzero: the launch also accepts a filter already in the prepared
+    // layout (ConvParams::w_prepared), the one h2_prepare_filter writes
+    int prepared_filter;
 };
 
 // Kernel-file registries.
@@ -89,6 +94,10 @@ const IgemmVariant* igemm_f32_skc_variants(int* count);
 const IgemmVariant* igemm_f32_skt_variants(int* count);
 const IgemmVariant* igemm_f16_variants(int* count);
 const IgemmVariant* igemm_f16v2_variants(int* count);
+
+// Half-precision prepared filter: wp [CO][ceil(CI/8)][T][8] = w [CO][CI][T]
+// regrouped into 16-byte records of 8 channels at one tap, zeros past CI.
+hipError_t h2_prepare_filter(const void* w, void* wp, int CO, int CI, int T, hipStream_t stream);
 
 // Direct (one lane per output) reference kernel.
 hipError_t launch_conv_direct(const ConvParams& p, int dtype, hipStream_t stream);

@@ -9,11 +9,13 @@
 // sit channel-fastest in LDS, so a fragment is one 16-byte LDS read:
 //   filter tile  [m][g][8]           window  [pixel][channel]
 // What differs from the first form is where the reordering happens:
-//  - the filter is reordered once per call by a small kernel into a
-//    stage-major copy [CO'][CI'/KC][9][KC] (zero-padded to CO' = multiple of
-//    256 and CI' = multiple of KC), so one stage of one filter row is 9*KC
-//    contiguous halves and staging the filter tile is a stream of 16-byte
-//    copies with no arithmetic;
+//  - the filter is reordered by a small kernel into the prepared layout
+//    [CO][CI8/8][T][8] (CI8 = CI rounded up to 8, zeros past CI): 8 channels
+//    at one tap per 16 bytes, so one stage of one filter row (KC/8 groups x T
+//    taps) is 9*KC contiguous halves, whatever KC is, and staging the filter
+//    tile is a stream of 16-byte copies with no arithmetic.  A caller with a
+//    static filter prepares it once (ct_conv2d_prepare_filter); otherwise
+//    each launch reorders into its scratch first;
 //  - the window is staged with vector loads of PX consecutive pixels of one
 //    channel (PX = 8, 4, 2 or 1, the largest the row width and alignment
 //    allow), 8 channels per task, transposed in registers into PX 16-byte
@@ -43,7 +45,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int uint4v __attribute__((ext_vector_type(4)));
 typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
 
-constexpr int kPackCO = 256;  // reordered filter rows: a multiple of this
 constexpr int kBufRaw = 0x00020000;       // raw buffer descriptor, 32-bit elements
 constexpr unsigned kBufOut = 0x80000000u;  // an offset past every buffer (all are < 2 GiB): reads zeros
 
@@ -61,21 +62,54 @@ template <> struct HMma2<DT_BF16> {
     }
 };
 
-// w [CO][CI][T] -> wp [COp][CIp/KC][T][KC], zeros outside CO x CI.
-__global__ __launch_bounds__(256) void h2_prepack_kernel(const uint16_t* __restrict__ w,
-                                                         uint16_t* __restrict__ wp, int CO, int CI,
-                                                         int T, int KC, int COp, int CIp) {
-    const long long total = (long long)COp * CIp * T;
-    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total;
-         i += (long long)gridDim.x * 256) {
-        const int c = (int)(i % KC);
-        const long long r1 = i / KC;
+// Record t of a prepared-filter unit: `in` holds one filter row's 8 channels
+// x T taps in the caller's layout (half h = c*T + t, channel-major); the
+// record is the 8 channels at tap t, each output word two halves picked by
+// one byte permute (v_perm_b32: bytes 0-3 of its second operand, 4-7 of its
+// first).
+template <int T>
+__device__ __forceinline__ uint4v tap_record(const uint4v* in, int t) {
+    uint4v o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int ia = 2 * j * T + t, ib = (2 * j + 1) * T + t;
+        const uint32_t wa = in[ia / 8][(ia % 8) / 2];
+        const uint32_t wb = in[ib / 8][(ib % 8) / 2];
+        const uint32_t sel = ((ib & 1) ? 0x07060000u : 0x05040000u) | ((ia & 1) ? 0x0302u : 0x0100u);
+        o[j] = __builtin_amdgcn_perm(wb, wa, sel);
+    }
+    return o;
+}
+
+// w [CO][CI][T] -> wp [CO][CI8/8][T][8], one thread per (row, 8-channel group)
+// unit: T 16-byte loads of the unit's contiguous run, T 16-byte records out.
+// Needs CI % 8 == 0 and a 16-byte aligned w.
+template <int T>
+__global__ __launch_bounds__(256) void h2_prepare_vec_kernel(const uint4v* __restrict__ w, uint4v* __restrict__ wp,
+                                                             long long units) {
+    const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (u >= units) return;
+    uint4v in[T];
+#pragma unroll
+    for (int i = 0; i < T; ++i) in[i] = w[u * T + i];
+#pragma unroll
+    for (int t = 0; t < T; ++t) wp[u * T + t] = T == 1 ? in[0] : tap_record<T>(in, t);
+}
+
+// The same for any CI and alignment, one element at a time.
+__global__ __launch_bounds__(256) void h2_prepare_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wp,
+                                                         int CO, int CI, int T) {
+    const int CG8 = (CI + 7) / 8;
+    const long long total = (long long)CO * CG8 * T * 8;
+    for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
+        const int j = (int)(i & 7);
+        const long long r1 = i >> 3;
         const int t = (int)(r1 % T);
         const long long r2 = r1 / T;
-        const int s = (int)(r2 % (CIp / KC));
-        const int co = (int)(r2 / (CIp / KC));
-        const int ci = s * KC + c;
-        wp[i] = (co < CO && ci < CI) ? w[((long long)co * CI + ci) * T + t] : (uint16_t)0;
+        const int g = (int)(r2 % CG8);
+        const long long co = r2 / CG8;
+        const int c = 8 * g + j;
+        wp[i] = c < CI ? w[(co * CI + c) * T + t] : (uint16_t)0;
     }
 }
 
@@ -228,9 +262,10 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     const long long HW = (long long)p.H * p.W;
 
     const uint16_t* __restrict__ xg = static_cast<const uint16_t*>(p.x);
-    const uint16_t* __restrict__ wpk = static_cast<const uint16_t*>(p.aux);
-    const int CIp = round_up(p.CI, KC);
-    const int NS = CIp / KC;  // stages of the whole reduction in the reordered filter
+    // the prepared filter: the caller's (p.w) or this launch's copy (p.aux)
+    const uint16_t* __restrict__ wpk = static_cast<const uint16_t*>(p.aux ? p.aux : p.w);
+    const int CG8 = (p.CI + 7) / 8;       // 8-channel groups of a prepared filter row
+    const int NS = (p.CI + KC - 1) / KC;  // stages of the whole reduction
 
     // ---- per-lane B columns --------------------------------------------------
     int pbase[RN];       // window pixel of the column's (0,0) tap
@@ -284,19 +319,26 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     }
 
     // ---- staging tasks (fixed for the kernel) ----------------------------------
-    // filter chunk q = (m, g): 16 bytes of row co0+m, group g of a stage
+    // filter chunk q = (m, r): 16 bytes of row co0+m, chunk r = cg*T + tap
+    // of a stage in the prepared layout (contiguous in r), LDS record g =
+    // tap*CG + cg
     int wsrc[WPT];  // halves, without the stage term; -1: no chunk
     int wdst[WPT];
+    int wcg[WPT];   // the chunk's channel group within a stage
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
         const int q = tid + j * NT;
         wsrc[j] = -1;
         wdst[j] = 0;
+        wcg[j] = 0;
         if (q < C::WCH) {
             const int m = q / G;
-            const int g = q - m * G;
-            wsrc[j] = (co0 + m) * NS * (T * KC) + g * 8;
-            wdst[j] = m * WST + g * 8;
+            const int r = q - m * G;
+            const int cg = r / T;
+            const int tap = r - cg * T;
+            wsrc[j] = (co0 + m) * CG8 * (T * 8) + r * 8;
+            wdst[j] = m * WST + (tap * CG + cg) * 8;
+            wcg[j] = cg;
         }
     }
     // window task q = (cg, window row r, run u): 8 channels x PX pixels
@@ -344,7 +386,7 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     // default, compiles to code on which the compiler must wait for every
     // load in flight, the prefetches included.)
     const long long x_bytes = (long long)p.N * p.CI * HW * 2;
-    const long long w_bytes = (long long)round_up(p.CO, kPackCO) * CIp * T * 2;
+    const long long w_bytes = (long long)p.CO * CG8 * T * 16;
     unsigned wvo[WPT], xvo[XPT];
 #pragma unroll
     for (int j = 0; j < WPT; ++j) wvo[j] = wsrc[j] >= 0 ? (unsigned)wsrc[j] * 2u : kBufOut;
@@ -414,12 +456,18 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
         // (descriptor fields pass through readfirstlane: they are uniform,
         // and a descriptor the compiler cannot prove uniform costs a loop
         // over the lanes around each load)
+        // The descriptor starts at the stage's first group of row 0, so rows
+        // past CO read zeros; a chunk whose channel group lies past the row
+        // (the last stage of a CI that is not a multiple of KC) reads zeros
+        // through an offset past the buffer.
         auto load_w1 = [&](int j, int s_abs) {
-            const int sb = __builtin_amdgcn_readfirstlane(s_abs * (T * KC));  // halves
+            const int g0 = s_abs * CG;                                        // first group of the stage
+            const int sb = __builtin_amdgcn_readfirstlane(g0 * (T * 8));      // halves
             const int nrec = __builtin_amdgcn_readfirstlane((int)(w_bytes - 2LL * sb));
             const __amdgpu_buffer_rsrc_t wrs =
                 __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wpk + sb), 0, nrec, kBufRaw);
-            wreg[j] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo[j], 0, 0));
+            const unsigned off = g0 + wcg[j] < CG8 ? wvo[j] : kBufOut;
+            wreg[j] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
         };
         auto load_x1 = [&](XRegs& rg, int i, int c0) {
             // one descriptor per channel (scalar work only)
@@ -594,11 +642,11 @@ int h2_bytes_for(const ConvParams& p, int px) {
     using C = H2<WM, WN, RM, RN, KC, T>;
     if (p.T != T || p.kc != KC) return 1 << 30;
     if (p.P >= (1LL << 31) || (long long)p.N * p.Hp >= (1LL << 31)) return 1 << 30;
-    const long long CIp = round_up(p.CI, KC);
-    const long long COp = round_up(p.CO, kPackCO);
-    // x and the reordered filter are read through buffer descriptors with
-    // 32-bit byte offsets; offset 2^31 must lie past both
-    if (COp * CIp * T * 2 >= (1LL << 31)) return 1 << 30;
+    // x and the prepared filter are read through buffer descriptors with
+    // 32-bit byte offsets; offset 2^31 must lie past both, also for the rows
+    // of the last tile past CO
+    const long long tiles_m = (p.CO + C::TM - 1) / C::TM;
+    if (tiles_m * C::TM * round_up(p.CI, 8) * T * 2 >= (1LL << 31)) return 1 << 30;
     if ((long long)p.N * p.CI * p.H * p.W * 2 >= (1LL << 31)) return 1 << 30;
     // the window tasks must fit the per-thread slots
     if ((long long)C::CG * p.R * (p.W / px) > (long long)C::XPT * C::NT) return 1 << 30;
@@ -611,9 +659,12 @@ int h2_lds_bytes(const ConvParams& p) {
     return h2_bytes_for<WM, WN, RM, RN, KC, T>(p, h2_px_for_shape(p.W));
 }
 
+// The launch's own prepared copy of the filter (none when the caller passes
+// a prepared filter).
 template <int WM, int WN, int RM, int RN, int KC, int T>
 long long h2_aux_bytes(const ConvParams& p) {
-    return 2LL * round_up(p.CO, kPackCO) * round_up(p.CI, KC) * T;
+    if (p.w_prepared) return 0;
+    return 2LL * p.CO * round_up(p.CI, 8) * T;
 }
 
 template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
@@ -638,7 +689,6 @@ hipError_t h2_launch_px(const ConvParams& q, int bytes, hipStream_t stream) {
 
 template <int DT, int WM, int WN, int RM, int RN, int KC, int T>
 hipError_t h2_launch(const ConvParams& p, hipStream_t stream) {
-    if (!p.aux) return hipErrorInvalidValue;
     // the widest window vector the shape and the pointer's alignment allow
     // (every run starts at a multiple of PX pixels of a row)
     int px = h2_px_for_shape(p.W);
@@ -647,20 +697,16 @@ hipError_t h2_launch(const ConvParams& p, hipStream_t stream) {
     const int bytes = h2_bytes_for<WM, WN, RM, RN, KC, T>(p, px);
     if (bytes > 163840 - 64) return hipErrorInvalidValue;
 
-    // reorder the filter into the stage-major copy
-    const int COp = round_up(p.CO, kPackCO);
-    const int CIp = round_up(p.CI, KC);
-    const long long total = (long long)COp * CIp * T;
-    long long blocks = (total + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(h2_prepack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(p.w), static_cast<uint16_t*>(p.aux), p.CO, p.CI,
-                       T, KC, COp, CIp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
-    ConvParams q = p;
+    ConvParams pp = p;
+    if (!p.w_prepared) {
+        // reorder the filter into this launch's prepared copy
+        if (!p.aux) return hipErrorInvalidValue;
+        const hipError_t e = h2_prepare_filter(p.w, p.aux, p.CO, p.CI, T, stream);
+        if (e != hipSuccess) return e;
+    } else {
+        pp.aux = nullptr;  // the caller's filter is prepared: stage from p.w
+    }
+    ConvParams q = pp;
     q.fd_kw = make_fastdiv((uint32_t)p.KW);
     switch (px) {
         case 8: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 8>(q, bytes, stream);
@@ -670,12 +716,37 @@ hipError_t h2_launch(const ConvParams& p, hipStream_t stream) {
     }
 }
 
+}  // namespace
+
+// wp [CO][CI8/8][T][8] = w [CO][CI][T] regrouped, zeros past CI.
+hipError_t h2_prepare_filter(const void* w, void* wp, int CO, int CI, int T, hipStream_t stream) {
+    (void)hipGetLastError();
+    const long long units = (long long)CO * ((CI + 7) / 8);
+    if (CI % 8 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0 && (T == 9 || T == 1)) {
+        const long long blocks = (units + 255) / 256;
+        if (T == 9)
+            hipLaunchKernelGGL(h2_prepare_vec_kernel<9>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                               static_cast<const uint4v*>(w), static_cast<uint4v*>(wp), units);
+        else
+            hipLaunchKernelGGL(h2_prepare_vec_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                               static_cast<const uint4v*>(w), static_cast<uint4v*>(wp), units);
+    } else {
+        long long blocks = (units * T * 8 + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(h2_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(w), static_cast<uint16_t*>(wp), CO, CI, T);
+    }
+    return hipGetLastError();
+}
+
+namespace {
+
 // descriptor: 32x32x16 instruction, waves WM x WN x 1, reps RM x RN; kc fixed
 // at KC (kc_max = KC); filters of T taps (3x3, and 1x1 for the matrix-product
 // view)
 #define CT_H2_VARIANT_T(NAME, DT, WM, WN, RM, RN, KC, T)                                         \
     {NAME, DT, 32, 32, 16, WM, WN, 1, RM, RN, KC, &h2_lds_bytes<WM, WN, RM, RN, KC, T>,          \
-     &h2_launch<DT, WM, WN, RM, RN, KC, T>, &h2_aux_bytes<WM, WN, RM, RN, KC, T>}
+     &h2_launch<DT, WM, WN, RM, RN, KC, T>, &h2_aux_bytes<WM, WN, RM, RN, KC, T>, 0, 0, 1}
 #define CT_H2_VARIANT(NAME, DT, WM, WN, RM, RN, KC) CT_H2_VARIANT_T(NAME, DT, WM, WN, RM, RN, KC, 9)
 
 const IgemmVariant kH2Variants[] = {

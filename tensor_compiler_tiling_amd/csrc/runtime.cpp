@@ -748,11 +748,11 @@ int noalloc_setup(int dev, hipStream_t setup_stream) {
 
 // A launch's scratch carved from the array, or CT_ERR_UNSUPPORTED when it
 // does not fit.
-int array_scratch(int dev, const ct_tile_config& c, const Resolved& r, LaunchScratch* out) {
+int array_scratch(int dev, const ct_tile_config& c, const Resolved& r, long long aux_bytes, LaunchScratch* out) {
     *out = LaunchScratch{};
     const long long nt = c.split_k > 1 ? (long long)r.tiles_m * r.tiles_n * kTicketStride : 0;
     const long long ws = c.split_k > 1 ? (r.ws_bytes + 255) / 256 * 256 : 0;
-    const long long aux = r.aux_bytes > 0 ? r.aux_bytes : 0;
+    const long long aux = aux_bytes > 0 ? aux_bytes : 0;
     if (nt * (long long)sizeof(unsigned) > kScratchTicketBytes)
         return fail(CT_ERR_UNSUPPORTED,
                     "%lld split tiles exceed the %lld arrival counters of the no-allocation scratch",
@@ -796,8 +796,9 @@ int launch_direct(const Shape& s, const void* x, const void* w, float* y, const 
 // dev (set up) with the given scratch.
 int launch_resolved(int dev, const Shape& s, const ct_tile_config& c, const Resolved& r, const LaunchScratch& sc,
                     const void* x, const void* w, float* y, const float* bias, const float* var, float eps,
-                    hipStream_t stream) {
+                    hipStream_t stream, bool prepared = false) {
     ConvParams p = base_params(s, x, w, y, bias, var, eps);
+    p.w_prepared = prepared ? 1 : 0;
     p.kc = c.kc;
     p.stages = c.stages;
     p.S = c.split_k;
@@ -819,12 +820,22 @@ long long tickets_needed(const ct_tile_config& c, const Resolved& r) {
     return c.split_k > 1 ? (long long)r.tiles_m * r.tiles_n * kTicketStride : 0;
 }
 
+// Bytes of a variant's own scratch for a launch (none when the caller passes
+// a prepared filter).
+long long launch_aux_bytes(const Shape& s, const Resolved& r, bool prepared) {
+    if (!r.v->ig->aux_bytes) return 0;
+    ConvParams p = base_params(s, nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f);
+    p.w_prepared = prepared ? 1 : 0;
+    return r.v->ig->aux_bytes(p);
+}
+
 // The stream's workspace (grown if needed) as a launch's scratch.
-int stream_scratch(int dev, const ct_tile_config& c, const Resolved& r, hipStream_t stream, LaunchScratch* out) {
+int stream_scratch(int dev, const ct_tile_config& c, const Resolved& r, long long aux_bytes, hipStream_t stream,
+                   LaunchScratch* out) {
     *out = LaunchScratch{};
-    if (c.split_k <= 1 && r.aux_bytes <= 0) return CT_OK;
+    if (c.split_k <= 1 && aux_bytes <= 0) return CT_OK;
     Workspace ws;
-    const int st = get_workspace(dev, stream, r.ws_bytes, tickets_needed(c, r), r.aux_bytes, &ws);
+    const int st = get_workspace(dev, stream, r.ws_bytes, tickets_needed(c, r), aux_bytes, &ws);
     if (st != CT_OK) return st;
     out->ws = ws.ws;
     out->tickets = ws.tickets;
@@ -842,14 +853,19 @@ int launch_tiled(const Shape& s, const ct_tile_config& c, const void* x, const v
     if (!legal(s, c, &r, &why))
         return fail(CT_ERR_UNSUPPORTED, "tile config not legal for this shape: %s", why.c_str());
     LaunchScratch sc;
-    st = stream_scratch(dev, c, r, stream, &sc);
+    st = stream_scratch(dev, c, r, launch_aux_bytes(s, r, false), stream, &sc);
     if (st != CT_OK) return st;
     return launch_resolved(dev, s, c, r, sc, x, w, y, bias, var, eps, stream);
 }
 
-// Built-in default: the legal point with the smallest predicted time.
-bool default_config(const Shape& s, ct_tile_config* out) {
-    const std::string key = s.key();
+// Built-in default: the legal point with the smallest predicted time (only
+// among variants that accept a prepared filter when `prepared`).
+bool accepts(const Shape& s, const ct_tile_config& c, bool prepared) {
+    return !prepared || (variants()[c.variant].ig && variants()[c.variant].ig->prepared_filter);
+}
+
+bool default_config(const Shape& s, ct_tile_config* out, bool prepared = false) {
+    const std::string key = s.key() + (prepared ? ",prepared" : "");
     {
         std::lock_guard<std::mutex> lk(g_cache_mu);
         auto it = g_default_memo.find(key);
@@ -866,7 +882,7 @@ bool default_config(const Shape& s, ct_tile_config* out) {
         ct_tile_config c;
         decode(sp, i, &c);
         Resolved r;
-        if (!legal(s, c, &r, nullptr)) continue;
+        if (!accepts(s, c, prepared) || !legal(s, c, &r, nullptr)) continue;
         const double t = predict_us(s, c, r);
         if (t < best) {
             best = t;
@@ -880,7 +896,10 @@ bool default_config(const Shape& s, ct_tile_config* out) {
 }
 
 // The config fwd uses: cached winner, else default; variant -1 = direct.
-ct_tile_config choose(const Shape& s, int* from_cache) {
+// With `prepared`, only configs whose variant accepts a prepared filter (a
+// cached winner that does not is passed over), and no direct fallback:
+// variant -1 when none is legal.
+ct_tile_config choose(const Shape& s, int* from_cache, bool prepared = false) {
     ct_tile_config c_cached{};
     bool have = false;
     {
@@ -892,14 +911,14 @@ ct_tile_config choose(const Shape& s, int* from_cache) {
         }
     }
     // a cached config may name a variant this device cannot run
-    if (have && legal(s, c_cached, nullptr, nullptr)) {
+    if (have && accepts(s, c_cached, prepared) && legal(s, c_cached, nullptr, nullptr)) {
         if (from_cache) *from_cache = 1;
         return c_cached;
     }
     if (from_cache) *from_cache = 0;
     ct_tile_config c{};
-    if (!default_config(s, &c)) {
-        c.variant = (int)s.dtype;  // the direct kernel of this dtype
+    if (!default_config(s, &c, prepared)) {
+        c.variant = prepared ? -1 : (int)s.dtype;  // the direct kernel of this dtype
         c.split_k = c.stages = c.kc = 1;
         c.index = -1;
     }
@@ -914,7 +933,7 @@ ct_tile_config choose(const Shape& s, int* from_cache) {
 // which retires every plan.
 
 struct PlanKey {
-    int v[12];
+    int v[13];
     bool operator==(const PlanKey& o) const { return memcmp(v, o.v, sizeof v) == 0; }
 };
 
@@ -941,9 +960,11 @@ std::mutex g_plan_mu;
 std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
 std::atomic<long long> g_plan_misses{0};
 
-// The plan of fwd for shape s on device dev (set up).
-int get_plan(int dev, const Shape& s, Plan* out) {
-    const PlanKey k{{dev, s.N, s.CI, s.H, s.W, s.CO, s.KH, s.KW, s.stride, s.pad, s.dtype, s.epilogue}};
+// The plan of fwd for shape s on device dev (set up); `prepared`: the plan
+// of the prepared-filter entry point.
+int get_plan(int dev, const Shape& s, Plan* out, bool prepared = false) {
+    const PlanKey k{{dev, s.N, s.CI, s.H, s.W, s.CO, s.KH, s.KW, s.stride, s.pad, s.dtype, s.epilogue,
+                     prepared ? 1 : 0}};
     const unsigned gen = g_cache_gen.load(std::memory_order_acquire);
     {
         std::lock_guard<std::mutex> lk(g_plan_mu);
@@ -956,7 +977,9 @@ int get_plan(int dev, const Shape& s, Plan* out) {
     g_plan_misses.fetch_add(1, std::memory_order_relaxed);
     Plan pl;
     pl.gen = gen;
-    pl.cfg = choose(s, &pl.from_cache);
+    pl.cfg = choose(s, &pl.from_cache, prepared);
+    if (pl.cfg.variant < 0)
+        return fail(CT_ERR_UNSUPPORTED, "no tile config of this shape accepts a prepared filter");
     pl.direct = !variants()[pl.cfg.variant].ig;
     if (!pl.direct) {
         std::string why;
@@ -1013,7 +1036,7 @@ int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y, int N, int CI, in
     if (st != CT_OK) return st;
     if (pl.direct) return launch_direct(s, x, w, y, bias, var, eps, hs);
     LaunchScratch sc;
-    st = stream_scratch(dev, pl.cfg, pl.r, hs, &sc);
+    st = stream_scratch(dev, pl.cfg, pl.r, launch_aux_bytes(s, pl.r, false), hs, &sc);
     if (st != CT_OK) return st;
     return launch_resolved(dev, s, pl.cfg, pl.r, sc, x, w, y, bias, var, eps, hs);
 }
@@ -1035,9 +1058,49 @@ int ct_conv2d_nchw_fwd_noalloc(const void* x, const void* w, float* y, int N, in
     if (st != CT_OK) return st;
     if (pl.direct) return launch_direct(s, x, w, y, bias, var, eps, hs);
     LaunchScratch sc;
-    st = array_scratch(dev, pl.cfg, pl.r, &sc);
+    st = array_scratch(dev, pl.cfg, pl.r, launch_aux_bytes(s, pl.r, false), &sc);
     if (st != CT_OK) return st;
     return launch_resolved(dev, s, pl.cfg, pl.r, sc, x, w, y, bias, var, eps, hs);
+}
+
+long long ct_conv2d_filter_prepared_bytes(int CO, int CI, int KH, int KW, int dtype) {
+    if (CO <= 0 || CI <= 0 || KH <= 0 || KW <= 0) return fail(CT_ERR_INVALID_ARG, "every dimension must be positive");
+    if (dtype != CT_F16 && dtype != CT_BF16)
+        return fail(CT_ERR_INVALID_ARG, "prepared filters exist for CT_F16 and CT_BF16 only");
+    return 2LL * CO * ((CI + 7) / 8 * 8) * KH * KW;
+}
+
+int ct_conv2d_prepare_filter(const void* w, void* wp, int CO, int CI, int KH, int KW, int dtype, void* stream) {
+    const long long bytes = ct_conv2d_filter_prepared_bytes(CO, CI, KH, KW, dtype);
+    if (bytes < 0) return (int)bytes;
+    if (!w || !wp) return fail(CT_ERR_INVALID_ARG, "w and wp must not be NULL");
+    if ((long long)KH * KW > 1024) return fail(CT_ERR_INVALID_ARG, "filter too large");
+    const hipError_t e = h2_prepare_filter(w, wp, CO, CI, KH * KW, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "filter preparation");
+    return CT_OK;
+}
+
+int ct_conv2d_nchw_fwd_prepared(const void* x, const void* wp, float* y, int N, int CI, int H, int W, int CO,
+                                int KH, int KW, int stride, int pad, int dtype, int epilogue,
+                                const float* bias, const float* var, float eps, void* stream) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    st = check_pointers(x, wp, y, epilogue, bias, var);
+    if (st != CT_OK) return st;
+    if (dtype != CT_F16 && dtype != CT_BF16)
+        return fail(CT_ERR_INVALID_ARG, "prepared filters exist for CT_F16 and CT_BF16 only");
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    int dev = 0;
+    st = ensure_device(hs, &dev);
+    if (st != CT_OK) return st;
+    Plan pl;
+    st = get_plan(dev, s, &pl, true);
+    if (st != CT_OK) return st;
+    LaunchScratch sc;
+    st = stream_scratch(dev, pl.cfg, pl.r, launch_aux_bytes(s, pl.r, true), hs, &sc);
+    if (st != CT_OK) return st;
+    return launch_resolved(dev, s, pl.cfg, pl.r, sc, x, wp, y, bias, var, eps, hs, true);
 }
 
 // Matrix product as the batch-1 1x1 convolution: C[M][N] = A[M][K] B[K][N]

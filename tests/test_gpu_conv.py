@@ -344,6 +344,9 @@ HALF_SMALL = [
     ("half_w14", 132, 2, 40, 10, 14, 70, 3, 3, 1, 1),
     # width 12, stride 2: 4-pixel runs
     ("half_w12_s2", 133, 1, 16, 12, 12, 32, 3, 3, 2, 1),
+    # 12 channels, not a multiple of 8: the filter goes through the reordered
+    # copy instead of being staged from the caller's layout
+    ("half_ci12", 136, 2, 12, 9, 11, 40, 3, 3, 1, 1),
 ]
 
 
@@ -364,6 +367,17 @@ def test_half_precision_small(dtype, shape):
     assert np.array_equal(run(w, ints), yi)
     for cfg in legal_configs(w):
         assert np.array_equal(run(w, ints, config=cfg), yi), ct.variants()[cfg.variant]["name"]
+    # a filter that is not 16-byte aligned (staged with 2-byte loads)
+    x = to_dev(ints["x"], dtype)
+    k = to_dev(ints["w"], dtype)
+    buf = torch.empty(k.numel() + 1, dtype=k.dtype, device=DEV)
+    buf[1:].copy_(k.reshape(-1))
+    k1 = buf[1:].view(k.shape)
+    assert k1.data_ptr() % 16 != 0
+    for cfg in [None] + legal_configs(w):
+        got = ct.conv2d(x, k1, w.stride, w.pad, config=cfg)
+        torch.cuda.synchronize()
+        assert np.array_equal(got.cpu().numpy().astype(np.float64), yi), ("misaligned w", cfg)
 
 
 HALF_FULL = ["f16_n64_c256_14x14_k3", "f16_n128_c128to256_32x32_k3_epi"]
@@ -470,3 +484,78 @@ def test_half_precision_epilogue_every_config(dtype, shape, epi):
             assert rel <= TOL[dtype] * S + 1e-5, (what, rel)
         else:
             assert float(np.abs(got - ref).max()) <= TOL[dtype] * S, what
+
+
+def _regroup(w: np.ndarray) -> np.ndarray:
+    """The documented prepared layout: wp[co][g][t][j] = w[co][8g+j][t],
+    zeros past CI (t = ky*KW + kx)."""
+    CO, CI, KH, KW = w.shape
+    G = (CI + 7) // 8
+    wpad = np.zeros((CO, 8 * G, KH * KW), w.dtype)
+    wpad[:, :CI] = w.reshape(CO, CI, KH * KW)
+    return wpad.reshape(CO, G, 8, KH * KW).transpose(0, 1, 3, 2).copy()
+
+
+def _bits16(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy()
+
+
+@pytest.mark.parametrize("misaligned", [False, True], ids=["aligned", "w_offset_2B"])
+@pytest.mark.parametrize("shape", HALF_SMALL, ids=lambda t: t[0])
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+def test_prepared_filter(dtype, shape, misaligned):
+    """ct_conv2d_prepare_filter writes exactly the documented layout, and the
+    prepared entry point gives the bits of ct_conv2d_nchw_fwd (same kernel and
+    config), within the oracle's gate -- or, for a shape where no tile config
+    reads a prepared filter (a channel count with no 16- or 32-channel
+    stage), refuses it."""
+    w = wl.ConvWorkload(*shape, dtype)
+    inp = wl.conv_inputs(w)
+    x = to_dev(inp["x"], dtype)
+    k = to_dev(inp["w"], dtype)
+    if misaligned:
+        buf = torch.empty(k.numel() + 1, dtype=k.dtype, device=DEV)
+        buf[1:].copy_(k.reshape(-1))
+        k = buf[1:].view(k.shape)
+        assert k.data_ptr() % 16 != 0
+    wp = ct.prepare_filter(k)
+    torch.cuda.synchronize()
+    want = _regroup(_bits16(k.contiguous()).reshape(k.shape))
+    assert np.array_equal(_bits16(wp).reshape(want.shape), want)
+    y_fwd = ct.conv2d(x, k, w.stride, w.pad)
+    if not any(ct.variants()[c.variant]["name"].startswith("h2") for c in legal_configs(w)):
+        y_pre = torch.empty_like(y_fwd)
+        st = ct.ct_conv2d_nchw_fwd_prepared(x, wp, y_pre, *w.shape_args(), CT_DT[dtype], w.epilogue)
+        assert st == ct.CT_ERR_UNSUPPORTED
+        return
+    y_pre = ct.conv2d_prepared(x, wp, tuple(k.shape), w.stride, w.pad)
+    torch.cuda.synchronize()
+    _, cfg, _ = ct.ct_conv2d_query(*w.shape_args(), CT_DT[dtype], w.epilogue)
+    if ct.variants()[cfg.variant]["name"].startswith("h2"):
+        assert torch.equal(y_fwd.view(torch.int32), y_pre.view(torch.int32))
+    y, a = oracle_full(w, inp)
+    assert_conv_close(y_pre.cpu().numpy().astype(np.float64), y, a, dtype, f"{w.name} prepared")
+
+
+@pytest.mark.parametrize("name", HALF_FULL)
+def test_prepared_filter_full_size(name):
+    """Both full-size half-precision workloads: the prepared entry point gives
+    the bits of ct_conv2d_nchw_fwd, the fused epilogue included."""
+    w = wl.CONV_WORKLOADS[name]
+    inp, y, a = _half_full_reference(name)
+    x = to_dev(inp["x"], w.dtype)
+    k = to_dev(inp["w"], w.dtype)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    v = torch.from_numpy(inp["var"]).to(DEV)
+    wp = ct.prepare_filter(k)
+    y_fwd = ct.conv2d(x, k, w.stride, w.pad, w.epilogue, b, v)
+    y_pre = ct.conv2d_prepared(x, wp, tuple(k.shape), w.stride, w.pad, w.epilogue, b, v)
+    torch.cuda.synchronize()
+    assert torch.equal(y_fwd.view(torch.int32), y_pre.view(torch.int32))
+    say(f"[conv-f16-prepared] {name}: bit-identical to the raw-filter entry point")
+
+
+def test_prepared_filter_rejects_fp32():
+    k = torch.zeros((8, 8, 3, 3), device=DEV)
+    wp = torch.zeros(8 * 8 * 9, device=DEV)
+    assert ct.ct_conv2d_prepare_filter(k, wp, 8, 8, 3, 3, ct.CT_F32) == ct.CT_ERR_INVALID_ARG

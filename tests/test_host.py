@@ -449,3 +449,12 @@ def test_tensor_helpers_reject_host_and_strided_tensors():
         ct.broadcast(torch.ones(4), 2, 3, 3)
     with pytest.raises(ValueError, match="GPU"):
         ct.broadcast_chain(ct.make_program([("set", 1.0)]), 2, 3, 4, arrays=[torch.ones(3)])
+
+
+def test_prepared_filter_bytes():
+    # [CO][ceil(CI/8)][KH*KW][8] halves
+    assert ct.ct_conv2d_filter_prepared_bytes(256, 256, 3, 3, ct.CT_F16) == 2 * 256 * 256 * 9
+    assert ct.ct_conv2d_filter_prepared_bytes(40, 12, 3, 3, ct.CT_BF16) == 2 * 40 * 16 * 9
+    assert ct.ct_conv2d_filter_prepared_bytes(4096, 4096, 1, 1, ct.CT_F16) == 2 * 4096 * 4096
+    assert ct.ct_conv2d_filter_prepared_bytes(8, 8, 3, 3, ct.CT_F32) == ct.CT_ERR_INVALID_ARG
+    assert ct.ct_conv2d_filter_prepared_bytes(0, 8, 3, 3, ct.CT_F16) == ct.CT_ERR_INVALID_ARG

@@ -69,16 +69,19 @@ def _check_pair(w):
     assert err <= gate
 
 
-# first call large, second smaller: fp32 split reduction, then the
-# half-precision kernel with its reordered filter in the scratch
+# first call large, second smaller: fp32 split reduction; the half-precision
+# kernel; the half-precision kernel with channel counts that are not a
+# multiple of 8, whose reordered filter copy lives in the scratch
 PAIRS = [
     ("resnet_final_c512_7x7_k3", "resnet_c64_14x14_k3"),
     ("f16_n64_c256_14x14_k3", wl.ConvWorkload("noalloc_f16_small", 140, 2, 32, 16, 16, 48, 3, 3, 1, 1, wl.F16,
                                                wl.EPI_EXP_BIAS_RSQRT)),
+    (wl.ConvWorkload("noalloc_f16_ci36", 141, 8, 36, 20, 20, 96, 3, 3, 1, 1, wl.F16),
+     wl.ConvWorkload("noalloc_f16_ci12", 142, 2, 12, 9, 11, 40, 3, 3, 1, 1, wl.F16)),
 ]
 
 
-@pytest.mark.parametrize("pair", PAIRS, ids=["fp32_split", "f16_filter"])
+@pytest.mark.parametrize("pair", PAIRS, ids=["fp32_split", "f16", "f16_reordered_filter"])
 def test_noalloc_matches_the_allocating_entry_point(pair):
     for item in pair:
         w = wl.CONV_WORKLOADS[item] if isinstance(item, str) else item
@@ -112,11 +115,9 @@ def test_noalloc_captures_without_an_earlier_launch():
 
 def test_noalloc_rejects_configs_beyond_its_scratch():
     """The tuned 2048^3 fp32 product splits its reduction 8 ways (128 MiB of
-    partials) and the 4096^3 fp16 product reorders a 32 MiB filter: both
-    exceed the fixed scratch, so the call fails before any launch; a call
-    that fits still works afterwards."""
-    for g in (wl.GEMM_WORKLOADS["gemm_f32_m2048_n2048_k2048_epi"],
-              wl.GEMM_WORKLOADS["gemm_f16_m4096_n4096_k4096"]):
+    partials), beyond the fixed scratch, so the call fails before any launch;
+    a call that fits still works afterwards."""
+    for g in (wl.GEMM_WORKLOADS["gemm_f32_m2048_n2048_k2048_epi"],):
         w = g.conv_view()
         tdt = torch.float32 if w.dtype == wl.F32 else torch.float16
         x = torch.zeros((w.N, w.CI, w.H, w.W), dtype=tdt, device=DEV)
