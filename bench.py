@@ -13,13 +13,17 @@ host through the C ABI (host dispatch included).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
                     [--tune] [--cache PATH | --no-cache] [--no-cpu-baseline]
-                    [--calibrate-copy]
+                    [--no-per-shape] [--calibrate-copy]
 
 The tile config comes from the tuning log shipped with the package (the
 search's recorded winners, loaded with ct_cache_load) unless --no-cache or
 --tune is given.  K steps are captured in one HIP graph and replayed
 (default) or launched eagerly (--eager); HIP events on the launch stream
 bracket the K steps.
+With no --workload the line also carries `per_shape`: every other row of
+the workload table (the batch-1 fp32 layers, both half-precision layers with
+the filter reordered per call and prepared once, the standalone broadcast in
+fp16 and fp32), each timed the same way.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -128,6 +132,8 @@ def _parse():
     ap.add_argument("--tune-trials", type=int, default=0)
     ap.add_argument("--tune-ms", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-shape", action="store_true",
+                    help="default workload only: leave out the per-shape list of the other rows")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cache", default=DEFAULT_CACHE,
                     help="tuning log (JSON lines) to load before dispatch")
@@ -487,6 +493,119 @@ def bench_chain(a, name: str) -> dict:
     return out
 
 
+def time_graph(step, stream, steps: int, warmup: int) -> float:
+    """Mean ms per step of `steps` calls of step() captured in one HIP graph
+    and replayed, timed with HIP events on `stream` (after `warmup` eager
+    calls and one untimed replay)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(steps):
+            step()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / steps
+
+
+def conv_step(w, prepared: bool = False):
+    """(step, config) for one convolution of workload w through the C ABI, on
+    the current stream at call time; inputs resident on the GPU."""
+    import torch
+    from tensor_compiler_tiling_amd import convtile as ct
+    from tensor_compiler_tiling_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    inp = wl.conv_inputs(w)
+    x = torch.from_numpy(inp["x"]).to(dev).to(tdt)
+    k = torch.from_numpy(inp["w"]).to(dev).to(tdt)
+    b = torch.from_numpy(inp["bias"]).to(dev)
+    v = torch.from_numpy(inp["var"]).to(dev)
+    y = torch.empty((w.N, w.CO, w.OH, w.OW), dtype=torch.float32, device=dev)
+    dt = ct.dtype_code(tdt)
+    args = w.shape_args() + (dt, w.epilogue)
+    lib = ct.library()
+    if prepared:
+        k = ct.prepare_filter(k)
+    fn = lib.ct_conv2d_nchw_fwd_prepared if prepared else lib.ct_conv2d_nchw_fwd
+    keep = (x, k, b, v, y)
+
+    def step():
+        st = fn(keep[0].data_ptr(), keep[1].data_ptr(), keep[4].data_ptr(), *args, keep[2].data_ptr(),
+                keep[3].data_ptr(), 1e-5, torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise ct.ConvTileError(st, "fwd")
+
+    st, cfg, from_cache = ct.ct_conv2d_query(*args)
+    ct.check(st, "query")
+    return step, cfg, from_cache
+
+
+def per_shape(a) -> list:
+    """Every other row of the workload table, each timed the way the headline
+    is (a HIP graph of back-to-back launches, HIP events on its stream): the
+    batch-1 fp32 layers, both half-precision layers (the filter reordered per
+    call, and prepared once), and the standalone broadcast in fp16 and fp32."""
+    import torch
+    from tensor_compiler_tiling_amd import convtile as ct
+    from tensor_compiler_tiling_amd import workloads as wl
+    steps = max(a.steps, 100)
+    out = []
+    names = ["resnet_c64_14x14_k3"] + wl.SWEEP + ["f16_n64_c256_14x14_k3", "f16_n128_c128to256_32x32_k3_epi"]
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
+    for name in names:
+        w = wl.CONV_WORKLOADS[name]
+        peak = PEAK_TFLOPS[w.dtype]
+        for prepared in ((False, True) if w.dtype != "f32" else (False,)):
+            step, cfg, _ = conv_step(w, prepared)
+            ms = time_graph(step, stream, steps, a.warmup)
+            tf = w.flops / (ms * 1e-3) / 1e12
+            vname = ct.variants()[cfg.variant]["name"]
+            tile = {"split_k": cfg.split_k, "stages": cfg.stages, "kc": cfg.kc}
+            out.append({"workload": name + (" (prepared filter)" if prepared else ""), "dtype": w.dtype,
+                        "us": round(ms * 1e3, 3), "TFLOP/s": round(tf, 2), "bound": "mfma",
+                        "frac": round(tf / peak, 4), "kernel": vname, "tile": tile,
+                        "traffic": measured_traffic(name, vname, tile) if not prepared else None})
+    for name in ("bcast_exp_128x256x32x32_f16", "bcast_exp_128x256x32x32_f32"):
+        bw = wl.BROADCAST_WORKLOADS[name]
+        dt = torch.float16 if bw.out_dtype == wl.F16 else torch.float32
+        var = torch.from_numpy(wl.broadcast_var(bw)).to("cuda:0")
+        nbytes = bw.bytes_written()
+        nbuf = max(2, -(-300 * 2 ** 20 // nbytes))
+        outs = [torch.empty((bw.N, bw.C, bw.H, bw.W), dtype=dt, device="cuda:0") for _ in range(nbuf)]
+        lib = ct.library()
+        code = ct.dtype_code(dt)
+        it = [0]
+
+        def bstep():
+            i = it[0] = it[0] + 1
+            st = lib.ct_broadcast_nchw(var.data_ptr(), outs[i % nbuf].data_ptr(), bw.N, bw.C, bw.H, bw.W, code,
+                                       ct.CT_BC_EXP, ct.CT_BC_CHANNEL, torch.cuda.current_stream().cuda_stream)
+            if st != 0:
+                raise ct.ConvTileError(st, "broadcast")
+
+        ms = time_graph(bstep, stream, steps, a.warmup)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.append({"workload": name, "dtype": bw.out_dtype, "us": round(ms * 1e3, 3), "GB/s": round(gbs, 1),
+                    "bound": "hbm", "frac": round(gbs / PEAK_HBM_GBS, 4), "kernel": "bcast_channel",
+                    "rotating_buffers": nbuf,
+                    "traffic": measured_traffic(name, "broadcast", {"mode": "channel"})})
+        del outs
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     a = _parse()
     if a.gpus != 1:
@@ -518,13 +637,8 @@ def main():
     w = gemm.conv_view() if gemm is not None else wl.CONV_WORKLOADS[name]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    ct.check(ct.ct_init(0), "init")
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
-    inp = wl.conv_inputs(w)
-    x = torch.from_numpy(inp["x"]).to(dev).to(tdt)
-    k = torch.from_numpy(inp["w"]).to(dev).to(tdt)
-    b = torch.from_numpy(inp["bias"]).to(dev)
-    v = torch.from_numpy(inp["var"]).to(dev)
-    y = torch.empty((w.N, w.CO, w.OH, w.OW), dtype=torch.float32, device=dev)
     dt = ct.dtype_code(tdt)
     args = w.shape_args() + (dt, w.epilogue)
 
@@ -544,67 +658,58 @@ def main():
         ct.check(st, "tune")
         tune_info = {"trials": len(recs), "seconds": round(time.perf_counter() - t0, 2),
                      "best_us": round(best.us, 3)}
-    if gemm is not None:
-        st, cfg, from_cache = ct.ct_gemm_query(gemm.M, gemm.N, gemm.K, dt, w.epilogue)
-    else:
-        st, cfg, from_cache = ct.ct_conv2d_query(*args)
-    ct.check(st, "query")
-    vdesc = ct.variants()[cfg.variant]
 
     # one side stream for warm-up, capture and replay (the library keys its
     # split workspace by stream, so warm-up on this stream allocates it)
     stream = torch.cuda.Stream()
     torch.cuda.set_stream(stream)
-    xp, kp, yp, bp, vp = x.data_ptr(), k.data_ptr(), y.data_ptr(), b.data_ptr(), v.data_ptr()
-    lib = ct.library()
+    if gemm is not None:
+        inp = wl.conv_inputs(w)
+        xg = torch.from_numpy(inp["x"]).to(dev).to(tdt)
+        kg = torch.from_numpy(inp["w"]).to(dev).to(tdt)
+        bg = torch.from_numpy(inp["bias"]).to(dev)
+        vg = torch.from_numpy(inp["var"]).to(dev)
+        yg = torch.empty((w.N, w.CO, w.OH, w.OW), dtype=torch.float32, device=dev)
+        lib = ct.library()
 
-    def step():
-        # the stream current at call time: inside graph capture it is the
-        # capture stream
-        if gemm is not None:
-            st = lib.ct_gemm_fwd(kp, xp, yp, gemm.M, gemm.N, gemm.K, dt, w.epilogue, bp, vp, 1e-5,
+        def step():
+            st = lib.ct_gemm_fwd(kg.data_ptr(), xg.data_ptr(), yg.data_ptr(), gemm.M, gemm.N, gemm.K, dt,
+                                 w.epilogue, bg.data_ptr(), vg.data_ptr(), 1e-5,
                                  torch.cuda.current_stream().cuda_stream)
-        else:
-            st = lib.ct_conv2d_nchw_fwd(xp, kp, yp, *args, bp, vp, 1e-5,
-                                        torch.cuda.current_stream().cuda_stream)
-        if st != 0:
-            raise ct.ConvTileError(st, "fwd")
+            if st != 0:
+                raise ct.ConvTileError(st, "fwd")
 
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    graph = None
-    if not a.eager:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            for _ in range(a.steps):
-                step()
-        torch.cuda.synchronize()
-        graph.replay()  # warm replay
-        torch.cuda.synchronize()
-
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    if graph is not None:
-        graph.replay()
+        st, cfg, from_cache = ct.ct_gemm_query(gemm.M, gemm.N, gemm.K, dt, w.epilogue)
+        ct.check(st, "query")
     else:
+        step, cfg, from_cache = conv_step(w)
+    vdesc = ct.variants()[cfg.variant]
+
+    t0 = time.perf_counter()
+    if a.eager:
+        for _ in range(a.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
         for _ in range(a.steps):
             step()
-    e1.record(stream)
-    torch.cuda.synchronize()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_per_step = e0.elapsed_time(e1) / a.steps
+    else:
+        ms_per_step = time_graph(step, stream, a.steps, a.warmup)
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1)
-    ms_per_step = ms / a.steps
     tflops = w.flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
-    # eager launch rate through the C ABI, for reference
+    # eager launch rate through the C ABI (host dispatch included), for reference
     eager_ms = None
-    if graph is not None:
+    if not a.eager:
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(a.steps):
             step()
@@ -635,7 +740,7 @@ def main():
                    "KH": w.KH, "KW": w.KW, "stride": w.stride, "pad": w.pad,
                    **({"M": gemm.M, "gemm_N": gemm.N, "K": gemm.K} if gemm is not None else {}),
                    "epilogue": w.epilogue, "flops_per_step": w.flops,
-                   "launch": "hip_graph" if graph is not None else "eager",
+                   "launch": "eager" if a.eager else "hip_graph",
                    "kernel": vdesc["name"], "split_k": cfg.split_k, "stages": cfg.stages,
                    "kc": cfg.kc, "config_index": cfg.index, "from_cache": bool(from_cache),
                    "tuning_log": cache_loaded},
@@ -650,6 +755,8 @@ def main():
     }
     if tune_info:
         out["tune"] = tune_info
+    if a.workload is None and not a.no_per_shape:
+        out["per_shape"] = per_shape(a)
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_gemm(gemm, a.cpu_seconds) if gemm is not None
                                else cpu_baseline(w, a.cpu_seconds))

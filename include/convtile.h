@@ -123,7 +123,11 @@ typedef struct ct_tune_record {
 /* ---- convolution ----------------------------------------------------- */
 
 /* Forward convolution with the cached tile config for this shape (or the
- * built-in default when none is cached).  Shapes/layouts as above; `eps` is
+ * built-in default when none is cached; with the environment variable
+ * CT_TUNE=1, a shape with no cached config is first searched with
+ * ct_conv2d_tune on `stream`, once per process -- CT_TUNE_TRIALS bounds the
+ * trials, CT_TUNE_MS sets min_repeat_ms (default 20) -- unless the stream is
+ * capturing).  Shapes/layouts as above; `eps` is
  * used only by CT_EPI_EXP_BIAS_RSQRT.  Errors: CT_ERR_INVALID_ARG for any
  * dimension <= 0, stride <= 0, pad < 0, OH or OW <= 0, NULL x/w/y, unknown
  * dtype/epilogue, or bias/var missing when the epilogue reads them;
@@ -344,17 +348,35 @@ int ct_conv2d_space_entity(int N, int CI, int H, int W, int CO, int KH, int KW,
 /* Enumerate the legal points, time up to `max_trials` of them on `stream`
  * (0 = all legal points), keep the fastest whose output matches the direct
  * reference kernel, store it in the cache and in *best_out.  Timing follows
- * the tutorial's runner: a warm-up, then `repeat` (3) measurements each of at
- * least `min_repeat_ms` milliseconds of back-to-back launches, a per-trial
- * limit of 4 s.  Scratch inputs are allocated and filled on the device by the
- * library.  `records` (may be NULL) receives up to `max_records` trial records
- * and *n_records their count.  Synchronises the stream; may take seconds.
- * Returns CT_ERR_TUNE_FAILED if no candidate ran correctly. */
+ * the TVM tutorial's runner (Step 2): a warm-up, then `repeat` (3)
+ * measurements each of at least `min_repeat_ms` milliseconds of back-to-back
+ * launches, and a per-trial limit of 4 s (CT_TUNE_TIMEOUT_S overrides it),
+ * checked while the launches run: a trial past it records error 6 and issues
+ * no more launches.  Scratch inputs are allocated and filled on the device
+ * by the library.  `records` (may be NULL) receives up to `max_records` trial
+ * records and *n_records their count.
+ * Tuning log (the tutorial's log_to_file): when the environment variable
+ * CT_CACHE_PATH names a file, every trial record is appended to it as one
+ * JSON line when the trial ends (error_no 1/4/6 included), and a search of a
+ * shape first reads the file: points already logged for the shape are not
+ * measured again (resume), and their logged results take part in choosing
+ * the winner; `records` lists only the trials measured by this call.
+ * Synchronises the stream; may take seconds.  Returns CT_ERR_TUNE_FAILED if
+ * no candidate ran correctly, CT_ERR_IO if the log cannot be appended. */
 int ct_conv2d_tune(int N, int CI, int H, int W, int CO, int KH, int KW,
                    int stride, int pad, int dtype, int epilogue,
                    int max_trials, float min_repeat_ms, void* stream,
                    ct_tile_config* best_out,
                    ct_tune_record* records, int max_records, int* n_records);
+
+/* The flat indices ct_conv2d_tune would time for this shape, in order (legal
+ * points by the analytic time estimate, then the illegal ones), leaving out
+ * the points already recorded in the CT_CACHE_PATH log (resume), at most
+ * `max_trials` (0 = all).  Writes up to `max_out` of them to order_out and
+ * their full count to *n_out.  Host-only: launches nothing. */
+int ct_conv2d_tune_order(int N, int CI, int H, int W, int CO, int KH, int KW,
+                         int stride, int pad, int dtype, int epilogue, int max_trials,
+                         long long* order_out, int max_out, int* n_out);
 
 /* Guided search for spaces too large to time exhaustively (the role of the
  * TVM tutorial's cost-model tuner, XGBTuner, in Step 2).  Times at most
@@ -364,7 +386,8 @@ int ct_conv2d_tune(int N, int CI, int H, int W, int CO, int KH, int KW,
  * (ct_ridge_fit, lambda 1e-3, refitted after every batch) plus max(1,
  * batch/4) uniform draws among the untimed configs.  Trials, records, the
  * cache entry and errors as ct_conv2d_tune; CT_ERR_INVALID_ARG also for
- * batch < 1. */
+ * batch < 1.  The CT_CACHE_PATH log is written and resumed from as for
+ * ct_conv2d_tune. */
 int ct_conv2d_tune_guided(int N, int CI, int H, int W, int CO, int KH, int KW,
                           int stride, int pad, int dtype, int epilogue,
                           int max_trials, int batch, unsigned long long seed,

@@ -97,6 +97,7 @@ _SIGS = {
     "ct_conv2d_tune": (_I, _SHAPE + [_I, _F, _P, ctypes.POINTER(ct_tile_config),
                                      ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
     "ct_conv2d_query": (_I, _SHAPE + [ctypes.POINTER(ct_tile_config), ctypes.POINTER(_I)]),
+    "ct_conv2d_tune_order": (_I, _SHAPE + [_I, ctypes.POINTER(_LL), _I, ctypes.POINTER(_I)]),
     "ct_conv2d_tune_guided": (_I, _SHAPE + [_I, _I, ctypes.c_ulonglong, _F, _P, ctypes.POINTER(ct_tile_config),
                                             ctypes.POINTER(ct_tune_record), _I, ctypes.POINTER(_I)]),
     "ct_ridge_fit": (_I, [_P, _P, _I, _I, ctypes.c_double, _P]),
@@ -408,6 +409,20 @@ def ct_init(device: int = 0) -> int:
 
 def ct_plan_misses() -> int:
     return _load().ct_plan_misses()
+
+
+def ct_conv2d_tune_order(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials=0):
+    """(status, [flat indices]) the exhaustive search would time, in order,
+    skipping points already in the CT_CACHE_PATH log."""
+    n = _I(0)
+    st = _load().ct_conv2d_tune_order(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials,
+                                      None, 0, ctypes.byref(n))
+    if st != 0:
+        return st, []
+    buf = (_LL * max(1, n.value))()
+    st = _load().ct_conv2d_tune_order(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials,
+                                      buf, n.value, ctypes.byref(n))
+    return st, list(buf[:n.value])
 
 
 def ct_version() -> str:

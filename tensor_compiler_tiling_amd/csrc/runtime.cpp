@@ -27,6 +27,7 @@
 #include <mutex>
 #include <sstream>
 #include <string>
+#include <thread>
 #include <tuple>
 #include <unordered_map>
 #include <vector>
@@ -925,6 +926,53 @@ ct_tile_config choose(const Shape& s, int* from_cache, bool prepared = false) {
     return c;
 }
 
+}  // namespace
+int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad, int dtype, int epilogue,
+              int max_trials, float min_repeat_ms, void* stream, ct_tile_config* best_out, ct_tune_record* records,
+              int max_records, int* n_records);
+namespace {
+
+// CT_TUNE=1: a launch of a shape with no tuning record first runs the
+// tile-config search on its stream (once per shape in the process; not while
+// the stream is capturing).  CT_TUNE_TRIALS bounds the trials (default: every
+// legal point), CT_TUNE_MS is the minimum milliseconds per repeat (default 20).
+std::mutex g_autotune_mu;
+std::map<std::string, bool> g_autotuned;
+
+void maybe_autotune(const Shape& s, hipStream_t stream) {
+    static const bool on = [] {
+        const char* v = getenv("CT_TUNE");
+        return v && strcmp(v, "1") == 0;
+    }();
+    if (!on) return;
+    {
+        std::lock_guard<std::mutex> lk(g_cache_mu);
+        if (g_cache.count(s.key())) return;
+    }
+    {
+        std::lock_guard<std::mutex> lk(g_autotune_mu);
+        if (g_autotuned.count(s.key())) return;
+        g_autotuned[s.key()] = true;
+    }
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+        (void)hipGetLastError();
+        return;
+    }
+    const char* t = getenv("CT_TUNE_TRIALS");
+    const char* m = getenv("CT_TUNE_MS");
+    const int trials = t ? std::max(0, atoi(t)) : 0;
+    const float ms = m && atof(m) > 0 ? (float)atof(m) : 20.0f;
+    ct_tile_config best{};
+    char saved[sizeof(g_last_error)];
+    memcpy(saved, g_last_error, sizeof(saved));
+    if (tune_impl(s.N, s.CI, s.H, s.W, s.CO, s.KH, s.KW, s.stride, s.pad, s.dtype, s.epilogue, trials, ms, stream,
+                  &best, nullptr, 0, nullptr) != CT_OK) {
+        if (log_debug()) fprintf(stderr, "[convtile tune] automatic search failed: %s\n", g_last_error);
+        memcpy(g_last_error, saved, sizeof(saved));  // the launch goes on with the default config
+    }
+}
+
 // ------------------------------------------------------------ launch plans --
 // The resolved launch of fwd per (device, shape): the config it uses, with
 // the legality check's resolution (grid, window rows, LDS and scratch
@@ -961,8 +1009,8 @@ std::unordered_map<PlanKey, Plan, PlanKeyHash> g_plans;
 std::atomic<long long> g_plan_misses{0};
 
 // The plan of fwd for shape s on device dev (set up); `prepared`: the plan
-// of the prepared-filter entry point.
-int get_plan(int dev, const Shape& s, Plan* out, bool prepared = false) {
+// of the prepared-filter entry point.  `stream`: the launch's (for CT_TUNE).
+int get_plan(int dev, const Shape& s, Plan* out, hipStream_t stream, bool prepared = false) {
     const PlanKey k{{dev, s.N, s.CI, s.H, s.W, s.CO, s.KH, s.KW, s.stride, s.pad, s.dtype, s.epilogue,
                      prepared ? 1 : 0}};
     const unsigned gen = g_cache_gen.load(std::memory_order_acquire);
@@ -975,6 +1023,7 @@ int get_plan(int dev, const Shape& s, Plan* out, bool prepared = false) {
         }
     }
     g_plan_misses.fetch_add(1, std::memory_order_relaxed);
+    maybe_autotune(s, stream);
     Plan pl;
     pl.gen = gen;
     pl.cfg = choose(s, &pl.from_cache, prepared);
@@ -1032,7 +1081,7 @@ int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y, int N, int CI, in
     st = ensure_device(hs, &dev);
     if (st != CT_OK) return st;
     Plan pl;
-    st = get_plan(dev, s, &pl);
+    st = get_plan(dev, s, &pl, hs);
     if (st != CT_OK) return st;
     if (pl.direct) return launch_direct(s, x, w, y, bias, var, eps, hs);
     LaunchScratch sc;
@@ -1054,7 +1103,7 @@ int ct_conv2d_nchw_fwd_noalloc(const void* x, const void* w, float* y, int N, in
     st = ensure_device(hs, &dev);
     if (st != CT_OK) return st;
     Plan pl;
-    st = get_plan(dev, s, &pl);
+    st = get_plan(dev, s, &pl, hs);
     if (st != CT_OK) return st;
     if (pl.direct) return launch_direct(s, x, w, y, bias, var, eps, hs);
     LaunchScratch sc;
@@ -1095,7 +1144,7 @@ int ct_conv2d_nchw_fwd_prepared(const void* x, const void* wp, float* y, int N, 
     st = ensure_device(hs, &dev);
     if (st != CT_OK) return st;
     Plan pl;
-    st = get_plan(dev, s, &pl, true);
+    st = get_plan(dev, s, &pl, hs, true);
     if (st != CT_OK) return st;
     LaunchScratch sc;
     st = stream_scratch(dev, pl.cfg, pl.r, launch_aux_bytes(s, pl.r, true), hs, &sc);
@@ -1482,8 +1531,30 @@ struct TuneBench {
     float min_repeat_ms = 0;
     long long ny = 0;
     std::map<long long, int> inject;
-    static constexpr double kTimeout = 4.0;  // seconds per trial
+    double timeout_s = 4.0;  // per trial, as the tutorial's runner; CT_TUNE_TIMEOUT_S overrides
     static constexpr int kRepeat = 3;
+
+    // Wait for `ev` while the trial stays within its time limit: the limit
+    // is checked while the launches run, not only after them.  On a timeout
+    // no more launches of the trial are issued and the ones in flight are
+    // drained (they cannot be cancelled) before the next trial.
+    int wait_event(hipEvent_t ev, std::chrono::steady_clock::time_point t_start) {
+        while (true) {
+            const hipError_t q = hipEventQuery(ev);
+            if (q == hipSuccess) return CT_TRIAL_OK;
+            if (q != hipErrorNotReady) {
+                (void)hipGetLastError();
+                return CT_TRIAL_RUNTIME;
+            }
+            const double wall = std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
+            if (wall > timeout_s) {
+                (void)hipStreamSynchronize(hs);
+                (void)hipGetLastError();
+                return CT_TRIAL_TIMEOUT;
+            }
+            std::this_thread::sleep_for(std::chrono::microseconds(20));
+        }
+    }
 
     ~TuneBench() {
         if (ev0) (void)hipEventDestroy(ev0);
@@ -1521,6 +1592,10 @@ struct TuneBench {
         if ((e = hipEventCreate(&ev0)) != hipSuccess) return hip_fail(e, "hipEventCreate");
         if ((e = hipEventCreate(&ev1)) != hipSuccess) return hip_fail(e, "hipEventCreate");
         inject = injected_errors();
+        if (const char* t = getenv("CT_TUNE_TIMEOUT_S")) {
+            const double v = atof(t);
+            if (v > 0.0) timeout_s = v;
+        }
         return CT_OK;
     }
 
@@ -1543,7 +1618,15 @@ struct TuneBench {
             // poison the output so a kernel that writes nothing cannot pass
             e = hipMemsetAsync(sc.y, 0xff, ny * 4, hs);
             st = (e == hipSuccess) ? launch_tiled(s, c, sc.x, sc.w, sc.y, sc.bias, sc.var, eps, hs) : CT_ERR_HIP;
-            if (st == CT_OK && (e = hipStreamSynchronize(hs)) != hipSuccess) st = CT_ERR_HIP;
+            if (st == CT_OK) {
+                if (hipEventRecord(ev1, hs) != hipSuccess) {
+                    st = CT_ERR_HIP;
+                } else {
+                    const int w = wait_event(ev1, t_start);
+                    if (w == CT_TRIAL_TIMEOUT) err = CT_TRIAL_TIMEOUT;
+                    if (w != CT_TRIAL_OK) st = CT_ERR_HIP;
+                }
+            }
             if (st == CT_OK) {
                 unsigned bad = 0;
                 if (hipMemsetAsync(sc.bad, 0, 4, hs) != hipSuccess ||
@@ -1553,7 +1636,7 @@ struct TuneBench {
                     st = CT_ERR_TUNE_FAILED;
             }
             if (st != CT_OK) {
-                err = CT_TRIAL_RUNTIME;
+                if (err == CT_TRIAL_OK) err = CT_TRIAL_RUNTIME;
             } else {
                 // calibrate the launch count so a repeat lasts >= min_repeat_ms
                 long long number = 1;
@@ -1563,17 +1646,12 @@ struct TuneBench {
                     for (long long i = 0; i < number && st == CT_OK; ++i)
                         st = launch_tiled(s, c, sc.x, sc.w, sc.y, sc.bias, sc.var, eps, hs);
                     (void)hipEventRecord(ev1, hs);
-                    if (st != CT_OK || hipEventSynchronize(ev1) != hipSuccess) {
-                        err = CT_TRIAL_RUNTIME;
+                    const int wv = st == CT_OK ? wait_event(ev1, t_start) : CT_TRIAL_RUNTIME;
+                    if (wv != CT_TRIAL_OK) {
+                        err = wv;
                         break;
                     }
                     (void)hipEventElapsedTime(&ms, ev0, ev1);
-                    const double wall =
-                        std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
-                    if (wall > kTimeout) {
-                        err = CT_TRIAL_TIMEOUT;
-                        break;
-                    }
                     if (ms >= min_repeat_ms || number >= (1LL << 20)) break;
                     const double want = ms > 0.0f ? 1.25 * min_repeat_ms / ms * number : 2.0 * number;
                     number = std::max<long long>(2 * number, (long long)std::ceil(want));
@@ -1584,16 +1662,14 @@ struct TuneBench {
                     for (long long i = 0; i < number && st == CT_OK; ++i)
                         st = launch_tiled(s, c, sc.x, sc.w, sc.y, sc.bias, sc.var, eps, hs);
                     (void)hipEventRecord(ev1, hs);
-                    if (st != CT_OK || hipEventSynchronize(ev1) != hipSuccess) {
-                        err = CT_TRIAL_RUNTIME;
+                    const int wv = st == CT_OK ? wait_event(ev1, t_start) : CT_TRIAL_RUNTIME;
+                    if (wv != CT_TRIAL_OK) {
+                        err = wv;
                         break;
                     }
                     (void)hipEventElapsedTime(&ms, ev0, ev1);
                     rec->costs_us[rep] = 1000.0f * ms / (float)number;
                     rec->n_costs = rep + 1;
-                    const double wall =
-                        std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
-                    if (wall > kTimeout) err = CT_TRIAL_TIMEOUT;
                 }
             }
         }
@@ -1611,36 +1687,132 @@ struct TuneBench {
     }
 };
 
-// Keep the best of the timed records and store the winner in the cache (and
-// in the file named by CT_CACHE_PATH).
-int tune_finish(const Shape& s, const std::vector<ct_tune_record>& recs, ct_tile_config* best_out,
-                ct_tune_record* records, int max_records, int* n_records) {
+// The tuning log named by CT_CACHE_PATH (the TVM tutorial's Step 2 writes
+// every measure record to a log file as it is measured, log_to_file): one
+// JSON line per trial, appended and flushed as each trial ends, so that a
+// search that stops part way leaves every finished trial in the file.  A
+// search of a shape resumes from it: the (variant, split) points already
+// logged for the shape's key are not measured again, and their logged
+// outcomes take part in choosing the winner.
+struct TuneLog {
+    std::string path;
+    std::ofstream out;
+    // logged trials of this shape: (variant name, split_k, stages, kc) -> record
+    std::map<std::tuple<std::string, int, int, int>, ct_tune_record> done;
+
+    static std::tuple<std::string, int, int, int> point(const ct_tile_config& c) {
+        return std::make_tuple(std::string(variants()[c.variant].desc.name), c.split_k, c.stages, c.kc);
+    }
+
+    // Read the log's records of shape s (when CT_CACHE_PATH is set).
+    void open(const Shape& s) {
+        const char* p = getenv("CT_CACHE_PATH");
+        if (!p || !*p) return;
+        path = p;
+        std::ifstream in(path);
+        std::string line;
+        const Space sp = space_of(s);
+        while (in && std::getline(in, line)) {
+            std::map<std::string, std::string> kv;
+            if (!parse_record(line, &kv) || kv["key"] != s.key()) continue;
+            long long v[4];
+            const char* need[] = {"split_k", "stages", "kc", "error_no"};
+            bool ok = true;
+            for (int i = 0; i < 4 && ok; ++i) ok = kv.count(need[i]) && to_int(kv[need[i]], &v[i]);
+            const int vid = ok ? find_variant(kv["variant"].c_str()) : -1;
+            if (vid < 0) continue;
+            ct_tune_record r{};
+            r.cfg.variant = vid;
+            r.cfg.split_k = (int)v[0];
+            r.cfg.stages = (int)v[1];
+            r.cfg.kc = (int)v[2];
+            r.cfg.index = encode(sp, r.cfg);
+            r.error_no = (int)v[3];
+            r.cfg.error_no = r.error_no;
+            r.cfg.us = (float)atof(kv["us"].c_str());
+            // costs "[a,b,c]"
+            const std::string cs = kv["costs_us"];
+            size_t i = cs.find('[');
+            while (i != std::string::npos && r.n_costs < 3) {
+                char* end = nullptr;
+                const double c = strtod(cs.c_str() + i + 1, &end);
+                if (end == cs.c_str() + i + 1) break;
+                r.costs_us[r.n_costs++] = (float)c;
+                i = cs.find(',', i + 1);
+            }
+            r.all_cost_s = atof(kv["all_cost"].c_str());
+            r.timestamp = atof(kv["timestamp"].c_str());
+            if (r.cfg.index < 0) continue;  // not a point of this shape's space
+            done[point(r.cfg)] = r;
+        }
+        out.open(path, std::ios::app);
+    }
+
+    bool logged(const ct_tile_config& c) const { return done.count(point(c)) != 0; }
+
+    int append(const Shape& s, const ct_tune_record& r) {
+        if (path.empty()) return CT_OK;
+        if (!out) return fail(CT_ERR_IO, "cannot append to %s", path.c_str());
+        out << json_record(s, r.cfg, variants()[r.cfg.variant].desc.name, r.costs_us, r.n_costs, r.all_cost_s,
+                           r.timestamp)
+            << "\n";
+        out.flush();
+        if (!out) return fail(CT_ERR_IO, "write to %s failed", path.c_str());
+        return CT_OK;
+    }
+};
+
+// Keep the best of the records (this search's and the ones it resumed from
+// the log) and store the winner in the in-memory cache.
+int tune_finish(const Shape& s, const std::vector<ct_tune_record>& recs, const TuneLog& log,
+                ct_tile_config* best_out, ct_tune_record* records, int max_records, int* n_records) {
     ct_tile_config best{};
     best.variant = -1;
-    for (size_t k = 0; k < recs.size(); ++k) {
-        const ct_tune_record& r = recs[k];
-        if ((int)k < max_records) records[k] = r;
-        if (r.error_no != CT_TRIAL_OK || r.n_costs != TuneBench::kRepeat) continue;
+    auto consider = [&](const ct_tune_record& r) {
+        if (r.error_no != CT_TRIAL_OK || r.n_costs != TuneBench::kRepeat) return;
         if (best.variant < 0 || r.cfg.us < best.us || (r.cfg.us == best.us && r.cfg.index < best.index))
             best = r.cfg;
+    };
+    for (size_t k = 0; k < recs.size(); ++k) {
+        if ((int)k < max_records) records[k] = recs[k];
+        consider(recs[k]);
     }
+    for (const auto& kv : log.done) consider(kv.second);
     if (n_records) *n_records = std::min((int)recs.size(), max_records);
     if (best.variant < 0) return fail(CT_ERR_TUNE_FAILED, "no candidate ran correctly");
     *best_out = best;
     float costs[1] = {best.us};
     const std::string line = json_record(s, best, variants()[best.variant].desc.name, costs, 1, 0.0, now_s());
-    {
-        std::lock_guard<std::mutex> lk(g_cache_mu);
-        g_cache[s.key()] = CacheEntry{variants()[best.variant].desc.name, best, line};
-        g_cache_gen.fetch_add(1, std::memory_order_acq_rel);
-    }
-    const char* path = getenv("CT_CACHE_PATH");
-    if (path && *path) {
-        std::ofstream f(path, std::ios::app);
-        if (!f) return fail(CT_ERR_IO, "cannot append to %s", path);
-        f << line << "\n";
-    }
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    g_cache[s.key()] = CacheEntry{variants()[best.variant].desc.name, best, line};
+    g_cache_gen.fetch_add(1, std::memory_order_acq_rel);
     return CT_OK;
+}
+
+// The order in which the exhaustive search times a shape's points: legal
+// points by predicted time, then the illegal ones (recorded as error 1
+// without a launch), leaving out the points the log already holds, at most
+// max_trials of them (0 = all).
+std::vector<long long> exhaustive_order(const Shape& s, int max_trials, const TuneLog& log) {
+    Space sp = space_of(s);
+    std::vector<std::pair<double, long long>> order;
+    std::vector<long long> illegal;
+    for (long long i = 0; i < sp.size(); ++i) {
+        ct_tile_config c;
+        decode(sp, i, &c);
+        if (log.logged(c)) continue;
+        Resolved r;
+        if (legal(s, c, &r, nullptr))
+            order.push_back({predict_us(s, c, r), i});
+        else
+            illegal.push_back(i);
+    }
+    std::stable_sort(order.begin(), order.end());
+    std::vector<long long> trials;
+    for (auto& o : order) trials.push_back(o.second);
+    for (long long i : illegal) trials.push_back(i);
+    if (max_trials > 0 && (long long)trials.size() > max_trials) trials.resize(max_trials);
+    return trials;
 }
 
 int tune_args(int max_trials, float min_repeat_ms, ct_tile_config* best_out, ct_tune_record* records,
@@ -1672,24 +1844,9 @@ int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, i
     st = tune_args(max_trials, min_repeat_ms, best_out, records, max_records, n_records);
     if (st != CT_OK) return st;
 
-    // search order: legal points by predicted time, then illegal points
-    Space sp = space_of(s);
-    std::vector<std::pair<double, long long>> order;
-    std::vector<long long> illegal;
-    for (long long i = 0; i < sp.size(); ++i) {
-        ct_tile_config c;
-        decode(sp, i, &c);
-        Resolved r;
-        if (legal(s, c, &r, nullptr))
-            order.push_back({predict_us(s, c, r), i});
-        else
-            illegal.push_back(i);
-    }
-    std::stable_sort(order.begin(), order.end());
-    std::vector<long long> trials;
-    for (auto& o : order) trials.push_back(o.second);
-    for (long long i : illegal) trials.push_back(i);
-    if (max_trials > 0 && (long long)trials.size() > max_trials) trials.resize(max_trials);
+    TuneLog log;
+    log.open(s);
+    const std::vector<long long> trials = exhaustive_order(s, max_trials, log);
 
     TuneBench tb;
     st = tb.init(s, stream, min_repeat_ms);
@@ -1700,8 +1857,27 @@ int tune_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, i
         tb.trial(idx, &rec);
         recs.push_back(rec);
         log_trial((int)recs.size(), rec);
+        st = log.append(s, rec);
+        if (st != CT_OK) return st;
     }
-    return tune_finish(s, recs, best_out, records, max_records, n_records);
+    return tune_finish(s, recs, log, best_out, records, max_records, n_records);
+}
+
+int tune_order_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad, int dtype,
+                    int epilogue, int max_trials, long long* order_out, int max_out, int* n_out) {
+    Shape s;
+    int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, &s);
+    if (st != CT_OK) return st;
+    if (max_trials < 0) return fail(CT_ERR_INVALID_ARG, "max_trials must be >= 0");
+    if (!n_out || max_out < 0 || (max_out > 0 && !order_out))
+        return fail(CT_ERR_INVALID_ARG, "order_out / max_out / n_out mismatch");
+    TuneLog log;
+    log.open(s);
+    const std::vector<long long> trials = exhaustive_order(s, max_trials, log);
+    const int n = (int)std::min<size_t>(trials.size(), (size_t)max_out);
+    for (int i = 0; i < n; ++i) order_out[i] = trials[i];
+    *n_out = (int)trials.size();
+    return CT_OK;
 }
 
 // ------------------------------------------------------- guided search --
@@ -1865,33 +2041,40 @@ int tune_guided_impl(int N, int CI, int H, int W, int CO, int KH, int KW, int st
     if (st != CT_OK) return st;
     if (batch < 1) return fail(CT_ERR_INVALID_ARG, "batch must be >= 1");
     Space sp = space_of(s);
+    TuneLog log;
+    log.open(s);
     std::vector<long long> idx;
     std::vector<double> feats;
     for (long long i = 0; i < sp.size(); ++i) {
         ct_tile_config c;
         decode(sp, i, &c);
         Resolved r;
-        if (!legal(s, c, &r, nullptr)) continue;
+        if (log.logged(c) || !legal(s, c, &r, nullptr)) continue;
         idx.push_back(i);
         feats.resize(feats.size() + kFeatures);
         config_features(s, c, r, feats.data() + feats.size() - kFeatures);
     }
-    if (idx.empty()) return fail(CT_ERR_TUNE_FAILED, "no legal config for this shape");
+    if (idx.empty() && log.done.empty()) return fail(CT_ERR_TUNE_FAILED, "no legal config for this shape");
     TuneBench tb;
     st = tb.init(s, stream, min_repeat_ms);
     if (st != CT_OK) return st;
     std::vector<ct_tune_record> recs;
     const int n = (int)idx.size();
     const int budget = max_trials == 0 ? n : std::min(max_trials, n);
-    (void)guided_search(n, kFeatures, feats.data(), budget, batch, std::max(1, batch / 4), seed, 1e-3,
-                        [&](int i) -> double {
-                            ct_tune_record rec;
-                            tb.trial(idx[i], &rec);
-                            recs.push_back(rec);
-                            log_trial((int)recs.size(), rec);
-                            return rec.error_no == CT_TRIAL_OK ? (double)rec.cfg.us : -1.0;
-                        });
-    return tune_finish(s, recs, best_out, records, max_records, n_records);
+    int log_st = CT_OK;
+    if (n > 0)
+        (void)guided_search(n, kFeatures, feats.data(), budget, batch, std::max(1, batch / 4), seed, 1e-3,
+                            [&](int i) -> double {
+                                ct_tune_record rec;
+                                tb.trial(idx[i], &rec);
+                                recs.push_back(rec);
+                                log_trial((int)recs.size(), rec);
+                                const int a = log.append(s, rec);
+                                if (a != CT_OK) log_st = a;
+                                return rec.error_no == CT_TRIAL_OK ? (double)rec.cfg.us : -1.0;
+                            });
+    if (log_st != CT_OK) return log_st;
+    return tune_finish(s, recs, log, best_out, records, max_records, n_records);
 }
 
 }  // namespace ct
@@ -1930,6 +2113,13 @@ int ct_conv2d_tune_guided(int N, int CI, int H, int W, int CO, int KH, int KW, i
 }
 
 }  // extern "C"
+
+extern "C" int ct_conv2d_tune_order(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad,
+                                    int dtype, int epilogue, int max_trials, long long* order_out, int max_out,
+                                    int* n_out) {
+    return ct::tune_order_impl(N, CI, H, W, CO, KH, KW, stride, pad, dtype, epilogue, max_trials, order_out,
+                               max_out, n_out);
+}
 
 extern "C" int ct_conv2d_tune(int N, int CI, int H, int W, int CO, int KH, int KW, int stride,
                               int pad, int dtype, int epilogue, int max_trials, float min_repeat_ms,

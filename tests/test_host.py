@@ -458,3 +458,67 @@ def test_prepared_filter_bytes():
     assert ct.ct_conv2d_filter_prepared_bytes(4096, 4096, 1, 1, ct.CT_F16) == 2 * 4096 * 4096
     assert ct.ct_conv2d_filter_prepared_bytes(8, 8, 3, 3, ct.CT_F32) == ct.CT_ERR_INVALID_ARG
     assert ct.ct_conv2d_filter_prepared_bytes(0, 8, 3, 3, ct.CT_F16) == ct.CT_ERR_INVALID_ARG
+
+
+def _log_line(shape, variant_name, split, stages, kc, error_no=0, us=5.0):
+    N, CI, H, W, CO, KH, KW, s, p, dt, epi = shape
+    key = f"{N},{CI},{H},{W},{CO},{KH},{KW},{s},{p},{dt},{epi},gfx950,v1"
+    return json.dumps({"key": key, "N": N, "CI": CI, "H": H, "W": W, "CO": CO, "KH": KH, "KW": KW,
+                       "stride": s, "pad": p, "dtype": dt, "epilogue": epi, "arch": "gfx950",
+                       "variant": variant_name, "split_k": split, "stages": stages, "kc": kc, "index": -1,
+                       "us": us, "error_no": error_no, "costs_us": [us, us, us], "all_cost": 0.1,
+                       "timestamp": 1.0})
+
+
+def test_tuning_log_resume_skips_logged_points(tmp_path, monkeypatch):
+    """The exhaustive search's trial order, then the same order with a log that
+    already holds some of the shape's points (successful, failed and illegal
+    outcomes, as the tutorial's log does): the logged points are left out and
+    the rest keep their order; lines of other shapes and malformed lines are
+    ignored."""
+    shape = (1, 512, 7, 7, 512, 3, 3, 1, 1, ct.CT_F32, ct.CT_EPI_NONE)
+    monkeypatch.delenv("CT_CACHE_PATH", raising=False)
+    st, full = ct.ct_conv2d_tune_order(*shape)
+    assert st == 0 and len(full) == ct.ct_conv2d_space_size(*shape)
+    assert len(set(full)) == len(full)
+    logged = full[:5] + full[-2:]  # the first legal points and two illegal ones
+    lines = []
+    for i, idx in enumerate(logged):
+        st, cfg, _ = ct.ct_conv2d_space_entity(*shape, idx)
+        assert st == 0
+        name = ct.variants()[cfg.variant]["name"]
+        lines.append(_log_line(shape, name, cfg.split_k, cfg.stages, cfg.kc, error_no=(0, 4, 6, 1)[i % 4]))
+    other = (1, 64, 14, 14, 64, 3, 3, 1, 1, ct.CT_F32, ct.CT_EPI_NONE)
+    st, cfg0, _ = ct.ct_conv2d_space_entity(*shape, full[5])
+    lines.append(_log_line(other, ct.variants()[cfg0.variant]["name"], cfg0.split_k, cfg0.stages, cfg0.kc))
+    lines.append("{not json")
+    log = tmp_path / "tune.jsonl"
+    log.write_text("\n".join(lines) + "\n")
+    monkeypatch.setenv("CT_CACHE_PATH", str(log))
+    st, resumed = ct.ct_conv2d_tune_order(*shape)
+    assert st == 0
+    assert resumed == [i for i in full if i not in set(logged)]
+    st, first3 = ct.ct_conv2d_tune_order(*shape, max_trials=3)
+    assert st == 0 and first3 == resumed[:3]
+
+
+def test_tuning_log_loads_the_fastest_successful_record(tmp_path):
+    """A log holding every trial of a search (failed ones included) loads as
+    one cache record per shape: the fastest successful one."""
+    shape = (1, 512, 7, 7, 512, 3, 3, 1, 1, ct.CT_F32, ct.CT_EPI_NONE)
+    st, full = ct.ct_conv2d_tune_order(*shape)
+    pts = []
+    for idx in full[:6]:
+        st, cfg, legal = ct.ct_conv2d_space_entity(*shape, idx)
+        assert legal
+        pts.append(cfg)
+    lines = [_log_line(shape, ct.variants()[c.variant]["name"], c.split_k, c.stages, c.kc,
+                       error_no=e, us=u) for c, e, u in zip(pts, (0, 0, 6, 0, 4, 0), (9.0, 7.5, 1.0, 8.0, 0.5, 7.75))]
+    log = tmp_path / "all.jsonl"
+    log.write_text("\n".join(lines) + "\n")
+    ct.ct_cache_clear()
+    assert ct.ct_cache_load(str(log)) == 0 and ct.ct_cache_size() == 1
+    st, cfg, from_cache = ct.ct_conv2d_query(*shape)
+    assert from_cache == 1 and (cfg.variant, cfg.split_k, cfg.stages, cfg.kc) == (
+        pts[1].variant, pts[1].split_k, pts[1].stages, pts[1].kc)
+    ct.ct_cache_clear()
