@@ -13,7 +13,7 @@ host through the C ABI (host dispatch included).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--eager]
                     [--tune] [--cache PATH | --no-cache] [--no-cpu-baseline]
-                    [--no-per-shape] [--calibrate-copy]
+                    [--prepared] [--no-per-shape] [--calibrate-copy]
 
 The tile config comes from the tuning log shipped with the package (the
 search's recorded winners, loaded with ct_cache_load) unless --no-cache or
@@ -132,6 +132,8 @@ def _parse():
     ap.add_argument("--tune-trials", type=int, default=0)
     ap.add_argument("--tune-ms", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prepared", action="store_true",
+                    help="half-precision convolution: time the prepared-filter entry point")
     ap.add_argument("--no-per-shape", action="store_true",
                     help="default workload only: leave out the per-shape list of the other rows")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -682,7 +684,10 @@ def main():
         st, cfg, from_cache = ct.ct_gemm_query(gemm.M, gemm.N, gemm.K, dt, w.epilogue)
         ct.check(st, "query")
     else:
-        step, cfg, from_cache = conv_step(w)
+        if a.prepared and w.dtype == "f32":
+            print("--prepared applies to half-precision layers only", file=sys.stderr)
+            sys.exit(2)
+        step, cfg, from_cache = conv_step(w, prepared=a.prepared)
     vdesc = ct.variants()[cfg.variant]
 
     t0 = time.perf_counter()
@@ -741,6 +746,7 @@ def main():
                    **({"M": gemm.M, "gemm_N": gemm.N, "K": gemm.K} if gemm is not None else {}),
                    "epilogue": w.epilogue, "flops_per_step": w.flops,
                    "launch": "eager" if a.eager else "hip_graph",
+                   **({"filter": "prepared"} if a.prepared else {}),
                    "kernel": vdesc["name"], "split_k": cfg.split_k, "stages": cfg.stages,
                    "kc": cfg.kc, "config_index": cfg.index, "from_cache": bool(from_cache),
                    "tuning_log": cache_loaded},

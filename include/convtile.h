@@ -147,8 +147,9 @@ int ct_conv2d_nchw_fwd(const void* x, const void* w, float* y,
  *
  *   wp[co][g][t][j] = w[co][8g + j][t]   (t = ky*KW + kx; 0 when 8g + j >= CI)
  *
- * wp is [CO][ceil(CI/8)][KH*KW][8] halves, ct_conv2d_filter_prepared_bytes
- * bytes.  ct_conv2d_nchw_fwd reorders the caller's filter into its scratch
+ * wp is [CO][CI64/8][KH*KW][8] halves with CI64 = CI rounded up to a multiple
+ * of 64 (every stage of the kernels' reduction then lies inside a row),
+ * ct_conv2d_filter_prepared_bytes bytes.  ct_conv2d_nchw_fwd reorders the caller's filter into its scratch
  * on every call (one small kernel before the convolution); a caller whose
  * filter does not change between calls (inference) prepares it once with
  * ct_conv2d_prepare_filter (asynchronous on `stream`, wp caller-owned device

@@ -95,8 +95,9 @@ const IgemmVariant* igemm_f32_skt_variants(int* count);
 const IgemmVariant* igemm_f16_variants(int* count);
 const IgemmVariant* igemm_f16v2_variants(int* count);
 
-// Half-precision prepared filter: wp [CO][ceil(CI/8)][T][8] = w [CO][CI][T]
-// regrouped into 16-byte records of 8 channels at one tap, zeros past CI.
+// Half-precision prepared filter: wp [CO][CI64/8][T][8] = w [CO][CI][T]
+// regrouped into 16-byte records of 8 channels at one tap, zeros past CI
+// (CI64 = CI rounded up to 64).
 hipError_t h2_prepare_filter(const void* w, void* wp, int CO, int CI, int T, hipStream_t stream);
 
 // Direct (one lane per output) reference kernel.

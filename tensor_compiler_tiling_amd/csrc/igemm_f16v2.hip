@@ -7,13 +7,14 @@
 // lane.  The reduction of a stage (KC channels x 9 taps) is ordered in groups
 // of 8 channels at one tap, g = tap * (KC/8) + channel/8, and both operands
 // sit channel-fastest in LDS, so a fragment is one 16-byte LDS read:
-//   filter tile  [m][g][8]           window  [pixel][channel]
+//   filter tile  [m][cg][tap][8]     window  [pixel][channel]
 // What differs from the first form is where the reordering happens:
 //  - the filter is reordered by a small kernel into the prepared layout
-//    [CO][CI8/8][T][8] (CI8 = CI rounded up to 8, zeros past CI): 8 channels
-//    at one tap per 16 bytes, so one stage of one filter row (KC/8 groups x T
-//    taps) is 9*KC contiguous halves, whatever KC is, and staging the filter
-//    tile is a stream of 16-byte copies with no arithmetic.  A caller with a
+//    [CO][CI64/8][T][8] (CI64 = CI rounded up to 64, zeros past CI): 8
+//    channels at one tap per 16 bytes, so one stage of one filter row (KC/8
+//    groups x T taps, KC = 16, 32 or 64, a divisor of 64) is 9*KC contiguous
+//    halves inside the row, whatever KC is, and staging the filter tile is a
+//    stream of 16-byte copies with no arithmetic and no range checks.  A caller with a
 //    static filter prepares it once (ct_conv2d_prepare_filter); otherwise
 //    each launch reorders into its scratch first;
 //  - the window is staged with vector loads of PX consecutive pixels of one
@@ -81,17 +82,19 @@ __device__ __forceinline__ uint4v tap_record(const uint4v* in, int t) {
     return o;
 }
 
-// w [CO][CI][T] -> wp [CO][CI8/8][T][8], one thread per (row, 8-channel group)
-// unit: T 16-byte loads of the unit's contiguous run, T 16-byte records out.
-// Needs CI % 8 == 0 and a 16-byte aligned w.
+// w [CO][CI][T] -> wp [CO][CGP][T][8], one thread per (row, 8-channel group)
+// unit: T 16-byte loads of the unit's contiguous run, T 16-byte records out
+// (zeros for the groups past CI).  Needs CI % 8 == 0 and a 16-byte aligned w.
 template <int T>
-__global__ __launch_bounds__(256) void h2_prepare_vec_kernel(const uint4v* __restrict__ w, uint4v* __restrict__ wp,
-                                                             long long units) {
-    const long long u = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (u >= units) return;
+__global__ __launch_bounds__(64) void h2_prepare_vec_kernel(const uint4v* __restrict__ w, uint4v* __restrict__ wp,
+                                                            int CO, int CG, int CGP) {
+    const long long u = (long long)blockIdx.x * 64 + threadIdx.x;  // unit (co, g), g < CGP
+    if (u >= (long long)CO * CGP) return;
+    const long long co = u / CGP;
+    const int g = (int)(u - co * CGP);
     uint4v in[T];
 #pragma unroll
-    for (int i = 0; i < T; ++i) in[i] = w[u * T + i];
+    for (int i = 0; i < T; ++i) in[i] = g < CG ? w[(co * CG + g) * T + i] : uint4v{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int t = 0; t < T; ++t) wp[u * T + t] = T == 1 ? in[0] : tap_record<T>(in, t);
 }
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(256) void h2_prepare_vec_kernel(const uint4v* __res
 // The same for any CI and alignment, one element at a time.
 __global__ __launch_bounds__(256) void h2_prepare_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wp,
                                                          int CO, int CI, int T) {
-    const int CG8 = (CI + 7) / 8;
+    const int CG8 = (CI + 63) / 64 * 8;  // groups of a prepared row
     const long long total = (long long)CO * CG8 * T * 8;
     for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long long)gridDim.x * 256) {
         const int j = (int)(i & 7);
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     const uint16_t* __restrict__ xg = static_cast<const uint16_t*>(p.x);
     // the prepared filter: the caller's (p.w) or this launch's copy (p.aux)
     const uint16_t* __restrict__ wpk = static_cast<const uint16_t*>(p.aux ? p.aux : p.w);
-    const int CG8 = (p.CI + 7) / 8;       // 8-channel groups of a prepared filter row
+    const int CG8 = (p.CI + 63) / 64 * 8;  // 8-channel groups of a prepared filter row
     const int NS = (p.CI + KC - 1) / KC;  // stages of the whole reduction
 
     // ---- per-lane B columns --------------------------------------------------
@@ -319,26 +322,21 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     }
 
     // ---- staging tasks (fixed for the kernel) ----------------------------------
-    // filter chunk q = (m, r): 16 bytes of row co0+m, chunk r = cg*T + tap
-    // of a stage in the prepared layout (contiguous in r), LDS record g =
-    // tap*CG + cg
+    // filter chunk q = (m, r): 16 bytes of row co0+m, record r = cg*T + tap of
+    // a stage, in the prepared row's order: a wave's reads and its LDS writes
+    // are both consecutive 16-byte pieces
     int wsrc[WPT];  // halves, without the stage term; -1: no chunk
     int wdst[WPT];
-    int wcg[WPT];   // the chunk's channel group within a stage
 #pragma unroll
     for (int j = 0; j < WPT; ++j) {
         const int q = tid + j * NT;
         wsrc[j] = -1;
         wdst[j] = 0;
-        wcg[j] = 0;
         if (q < C::WCH) {
             const int m = q / G;
             const int r = q - m * G;
-            const int cg = r / T;
-            const int tap = r - cg * T;
             wsrc[j] = (co0 + m) * CG8 * (T * 8) + r * 8;
-            wdst[j] = m * WST + (tap * CG + cg) * 8;
-            wcg[j] = cg;
+            wdst[j] = m * WST + r * 8;
         }
     }
     // window task q = (cg, window row r, run u): 8 channels x PX pixels
@@ -409,9 +407,12 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
         uint4v a[2][RM], bf[2][RN];
         auto frag = [&](int s, uint4v (&ar)[RM], uint4v (&br)[RN]) {
 #pragma unroll
+            // groups 2s and 2s+1 of the step (tap-major) are records
+            // (cg*T + tap) of the filter tile: channel groups cg and cg+1 of
+            // one tap, T records apart
             for (int rm = 0; rm < RM; ++rm)
-                ar[rm] = *reinterpret_cast<const uint4v*>(Wb + ((wm * RM + rm) * 32 + lj) * WST +
-                                                          (2 * s + lh) * 8);
+                ar[rm] = *reinterpret_cast<const uint4v*>(Wb + ((wm * RM + rm) * 32 + lj) * WST + lh * (T * 8) +
+                                                          (((2 * s) % CG) * T + (2 * s) / CG) * 8);
 #pragma unroll
             for (int rn = 0; rn < RN; ++rn)
                 br[rn] = *reinterpret_cast<const uint4v*>(Xb + xlane[rn] + koff[s]);
@@ -456,18 +457,15 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
         // (descriptor fields pass through readfirstlane: they are uniform,
         // and a descriptor the compiler cannot prove uniform costs a loop
         // over the lanes around each load)
-        // The descriptor starts at the stage's first group of row 0, so rows
-        // past CO read zeros; a chunk whose channel group lies past the row
-        // (the last stage of a CI that is not a multiple of KC) reads zeros
-        // through an offset past the buffer.
+        // The descriptor starts at the stage's first group of row 0 (a stage
+        // never runs past its row: rows hold a multiple of 64 channels), so
+        // only rows past CO fall outside it and read zeros.
         auto load_w1 = [&](int j, int s_abs) {
-            const int g0 = s_abs * CG;                                        // first group of the stage
-            const int sb = __builtin_amdgcn_readfirstlane(g0 * (T * 8));      // halves
+            const int sb = __builtin_amdgcn_readfirstlane(s_abs * CG * (T * 8));  // halves
             const int nrec = __builtin_amdgcn_readfirstlane((int)(w_bytes - 2LL * sb));
             const __amdgpu_buffer_rsrc_t wrs =
                 __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wpk + sb), 0, nrec, kBufRaw);
-            const unsigned off = g0 + wcg[j] < CG8 ? wvo[j] : kBufOut;
-            wreg[j] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wrs, off, 0, 0));
+            wreg[j] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo[j], 0, 0));
         };
         auto load_x1 = [&](XRegs& rg, int i, int c0) {
             // one descriptor per channel (scalar work only)
@@ -646,7 +644,8 @@ int h2_bytes_for(const ConvParams& p, int px) {
     // 32-bit byte offsets; offset 2^31 must lie past both, also for the rows
     // of the last tile past CO
     const long long tiles_m = (p.CO + C::TM - 1) / C::TM;
-    if (tiles_m * C::TM * round_up(p.CI, 8) * T * 2 >= (1LL << 31)) return 1 << 30;
+    if (tiles_m * C::TM * round_up(p.CI, 64) * T * 2 >= (1LL << 31)) return 1 << 30;
+    static_assert(64 % KC == 0, "a stage divides a prepared row's 64-channel blocks");
     if ((long long)p.N * p.CI * p.H * p.W * 2 >= (1LL << 31)) return 1 << 30;
     // the window tasks must fit the per-thread slots
     if ((long long)C::CG * p.R * (p.W / px) > (long long)C::XPT * C::NT) return 1 << 30;
@@ -664,7 +663,7 @@ int h2_lds_bytes(const ConvParams& p) {
 template <int WM, int WN, int RM, int RN, int KC, int T>
 long long h2_aux_bytes(const ConvParams& p) {
     if (p.w_prepared) return 0;
-    return 2LL * p.CO * round_up(p.CI, 8) * T;
+    return 2LL * p.CO * round_up(p.CI, 64) * T;
 }
 
 template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
@@ -718,18 +717,21 @@ hipError_t h2_launch(const ConvParams& p, hipStream_t stream) {
 
 }  // namespace
 
-// wp [CO][CI8/8][T][8] = w [CO][CI][T] regrouped, zeros past CI.
+// wp [CO][CI64/8][T][8] = w [CO][CI][T] regrouped, zeros past CI (CI64 = CI
+// rounded up to 64).
 hipError_t h2_prepare_filter(const void* w, void* wp, int CO, int CI, int T, hipStream_t stream) {
     (void)hipGetLastError();
-    const long long units = (long long)CO * ((CI + 7) / 8);
+    const int CGP = (CI + 63) / 64 * 8;
+    const long long units = (long long)CO * CGP;
     if (CI % 8 == 0 && reinterpret_cast<uintptr_t>(w) % 16 == 0 && (T == 9 || T == 1)) {
-        const long long blocks = (units + 255) / 256;
+        // one wave per 64 units: small filters still spread over many CUs
+        const long long blocks = (units + 63) / 64;
         if (T == 9)
-            hipLaunchKernelGGL(h2_prepare_vec_kernel<9>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                               static_cast<const uint4v*>(w), static_cast<uint4v*>(wp), units);
+            hipLaunchKernelGGL(h2_prepare_vec_kernel<9>, dim3((unsigned)blocks), dim3(64), 0, stream,
+                               static_cast<const uint4v*>(w), static_cast<uint4v*>(wp), CO, CI / 8, CGP);
         else
-            hipLaunchKernelGGL(h2_prepare_vec_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                               static_cast<const uint4v*>(w), static_cast<uint4v*>(wp), units);
+            hipLaunchKernelGGL(h2_prepare_vec_kernel<1>, dim3((unsigned)blocks), dim3(64), 0, stream,
+                               static_cast<const uint4v*>(w), static_cast<uint4v*>(wp), CO, CI / 8, CGP);
     } else {
         long long blocks = (units * T * 8 + 255) / 256;
         if (blocks > 4096) blocks = 4096;

@@ -1116,7 +1116,7 @@ long long ct_conv2d_filter_prepared_bytes(int CO, int CI, int KH, int KW, int dt
     if (CO <= 0 || CI <= 0 || KH <= 0 || KW <= 0) return fail(CT_ERR_INVALID_ARG, "every dimension must be positive");
     if (dtype != CT_F16 && dtype != CT_BF16)
         return fail(CT_ERR_INVALID_ARG, "prepared filters exist for CT_F16 and CT_BF16 only");
-    return 2LL * CO * ((CI + 7) / 8 * 8) * KH * KW;
+    return 2LL * CO * ((CI + 63) / 64 * 64) * KH * KW;
 }
 
 int ct_conv2d_prepare_filter(const void* w, void* wp, int CO, int CI, int KH, int KW, int dtype, void* stream) {

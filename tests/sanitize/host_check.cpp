@@ -52,7 +52,7 @@ int main(int argc, char** argv) {
     prog.n_ops[0] = CT_CHAIN_MAX_OPS + 1;
     CHECK(ct_broadcast_chain(&prog, nullptr, nullptr, nullptr, nullptr, nullptr, &y, CT_F32, 1, 1, 1, CT_BC_AUTO,
                              nullptr) == CT_ERR_INVALID_ARG);
-    CHECK(ct_conv2d_filter_prepared_bytes(40, 12, 3, 3, CT_F16) == 2LL * 40 * 16 * 9);
+    CHECK(ct_conv2d_filter_prepared_bytes(40, 12, 3, 3, CT_F16) == 2LL * 40 * 64 * 9);
     CHECK(ct_conv2d_filter_prepared_bytes(40, 12, 3, 3, CT_F32) == CT_ERR_INVALID_ARG);
 
     // the config space of the final ResNet layer: every point decodes, the

@@ -488,9 +488,9 @@ def test_half_precision_epilogue_every_config(dtype, shape, epi):
 
 def _regroup(w: np.ndarray) -> np.ndarray:
     """The documented prepared layout: wp[co][g][t][j] = w[co][8g+j][t],
-    zeros past CI (t = ky*KW + kx)."""
+    zeros past CI (t = ky*KW + kx), rows of CI rounded up to 64 channels."""
     CO, CI, KH, KW = w.shape
-    G = (CI + 7) // 8
+    G = (CI + 63) // 64 * 8
     wpad = np.zeros((CO, 8 * G, KH * KW), w.dtype)
     wpad[:, :CI] = w.reshape(CO, CI, KH * KW)
     return wpad.reshape(CO, G, 8, KH * KW).transpose(0, 1, 3, 2).copy()

@@ -452,9 +452,10 @@ def test_tensor_helpers_reject_host_and_strided_tensors():
 
 
 def test_prepared_filter_bytes():
-    # [CO][ceil(CI/8)][KH*KW][8] halves
+    # [CO][CI64/8][KH*KW][8] halves, CI64 = CI rounded up to 64
     assert ct.ct_conv2d_filter_prepared_bytes(256, 256, 3, 3, ct.CT_F16) == 2 * 256 * 256 * 9
-    assert ct.ct_conv2d_filter_prepared_bytes(40, 12, 3, 3, ct.CT_BF16) == 2 * 40 * 16 * 9
+    assert ct.ct_conv2d_filter_prepared_bytes(40, 12, 3, 3, ct.CT_BF16) == 2 * 40 * 64 * 9
+    assert ct.ct_conv2d_filter_prepared_bytes(40, 72, 3, 3, ct.CT_F16) == 2 * 40 * 128 * 9
     assert ct.ct_conv2d_filter_prepared_bytes(4096, 4096, 1, 1, ct.CT_F16) == 2 * 4096 * 4096
     assert ct.ct_conv2d_filter_prepared_bytes(8, 8, 3, 3, ct.CT_F32) == ct.CT_ERR_INVALID_ARG
     assert ct.ct_conv2d_filter_prepared_bytes(0, 8, 3, 3, ct.CT_F16) == ct.CT_ERR_INVALID_ARG
