@@ -21,11 +21,12 @@
 //    channel (PX = 8, 4, 2 or 1, the largest the row width and alignment
 //    allow), 8 channels per task, transposed in registers into PX 16-byte
 //    pixel records;
-//  - LDS holds two copies of (filter tile, window): the next stage's global
-//    loads are issued before the current stage's matrix steps and written to
-//    the other copy after them, with one barrier per stage; the window loads
-//    (from HBM) go out two stages ahead into a second register set, the
-//    filter loads (an L2-resident reordered copy) one stage ahead;
+//  - LDS holds two copies of (filter tile, window).  The next stage's filter
+//    tile goes from memory straight into the other copy (16-byte loads that
+//    write LDS, no registers), all issued as the current stage starts; the
+//    window loads (from HBM) go out two stages ahead into a second register
+//    set and are transposed into the other copy after the stage's matrix
+//    steps; one barrier per stage;
 //  - a stage's 9*KC/16 matrix steps are unrolled, each reading the next
 //    step's fragments before issuing its own instructions.
 // The window's padding is zeroed once at kernel start and never written
@@ -48,6 +49,19 @@ typedef unsigned int uint2v __attribute__((ext_vector_type(2)));
 
 constexpr int kBufRaw = 0x00020000;       // raw buffer descriptor, 32-bit elements
 constexpr unsigned kBufOut = 0x80000000u;  // an offset past every buffer (all are < 2 GiB): reads zeros
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// One wave fills 64 consecutive 16-byte LDS slots from lane_off (bytes)
+// within r, lane l the l-th; lds is wave-uniform.
+__device__ __forceinline__ void load_chunk_to_lds(__amdgpu_buffer_rsrc_t r, uint16_t* lds, unsigned lane_off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)lds, 16, lane_off, 0, 0, 0);
+}
+
+// s_waitcnt immediates that wait for the memory-load counter only (vmcnt in
+// bits 3:0 and 15:14; expcnt 6:4 and lgkmcnt 11:8 at their maxima)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kVmcnt0 = vmcnt_imm(0);
+template <int XPT> constexpr int kVmcnt8Xpt = vmcnt_imm(8 * XPT);
 
 template <int DT> struct HMma2;
 template <> struct HMma2<DT_F16> {
@@ -126,8 +140,13 @@ struct H2 {
     static constexpr int NSTEP = G / 2;        // instruction steps per stage
     static constexpr int WST = (G + 1) * 8;    // halves per filter row in LDS (odd x 16 B)
     static constexpr int KCS = (CG + 1) * 8;   // halves per window pixel (odd x 16 B)
-    static constexpr int WCH = TM * G;         // 16-byte filter chunks per stage
-    static constexpr int WPT = (WCH + NT - 1) / NT;
+    static constexpr int NW = WM * WN;         // waves
+    // the filter tile of a stage as 16-byte LDS slots [TM][G + 1] (the last
+    // slot of a row is padding), filled 64 slots (one load per wave) at a time
+    static constexpr int WSL = TM * (G + 1);
+    static constexpr int WCK = WSL / 64;       // 64-slot chunks
+    static constexpr int WLD = (WCK + NW - 1) / NW;  // chunk loads per wave
+    static_assert(WSL % 64 == 0, "whole chunks");
     static constexpr int XPT = NT >= 256 ? 1 : 2;  // window tasks per thread
     static constexpr int WB = TM * WST;        // halves per filter copy
     static_assert(G % 2 == 0, "a step takes two groups");
@@ -189,17 +208,44 @@ template <> struct BufLoad<1> {
     }
 };
 
-// Divisors: fd_kw = KW.
 // Column tiles of the grid: tiles_n rounded up to a multiple of 8, so that
 // every XCD (workgroup b runs on XCD b % 8) takes a block of whole columns.
 __host__ __device__ inline int h2_col_tiles(int tiles_n) { return (tiles_n + 7) & ~7; }
 
-template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
-__global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
+// The kernel's arguments: the convolution's plus the divisors of its index
+// set-up, so that the set-up runs on 32-bit multiply-high divisions (a
+// 64-bit or runtime 32-bit division is a long instruction sequence, and the
+// set-up precedes every load of the workgroup).
+struct H2Params : ConvParams {
+    FastDiv fd_ohw;    // OH * OW
+    FastDiv fd_tiles;  // workgroups per split: tiles_m * h2_col_tiles(tiles_n)
+    FastDiv fd_lm;     // row tiles of one XCD's rectangle (all of them without XCD groups)
+    FastDiv fd_rn;     // window tasks per channel group: R * runs per row
+    FastDiv fd_run;    // runs per window row: W / PX
+    int cgl;           // log2 of the XCD column groups; -1: column blocks per XCD
+};
+// also fd_kw = KW, fd_ow = OW, fd_hp = Hp (filled by the launcher)
+
+__device__ __forceinline__ void fetch_h2_kernargs(const H2Params& p) {
     fetch_kernargs(p);
+    asm volatile("" ::"s"(p.fd_lm.d));  // the sixth 64-byte line
+}
+// (the derived fields follow the base's: fd_lm starts the sixth line)
+static_assert((sizeof(ConvParams) + 2 * sizeof(FastDiv)) / 64 == 5 && sizeof(H2Params) <= 384,
+              "six argument lines");
+
+// n / d for any 32-bit n (the divisor's round-up multiplier and shift)
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
+    return (uint32_t)(((uint64_t)__umulhi(n, f.mul) + n) >> f.shift);
+}
+
+template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
+__global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
+    fetch_h2_kernargs(p);
     using C = H2<WM, WN, RM, RN, KC, T>;
     constexpr int TM = C::TM, TN = C::TN, NT = C::NT, CG = C::CG, G = C::G;
-    constexpr int NSTEP = C::NSTEP, WST = C::WST, KCS = C::KCS, WPT = C::WPT, XPT = C::XPT;
+    constexpr int NSTEP = C::NSTEP, WST = C::WST, KCS = C::KCS, XPT = C::XPT;
+    constexpr int NW = C::NW, WCK = C::WCK, WLD = C::WLD;
     extern __shared__ __align__(16) uint16_t hs[];
     __shared__ int s_last;
 
@@ -221,47 +267,34 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
 
     // workgroup -> (split, tile).  When the column tiles come in multiples
     // of 8, workgroup b runs on XCD x = b % 8 (round-robin placement) and the
-    // XCDs split the tile grid into ga row groups x 8/ga column groups: XCD x
-    // takes one rectangle, row tiles fastest (the readers of one window run
-    // together).  Each filter row block is then read by 8/ga XCDs and each
-    // window by ga, and ga minimises the estimate of the bytes they fetch,
-    // (8/ga) * tiles_m*TM*K + ga * tiles_n*TN*CI: 1 for convolutions (small
-    // filters), 2 or 4 for large matrix products.  Otherwise the grid holds
-    // column tiles rounded up to a multiple of 8 (h2_col_tiles) and each XCD
-    // takes a block of whole columns (ga = 1); workgroups past the last
-    // column exit at once.
-    const int cols = h2_col_tiles(p.tiles_n);
-    const int tiles = p.tiles_m * cols;
-    const int split = blockIdx.x / tiles;
-    const int b = blockIdx.x - split * tiles;
+    // XCDs split the tile grid into ga row groups x 8/ga column groups
+    // (2^cgl = 8/ga): XCD x takes one rectangle, row tiles fastest (the
+    // readers of one window run together).  Each filter row block is then
+    // read by 8/ga XCDs and each window by ga; the launcher picks ga.
+    // Otherwise (cgl < 0) the grid holds column tiles rounded up to a
+    // multiple of 8 (h2_col_tiles) and each XCD takes a block of whole
+    // columns; workgroups past the last column exit at once.
+    const int split = (int)fdiv(blockIdx.x, p.fd_tiles);
+    const uint32_t b = blockIdx.x - (uint32_t)split * p.fd_tiles.d;
+    const uint32_t x = b & 7, l = b >> 3;
+    const uint32_t lq = fdiv(l, p.fd_lm);
+    const int lr = (int)(l - lq * p.fd_lm.d);
     int tm, tn;
-    if ((p.tiles_n & 7) == 0) {
-        const double wbytes = (double)p.tiles_m * TM * p.K, xbytes = (double)p.tiles_n * TN * p.CI;
-        int ga = 1;
-        double best = 8.0 * wbytes + xbytes;
-        for (int g = 2; g <= 8; g *= 2) {
-            const double cost = (8 / g) * wbytes + g * xbytes;
-            if (p.tiles_m % g == 0 && p.tiles_n % (8 / g) == 0 && cost < best) {
-                best = cost;
-                ga = g;
-            }
-        }
-        const int x = b & 7, l = b >> 3;
-        const int rm = p.tiles_m / ga, rn = p.tiles_n / (8 / ga);
-        tm = (x / (8 / ga)) * rm + l % rm;
-        tn = (x % (8 / ga)) * rn + l / rm;
+    if (p.cgl >= 0) {
+        tm = (int)(x >> p.cgl) * (int)p.fd_lm.d + lr;
+        tn = (int)(x & ((1u << p.cgl) - 1)) * (p.tiles_n >> p.cgl) + (int)lq;
     } else {
-        const int x = b & 7, l = b >> 3;
-        tm = l % p.tiles_m;
-        tn = x * (cols >> 3) + l / p.tiles_m;
+        tm = lr;
+        tn = (int)x * (h2_col_tiles(p.tiles_n) >> 3) + (int)lq;
         if (tn >= p.tiles_n) return;  // padding of the grid: uniform over the workgroup
     }
     const int tile = tm + tn * p.tiles_m;
     const int co0 = tm * TM;
-    const long long p0 = (long long)tn * TN;
-    const long long n_first = p0 / p.OHW;
-    const int oy_first = (int)((p0 % p.OHW) / p.OW);
-    const long long vr_first = n_first * p.Hp + (long long)oy_first * p.stride;
+    // column indices fit 32 bits (P < 2^31, checked by the launcher)
+    const uint32_t p0 = (uint32_t)tn * TN;
+    const uint32_t n_first = fdiv(p0, p.fd_ohw);
+    const uint32_t oy_first = fdiv(p0 - n_first * p.fd_ohw.d, p.fd_ow);
+    const int vr_first = (int)(n_first * p.Hp + oy_first * p.stride);
     const long long HW = (long long)p.H * p.W;
 
     const uint16_t* __restrict__ xg = static_cast<const uint16_t*>(p.x);
@@ -275,16 +308,16 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     long long yoff[RN];  // y offset of (n, 0, oy, ox); -1 past P
 #pragma unroll
     for (int rn = 0; rn < RN; ++rn) {
-        const long long pc = p0 + (long long)(wn * RN + rn) * 32 + lj;
+        const uint32_t pc = p0 + (uint32_t)((wn * RN + rn) * 32 + lj);
         pbase[rn] = 0;
         yoff[rn] = -1;
-        if (pc < p.P) {
-            const long long n = pc / p.OHW;
-            const int rem = (int)(pc - n * p.OHW);
-            const int oy = rem / p.OW;
+        if ((long long)pc < p.P) {
+            const uint32_t n = fdiv(pc, p.fd_ohw);
+            const int rem = (int)(pc - n * p.fd_ohw.d);
+            const int oy = (int)fdiv((uint32_t)rem, p.fd_ow);
             const int ox = rem - oy * p.OW;
-            pbase[rn] = (int)(n * p.Hp + (long long)oy * p.stride - vr_first) * p.Wp + ox * p.stride;
-            yoff[rn] = n * (long long)p.CO * p.OHW + rem;
+            pbase[rn] = ((int)n * p.Hp + oy * p.stride - vr_first) * p.Wp + ox * p.stride;
+            yoff[rn] = (long long)n * p.CO * p.OHW + rem;
         }
     }
     // Window offset of this lane's group 2s + lh at step s.  With an even
@@ -297,7 +330,7 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     for (int s = 0; s < NSTEP; ++s) {
         const int t = (2 * s) / CG;
         const int cg = 2 * s - t * CG;
-        const int ky = (int)(((uint64_t)__umulhi((uint32_t)t, p.fd_kw.mul) + (uint32_t)t) >> p.fd_kw.shift);
+        const int ky = (int)fdiv((uint32_t)t, p.fd_kw);
         const int kx = t - ky * p.KW;
         koff[s] = __builtin_amdgcn_readfirstlane((ky * p.Wp + kx) * KCS + cg * 8);
     }
@@ -305,39 +338,36 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
 #pragma unroll
     for (int rn = 0; rn < RN; ++rn) xlane[rn] = pbase[rn] * KCS + lh * 8;
 
-    // ---- epilogue tables; zero both windows ----------------------------------
-    for (int m = tid; m < TM; m += NT) {
-        const int co = co0 + m;
-        float bb = 0.0f, r = 1.0f;
-        if (co < p.CO) {
-            if (p.epilogue != EPI_NONE) bb = p.bias[co];
-            if (p.epilogue == EPI_EXP_BIAS_RSQRT) r = dev_rsqrt(p.var[co] + p.eps);
+    // ---- epilogue values of row m = tid, loaded now (ahead of the stage
+    //      loads, so that waiting for them never waits for those) and written
+    //      to the LDS tables once the first stage's loads are out; zero both
+    //      windows -------------------------------------------------------------
+    static_assert(TM <= NT, "one epilogue row per thread");
+    float e_b = 0.0f, e_v = 0.0f;
+    const bool e_row = tid < TM && co0 + tid < p.CO;
+    if (e_row && p.epilogue != EPI_NONE) e_b = p.bias[co0 + tid];
+    if (e_row && p.epilogue == EPI_EXP_BIAS_RSQRT) e_v = p.var[co0 + tid];
+    auto write_tables = [&]() {
+        if (tid < TM) {
+            e_bias[tid] = e_b;
+            e_rs[tid] = (e_row && p.epilogue == EPI_EXP_BIAS_RSQRT) ? dev_rsqrt(e_v + p.eps) : 1.0f;
         }
-        e_bias[m] = bb;
-        e_rs[m] = r;
-    }
+    };
     {
         uint4v* xz = reinterpret_cast<uint4v*>(Xsb);
         for (int i = tid; i < XB / 4; i += NT) xz[i] = uint4v{0u, 0u, 0u, 0u};  // 2*XB halves
     }
 
     // ---- staging tasks (fixed for the kernel) ----------------------------------
-    // filter chunk q = (m, r): 16 bytes of row co0+m, record r = cg*T + tap of
-    // a stage, in the prepared row's order: a wave's reads and its LDS writes
-    // are both consecutive 16-byte pieces
-    int wsrc[WPT];  // halves, without the stage term; -1: no chunk
-    int wdst[WPT];
+    // filter slot q = (m, r) of chunk wave + j*NW: record r = cg*T + tap of
+    // row co0+m's stage, in the prepared row's order (r = G: padding)
+    int wsrc[WLD];  // halves, without the stage term; -1: padding
 #pragma unroll
-    for (int j = 0; j < WPT; ++j) {
-        const int q = tid + j * NT;
-        wsrc[j] = -1;
-        wdst[j] = 0;
-        if (q < C::WCH) {
-            const int m = q / G;
-            const int r = q - m * G;
-            wsrc[j] = (co0 + m) * CG8 * (T * 8) + r * 8;
-            wdst[j] = m * WST + r * 8;
-        }
+    for (int j = 0; j < WLD; ++j) {
+        const int q = (wave + j * NW) * 64 + lane;
+        const int m = q / (G + 1);
+        const int r = q - m * (G + 1);
+        wsrc[j] = (q < C::WSL && r < G) ? (co0 + m) * CG8 * (T * 8) + r * 8 : -1;
     }
     // window task q = (cg, window row r, run u): 8 channels x PX pixels
     const int nrun = p.W / PX;
@@ -352,13 +382,13 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
         xdst[j] = 0;
         xch[j] = 0;
         if (q < n_xt) {
-            const int cg = q / (p.R * nrun);
-            const int rem = q - cg * (p.R * nrun);
-            const int r = rem / nrun;
+            const int cg = (int)fdiv((uint32_t)q, p.fd_rn);
+            const int rem = q - cg * (int)p.fd_rn.d;
+            const int r = (int)fdiv((uint32_t)rem, p.fd_run);
             const int u = rem - r * nrun;
-            const long long vr = vr_first + r;
-            const long long n = vr / p.Hp;
-            const int iy = (int)(vr - n * p.Hp) - p.pad;
+            const uint32_t vr = (uint32_t)vr_first + (uint32_t)r;
+            const int n = (int)fdiv(vr, p.fd_hp);
+            const int iy = (int)(vr - (uint32_t)n * p.Hp) - p.pad;
             if (n < p.N && iy >= 0 && iy < p.H) {
                 xsrc[j] = ((n * p.CI + cg * 8) * p.H + iy) * (long long)p.W + u * PX;
                 xdst[j] = (r * p.Wp + p.pad + u * PX) * KCS + cg * 8;
@@ -385,9 +415,9 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     // load in flight, the prefetches included.)
     const long long x_bytes = (long long)p.N * p.CI * HW * 2;
     const long long w_bytes = (long long)p.CO * CG8 * T * 16;
-    unsigned wvo[WPT], xvo[XPT];
+    unsigned wvo[WLD], xvo[XPT];
 #pragma unroll
-    for (int j = 0; j < WPT; ++j) wvo[j] = wsrc[j] >= 0 ? (unsigned)wsrc[j] * 2u : kBufOut;
+    for (int j = 0; j < WLD; ++j) wvo[j] = wsrc[j] >= 0 ? (unsigned)wsrc[j] * 2u : kBufOut;
 #pragma unroll
     for (int j = 0; j < XPT; ++j) xvo[j] = xsrc[j] >= 0 ? (unsigned)xsrc[j] * 2u : kBufOut;
 
@@ -448,10 +478,9 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
     const int last = nst - 1;
     auto run_stages = [&](auto hx_tag) {
         constexpr bool HX = decltype(hx_tag)::value;
-        uint4v wreg[WPT];
         XRegs xa, xb;
-        // Load units: filter chunk j of stage s_abs (j < WPT), and window
-        // channel i of every task of the stage starting at channel c0.
+        // Load units: filter chunk j of stage s_abs (into LDS copy buf), and
+        // window channel i of every task of the stage starting at channel c0.
         // Channels past CI in the last image read zeros; those past CI inside
         // the tensor are zeroed by store_stage.
         // (descriptor fields pass through readfirstlane: they are uniform,
@@ -460,12 +489,21 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
         // The descriptor starts at the stage's first group of row 0 (a stage
         // never runs past its row: rows hold a multiple of 64 channels), so
         // only rows past CO fall outside it and read zeros.
-        auto load_w1 = [&](int j, int s_abs) {
+        // Each load writes the 64 consecutive 16-byte LDS slots of one chunk,
+        // lane l the l-th (the LDS address is the chunk's, a wave-uniform
+        // value).
+        auto load_w = [&](int s_abs, int buf) {
             const int sb = __builtin_amdgcn_readfirstlane(s_abs * CG * (T * 8));  // halves
             const int nrec = __builtin_amdgcn_readfirstlane((int)(w_bytes - 2LL * sb));
             const __amdgpu_buffer_rsrc_t wrs =
                 __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(wpk + sb), 0, nrec, kBufRaw);
-            wreg[j] = __builtin_bit_cast(uint4v, __builtin_amdgcn_raw_buffer_load_b128(wrs, wvo[j], 0, 0));
+            auto one = [&](int j) { load_chunk_to_lds(wrs, Wsb + buf * C::WB + (wave + j * NW) * 512, wvo[j]); };
+            // only a wave's last chunk can lie past the tile
+#pragma unroll
+            for (int j = 0; j + 1 < WLD; ++j) one(j);
+            if (WCK % NW == 0 || wave + (WLD - 1) * NW < WCK) one(WLD - 1);
+            // loads issued later stay later (wait_filter counts on it)
+            __builtin_amdgcn_sched_barrier(0);
         };
         auto load_x1 = [&](XRegs& rg, int i, int c0) {
             // one descriptor per channel (scalar work only)
@@ -476,40 +514,38 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
 #pragma unroll
             for (int j = 0; j < XPT; ++j) rg.v[j][i] = BufLoad<PX>::load(xrs, xvo[j]);
         };
-        auto load_w = [&](int s_abs) {
-#pragma unroll
-            for (int j = 0; j < WPT; ++j) load_w1(j, s_abs);
-        };
         auto load_x = [&](XRegs& rg, int c0) {
             if constexpr (HX) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) load_x1(rg, i, c0);
             }
         };
-        // The next stages' loads, spread over the matrix steps so that no
-        // wave stalls on a full memory queue with its matrix work waiting:
-        // unit u (filter chunks, then window channels) goes out at step
-        // u * NSTEP / NU.
-        constexpr int NU = WPT + (HX ? 8 : 0);
-        auto spread_loads = [&](int s, int s_w, XRegs& rg, int c0) {
+        // The next stages' loads: the filter chunks as the stage's first
+        // matrix step issues, the window channels spread over the later
+        // steps (channel i at step 1 + i * (NSTEP - 1) / 8; all at the first
+        // when a stage is one step), so that no wave
+        // stalls on a full memory queue with its matrix work waiting.  Every
+        // filter load precedes every window load of the stage.
+        auto spread_loads = [&](int s, int s_w, int buf_w, XRegs& rg, int c0) {
+            if (s == 0) load_w(s_w, buf_w);
+            if constexpr (HX) {
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                if (u * NSTEP / NU != s) continue;
-                if (u < WPT)
-                    load_w1(u, s_w);
-                else
-                    load_x1(rg, u - WPT, c0);
+                for (int i = 0; i < 8; ++i)
+                    if ((NSTEP > 1 ? 1 + i * (NSTEP - 1) / 8 : 0) == s) load_x1(rg, i, c0);
             }
         };
-        // LDS writes of a stage: the filter chunks and the window's pixel
-        // records (channels past CI zeroed first).  c0: the stage's first
-        // channel.
+        // Wait for this wave's filter loads: the window loads issued after
+        // them may stay in flight (memory loads complete in order).
+        auto wait_filter = [&]() {
+            if constexpr (HX)
+                __builtin_amdgcn_s_waitcnt(kVmcnt8Xpt<XPT>);
+            else
+                __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        };
+        // LDS writes of a stage's window: its pixel records (channels past
+        // CI zeroed first).  c0: the stage's first channel.
         auto store_stage = [&](XRegs& rg, int buf, int c0) {
-            uint16_t* Wb = Wsb + buf * C::WB;
             uint16_t* Xb = Xsb + buf * XB;
-#pragma unroll
-            for (int j = 0; j < WPT; ++j)
-                if (wvo[j] != kBufOut) *reinterpret_cast<uint4v*>(Wb + wdst[j]) = wreg[j];
             if constexpr (HX) {
                 auto& xreg = rg.v;
 #pragma unroll
@@ -531,21 +567,24 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(ConvParams p) {
             }
         };
         if (nst > 0) {
-            load_w(s_first);
+            load_w(s_first, 0);
             load_x(xa, s_first * KC);
             load_x(xb, (s_first + min(1, last)) * KC);
             store_stage(xa, 0, s_first * KC);
         }
+        write_tables();
+        if (nst > 0) wait_filter();
         __syncthreads();
         // stage st: `held` has stage st+1's window, `free` takes stage st+2's
         auto step = [&](int st, XRegs& held, XRegs& free) {
             const int s_w = s_first + min(st + 1, last);
             const int c0x = (s_first + min(st + 2, last)) * KC;
-            mfma_stage(st & 1, [&](int s) { spread_loads(s, s_w, free, c0x); });
+            mfma_stage(st & 1, [&](int s) { spread_loads(s, s_w, (st + 1) & 1, free, c0x); });
             // LDS writes after the matrix steps: interleaved with them, the
             // window's register transposes lengthen the matrix phase by as
             // much as they take
             store_stage(held, (st + 1) & 1, (s_first + min(st + 1, last)) * KC);
+            wait_filter();
             __syncthreads();
         };
         int st = 0;
@@ -667,9 +706,42 @@ long long h2_aux_bytes(const ConvParams& p) {
 }
 
 template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
-hipError_t h2_launch_px(const ConvParams& q, int bytes, hipStream_t stream) {
+hipError_t h2_launch_px(const ConvParams& base, int bytes, hipStream_t stream) {
     using C = H2<WM, WN, RM, RN, KC, T>;
     auto kern = igemm_h2_kernel<DT, WM, WN, RM, RN, KC, T, PX>;
+    H2Params q;
+    static_cast<ConvParams&>(q) = base;
+    q.fd_kw = make_fastdiv((uint32_t)base.KW);
+    q.fd_ow = make_fastdiv((uint32_t)base.OW);
+    q.fd_hp = make_fastdiv((uint32_t)base.Hp);
+    q.fd_ohw = make_fastdiv((uint32_t)base.OHW);
+    const int cols = h2_col_tiles(base.tiles_n);
+    q.fd_tiles = make_fastdiv((uint32_t)(base.tiles_m * cols));
+    // XCD row groups ga: the one that minimises the estimate of the bytes
+    // the XCDs fetch, (8/ga) * tiles_m*TM*K + ga * tiles_n*TN*CI (1 for
+    // convolutions, whose filters are small; 2 or 4 for large matrix
+    // products), among those that divide the grid
+    q.cgl = -1;
+    int lm = base.tiles_m;
+    if ((base.tiles_n & 7) == 0) {
+        const double wbytes = (double)base.tiles_m * C::TM * base.K;
+        const double xbytes = (double)base.tiles_n * C::TN * base.CI;
+        int ga = 1;
+        double best = 8.0 * wbytes + xbytes;
+        for (int g = 2; g <= 8; g *= 2) {
+            const double cost = (8 / g) * wbytes + g * xbytes;
+            if (base.tiles_m % g == 0 && base.tiles_n % (8 / g) == 0 && cost < best) {
+                best = cost;
+                ga = g;
+            }
+        }
+        q.cgl = ga == 1 ? 3 : ga == 2 ? 2 : ga == 4 ? 1 : 0;
+        lm = base.tiles_m / ga;
+    }
+    q.fd_lm = make_fastdiv((uint32_t)lm);
+    const int nrun = base.W / PX;
+    q.fd_rn = make_fastdiv((uint32_t)(base.R * nrun));
+    q.fd_run = make_fastdiv((uint32_t)nrun);
     static std::atomic<int> lds_limit{65536};
     if (bytes > lds_limit.load(std::memory_order_relaxed)) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -705,13 +777,11 @@ hipError_t h2_launch(const ConvParams& p, hipStream_t stream) {
     } else {
         pp.aux = nullptr;  // the caller's filter is prepared: stage from p.w
     }
-    ConvParams q = pp;
-    q.fd_kw = make_fastdiv((uint32_t)p.KW);
     switch (px) {
-        case 8: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 8>(q, bytes, stream);
-        case 4: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 4>(q, bytes, stream);
-        case 2: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 2>(q, bytes, stream);
-        default: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 1>(q, bytes, stream);
+        case 8: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 8>(pp, bytes, stream);
+        case 4: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 4>(pp, bytes, stream);
+        case 2: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 2>(pp, bytes, stream);
+        default: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 1>(pp, bytes, stream);
     }
 }
 

@@ -378,6 +378,15 @@ def test_half_precision_small(dtype, shape):
         got = ct.conv2d(x, k1, w.stride, w.pad, config=cfg)
         torch.cuda.synchronize()
         assert np.array_equal(got.cpu().numpy().astype(np.float64), yi), ("misaligned w", cfg)
+    # an output that is not 16-byte aligned (stored element by element)
+    ybuf = torch.empty(yi.size + 1, device=DEV)
+    y1 = ybuf[1:].view(yi.shape)
+    assert y1.data_ptr() % 16 != 0
+    for cfg in [None] + legal_configs(w):
+        y1.fill_(float("nan"))
+        ct.conv2d(x, k, w.stride, w.pad, config=cfg, out=y1)
+        torch.cuda.synchronize()
+        assert np.array_equal(y1.cpu().numpy().astype(np.float64), yi), ("misaligned y", cfg)
 
 
 HALF_FULL = ["f16_n64_c256_14x14_k3", "f16_n128_c128to256_32x32_k3_epi"]
