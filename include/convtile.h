@@ -430,6 +430,60 @@ int ct_variant_info(int variant, ct_variant_desc* out);
 long long ct_split_count(long long n, int k);
 int ct_split_entity(long long n, int k, long long i, long long* out);
 
+/* ---- the tutorial template's own space ---------------------------------
+ * The conv2d_nchw schedule of the TVM tutorial "Tuning High Performance
+ * Convolution on NVIDIA GPUs" (Step 1) has eight knobs, in declaration order:
+ *   tile_f = split(CO, 4), tile_y = split(OH, 4), tile_x = split(OW, 4),
+ *   tile_rc = split(CI, 3), tile_ry = split(KH, 3), tile_rx = split(KW, 3)
+ *   (each in ct_split_entity's order), auto_unroll_max_step in {0, 512,
+ *   1500}, unroll_explicit in {0, 1};
+ * the flat index is mixed radix over them, tile_f least significant: the
+ * space the gist's run prints for the last ResNet layer (10,454,400 points)
+ * and the index beside each record of its tuning log.  This library does not
+ * build that schedule (its kernels are the MFMA variants above); the space
+ * and the check below reproduce which of the tutorial's candidates its run
+ * rejected before timing them (error_no 1, "invalid gpu kernel"). */
+typedef struct {
+    int tile_f[4], tile_y[4], tile_x[4];
+    int tile_rc[3], tile_ry[3], tile_rx[3];
+    int auto_unroll_max_step;
+    int unroll_explicit;
+} ct_tvm_config;
+
+/* Points of the template's space for this shape; < 0 on a bad shape. */
+long long ct_tvm_space_size(int N, int CI, int H, int W, int CO, int KH, int KW,
+                            int stride, int pad);
+/* Decode flat `index` into *out.  CT_ERR_INVALID_ARG for a bad shape, a NULL
+ * out or an index outside [0, size). */
+int ct_tvm_space_entity(int N, int CI, int H, int W, int CO, int KH, int KW,
+                        int stride, int pad, long long index, ct_tvm_config* out);
+/* The flat index of *cfg in the space (the inverse of ct_tvm_space_entity);
+ * CT_ERR_INVALID_ARG for a bad shape or a NULL cfg, -1 (with no error
+ * recorded) when *cfg is not a point of the space. */
+long long ct_tvm_space_index(int N, int CI, int H, int W, int CO, int KH, int KW,
+                             int stride, int pad, const ct_tvm_config* cfg);
+
+#define CT_TVM_LIMITS_PAGE 0    /* the tutorial run's GPU: 48 KiB shared memory, 1024 threads per block */
+#define CT_TVM_LIMITS_GFX950 1  /* this device: 160 KiB LDS, 1024 threads per workgroup */
+
+/* The tutorial schedule's block resources under *cfg, without building it.
+ * The schedule stages the padded input (AA) and the filter (WW) in shared
+ * memory at the outer rx loop, inside the outer rc, ry and rx loops, so each
+ * holds one block's output tile against the middle x inner reduction
+ * extents, in fp32:
+ *   AA = RC_s * ((Y_b - 1) * stride + RY_s) * ((X_b - 1) * stride + RX_s)
+ *   WW = F_b * RC_s * RY_s * RX_s
+ * with F_b = tile_f[1] * tile_f[2] * tile_f[3] (vthread, thread and inner
+ * factors; Y_b and X_b alike), RC_s = tile_rc[1] * tile_rc[2] and, as the
+ * schedule is printed, the ry axis split by tile_rx's factors and rx by
+ * tile_ry's: RY_s = tile_rx[1] * tile_rx[2], RX_s = tile_ry[1] * tile_ry[2].
+ * Threads per block = tile_f[2] * tile_y[2] * tile_x[2].  Writes
+ * *shared_bytes = 4 * (AA + WW) and *threads (either may be NULL); returns
+ * 1 when both fit the limits of `mode`, 0 when not, CT_ERR_INVALID_ARG for a
+ * NULL cfg, a factor < 1, stride < 1 or an unknown mode. */
+int ct_tvm_config_check(const ct_tvm_config* cfg, int stride, int mode,
+                        long long* shared_bytes, int* threads);
+
 /* ---- per-channel broadcast --------------------------------------------
  * out[n][c][h][w] = exp(var[c])  (Paddle PR, Introduction and Example:
  * [1,C,1,1] => [N,C,H,W]).  var: C floats on the device; out: N*C*H*W

@@ -52,6 +52,32 @@ class ct_bcast_program(ctypes.Structure):
     _fields_ = [("n_ops", ctypes.c_int * 3), ("ops", (ct_chain_op * CT_CHAIN_MAX_OPS) * 3)]
 
 
+class ct_tvm_config(ctypes.Structure):
+    _fields_ = [("tile_f", ctypes.c_int * 4), ("tile_y", ctypes.c_int * 4), ("tile_x", ctypes.c_int * 4),
+                ("tile_rc", ctypes.c_int * 3), ("tile_ry", ctypes.c_int * 3), ("tile_rx", ctypes.c_int * 3),
+                ("auto_unroll_max_step", ctypes.c_int), ("unroll_explicit", ctypes.c_int)]
+
+    def as_dict(self):
+        return {f: (list(getattr(self, f)) if f.startswith("tile_") else getattr(self, f))
+                for f, _ in self._fields_}
+
+    @classmethod
+    def from_dict(cls, d):
+        c = cls()
+        for f, _ in cls._fields_:
+            if f.startswith("tile_"):
+                arr = getattr(c, f)
+                for i, v in enumerate(d[f]):
+                    arr[i] = v
+            else:
+                setattr(c, f, d[f])
+        return c
+
+
+CT_TVM_LIMITS_PAGE = 0
+CT_TVM_LIMITS_GFX950 = 1
+
+
 class ct_variant_desc(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 48), ("dtype", ctypes.c_int), ("kind", ctypes.c_int),
                 ("mfma_m", ctypes.c_int), ("mfma_n", ctypes.c_int), ("mfma_k", ctypes.c_int),
@@ -112,6 +138,11 @@ _SIGS = {
     "ct_variant_info": (_I, [_I, ctypes.POINTER(ct_variant_desc)]),
     "ct_split_count": (_LL, [_LL, _I]),
     "ct_split_entity": (_I, [_LL, _I, _LL, ctypes.POINTER(_LL)]),
+    "ct_tvm_space_size": (_LL, [_I] * 9),
+    "ct_tvm_space_entity": (_I, [_I] * 9 + [_LL, ctypes.POINTER(ct_tvm_config)]),
+    "ct_tvm_space_index": (_LL, [_I] * 9 + [ctypes.POINTER(ct_tvm_config)]),
+    "ct_tvm_config_check": (_I, [ctypes.POINTER(ct_tvm_config), _I, _I, ctypes.POINTER(_LL),
+                                 ctypes.POINTER(_I)]),
     "ct_broadcast_nchw": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "ct_cache_load": (_I, [ctypes.c_char_p]),
     "ct_cache_save": (_I, [ctypes.c_char_p]),
@@ -367,6 +398,30 @@ def ct_split_entity(n: int, k: int, i: int):
     out = (_LL * k)()
     st = _load().ct_split_entity(n, k, i, out)
     return st, list(out)
+
+
+def ct_tvm_space_size(N, CI, H, W, CO, KH, KW, stride, pad) -> int:
+    return _load().ct_tvm_space_size(N, CI, H, W, CO, KH, KW, stride, pad)
+
+
+def ct_tvm_space_entity(N, CI, H, W, CO, KH, KW, stride, pad, index):
+    """(status, config dict) of flat index `index` of the template's space."""
+    out = ct_tvm_config()
+    st = _load().ct_tvm_space_entity(N, CI, H, W, CO, KH, KW, stride, pad, index, ctypes.byref(out))
+    return st, out.as_dict()
+
+
+def ct_tvm_space_index(N, CI, H, W, CO, KH, KW, stride, pad, cfg: dict) -> int:
+    c = ct_tvm_config.from_dict(cfg)
+    return _load().ct_tvm_space_index(N, CI, H, W, CO, KH, KW, stride, pad, ctypes.byref(c))
+
+
+def ct_tvm_config_check(cfg: dict, stride: int, mode: int = CT_TVM_LIMITS_PAGE):
+    """(fits 1/0 or status < 0, shared bytes, threads per block)."""
+    c = ct_tvm_config.from_dict(cfg)
+    nb, nt = _LL(0), _I(0)
+    r = _load().ct_tvm_config_check(ctypes.byref(c), stride, mode, ctypes.byref(nb), ctypes.byref(nt))
+    return r, nb.value, nt.value
 
 
 def ct_broadcast_nchw(var, out, N, C, H, W, out_dtype, op=CT_BC_EXP, mode=CT_BC_AUTO,

@@ -1284,6 +1284,146 @@ int ct_split_entity(long long n, int k, long long i, long long* out) {
     return CT_OK;
 }
 
+// ---- the tutorial template's space and resource check --------------------
+
+namespace {
+
+constexpr int kTvmUnroll[3] = {0, 512, 1500};
+
+// Knob tables of the template for a shape: the six splits (tile_f, tile_y,
+// tile_x over CO, OH, OW into 4; tile_rc, tile_ry, tile_rx over CI, KH, KW
+// into 3) and the two option lists, with their lengths in declaration order.
+struct TvmKnobs {
+    const std::vector<std::vector<long long>>* split[6];
+    long long len[8];
+    long long size;
+};
+
+int tvm_knobs(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad, TvmKnobs* k) {
+    Shape s;
+    const int st = make_shape(N, CI, H, W, CO, KH, KW, stride, pad, CT_F32, CT_EPI_NONE, &s);
+    if (st != CT_OK) return st;
+    const long long ext[6] = {s.CO, s.OH, s.OW, s.CI, s.KH, s.KW};
+    const int parts[6] = {4, 4, 4, 3, 3, 3};
+    k->size = 1;
+    for (int i = 0; i < 6; ++i) {
+        k->split[i] = &splits(ext[i], parts[i]);
+        k->len[i] = (long long)k->split[i]->size();
+    }
+    k->len[6] = 3;
+    k->len[7] = 2;
+    for (int i = 0; i < 8; ++i) {
+        if (k->size > (1LL << 62) / k->len[i]) return fail(CT_ERR_INVALID_ARG, "space too large");
+        k->size *= k->len[i];
+    }
+    return CT_OK;
+}
+
+int* tvm_knob_field(ct_tvm_config* c, int i) {
+    switch (i) {
+        case 0: return c->tile_f;
+        case 1: return c->tile_y;
+        case 2: return c->tile_x;
+        case 3: return c->tile_rc;
+        case 4: return c->tile_ry;
+        default: return c->tile_rx;
+    }
+}
+
+}  // namespace
+
+long long ct_tvm_space_size(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad) {
+    TvmKnobs k;
+    const int st = tvm_knobs(N, CI, H, W, CO, KH, KW, stride, pad, &k);
+    return st != CT_OK ? st : k.size;
+}
+
+int ct_tvm_space_entity(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad,
+                        long long index, ct_tvm_config* out) {
+    if (!out) return fail(CT_ERR_INVALID_ARG, "out must not be NULL");
+    TvmKnobs k;
+    const int st = tvm_knobs(N, CI, H, W, CO, KH, KW, stride, pad, &k);
+    if (st != CT_OK) return st;
+    if (index < 0 || index >= k.size) return fail(CT_ERR_INVALID_ARG, "index outside the space");
+    long long rest = index;
+    for (int i = 0; i < 6; ++i) {
+        const auto& e = (*k.split[i])[rest % k.len[i]];
+        rest /= k.len[i];
+        int* f = tvm_knob_field(out, i);
+        for (size_t j = 0; j < e.size(); ++j) f[j] = (int)e[j];
+    }
+    out->auto_unroll_max_step = kTvmUnroll[rest % 3];
+    rest /= 3;
+    out->unroll_explicit = (int)(rest % 2);
+    return CT_OK;
+}
+
+long long ct_tvm_space_index(int N, int CI, int H, int W, int CO, int KH, int KW, int stride, int pad,
+                             const ct_tvm_config* cfg) {
+    if (!cfg) return fail(CT_ERR_INVALID_ARG, "cfg must not be NULL");
+    TvmKnobs k;
+    const int st = tvm_knobs(N, CI, H, W, CO, KH, KW, stride, pad, &k);
+    if (st != CT_OK) return st;
+    ct_tvm_config c = *cfg;
+    long long digit[8];
+    for (int i = 0; i < 6; ++i) {
+        const int* f = tvm_knob_field(&c, i);
+        digit[i] = -1;
+        const auto& sp = *k.split[i];
+        for (size_t t = 0; t < sp.size() && digit[i] < 0; ++t) {
+            bool same = true;
+            for (size_t j = 0; j < sp[t].size(); ++j) same = same && sp[t][j] == f[j];
+            if (same) digit[i] = (long long)t;
+        }
+        if (digit[i] < 0) return -1;
+    }
+    digit[6] = -1;
+    for (int t = 0; t < 3; ++t)
+        if (kTvmUnroll[t] == cfg->auto_unroll_max_step) digit[6] = t;
+    if (digit[6] < 0 || (cfg->unroll_explicit != 0 && cfg->unroll_explicit != 1)) return -1;
+    digit[7] = cfg->unroll_explicit;
+    long long index = 0, radix = 1;
+    for (int i = 0; i < 8; ++i) {
+        index += digit[i] * radix;
+        radix *= k.len[i];
+    }
+    return index;
+}
+
+int ct_tvm_config_check(const ct_tvm_config* cfg, int stride, int mode, long long* shared_bytes,
+                        int* threads) {
+    if (!cfg) return fail(CT_ERR_INVALID_ARG, "cfg must not be NULL");
+    if (stride < 1) return fail(CT_ERR_INVALID_ARG, "stride must be positive");
+    if (mode != CT_TVM_LIMITS_PAGE && mode != CT_TVM_LIMITS_GFX950)
+        return fail(CT_ERR_INVALID_ARG, "unknown mode %d", mode);
+    const int* four[3] = {cfg->tile_f, cfg->tile_y, cfg->tile_x};
+    const int* three[3] = {cfg->tile_rc, cfg->tile_ry, cfg->tile_rx};
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 4; ++j)
+            if (four[i][j] < 1) return fail(CT_ERR_INVALID_ARG, "split factors must be >= 1");
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            if (three[i][j] < 1) return fail(CT_ERR_INVALID_ARG, "split factors must be >= 1");
+    // a block's output extents: vthread x thread x inner factors
+    const long long fb = (long long)cfg->tile_f[1] * cfg->tile_f[2] * cfg->tile_f[3];
+    const long long yb = (long long)cfg->tile_y[1] * cfg->tile_y[2] * cfg->tile_y[3];
+    const long long xb = (long long)cfg->tile_x[1] * cfg->tile_x[2] * cfg->tile_x[3];
+    // reduction extents inside the outer rc, ry, rx loops, where the shared
+    // stages are computed (ry split by tile_rx's factors and rx by tile_ry's,
+    // as the schedule is printed)
+    const long long rcs = (long long)cfg->tile_rc[1] * cfg->tile_rc[2];
+    const long long rys = (long long)cfg->tile_rx[1] * cfg->tile_rx[2];
+    const long long rxs = (long long)cfg->tile_ry[1] * cfg->tile_ry[2];
+    const long long aa = rcs * ((yb - 1) * stride + rys) * ((xb - 1) * stride + rxs);
+    const long long ww = fb * rcs * rys * rxs;
+    const long long bytes = 4 * (aa + ww);
+    const long long nthr = (long long)cfg->tile_f[2] * cfg->tile_y[2] * cfg->tile_x[2];
+    if (shared_bytes) *shared_bytes = bytes;
+    if (threads) *threads = (int)std::min<long long>(nthr, 1LL << 30);
+    const long long limit = mode == CT_TVM_LIMITS_PAGE ? 48LL * 1024 : 160LL * 1024;
+    return (bytes <= limit && nthr <= 1024) ? 1 : 0;
+}
+
 int ct_broadcast_nchw(const float* var, void* out, int N, int C, int H, int W, int out_dtype, int op,
                       int mode, void* stream) {
     if (!var || !out) return fail(CT_ERR_INVALID_ARG, "var and out must not be NULL");

@@ -89,6 +89,25 @@ int main(int argc, char** argv) {
     CHECK(ct_split_entity(512, 4, 220, e) == CT_ERR_INVALID_ARG);
     CHECK(ct_split_count(0, 2) < 0 && ct_split_count(8, 9) < 0);
 
+    // the tutorial template's space: the printed size, a decode/encode round
+    // trip over a stride of the space, and the best config's shared bytes
+    CHECK(ct_tvm_space_size(1, 512, 7, 7, 512, 3, 3, 1, 1) == 10454400);
+    for (long long i = 0; i < 10454400; i += 104543) {
+        ct_tvm_config tc{};
+        CHECK(ct_tvm_space_entity(1, 512, 7, 7, 512, 3, 3, 1, 1, i, &tc) == CT_OK);
+        CHECK(ct_tvm_space_index(1, 512, 7, 7, 512, 3, 3, 1, 1, &tc) == i);
+        long long nb = 0;
+        int nt = 0;
+        const int fits = ct_tvm_config_check(&tc, 1, CT_TVM_LIMITS_GFX950, &nb, &nt);
+        CHECK((fits == 0 || fits == 1) && nb > 0 && nt > 0);
+    }
+    const ct_tvm_config best = {{8, 1, 64, 1}, {1, 7, 1, 1}, {1, 7, 1, 1}, {64, 2, 4}, {1, 1, 3}, {1, 3, 1}, 1500, 1};
+    long long best_bytes = 0;
+    CHECK(ct_tvm_config_check(&best, 1, CT_TVM_LIMITS_PAGE, &best_bytes, nullptr) == 1);
+    CHECK(best_bytes == 4LL * (8 * 9 * 9 + 64 * 8 * 3 * 3));
+    CHECK(ct_tvm_space_index(1, 512, 7, 7, 512, 3, 3, 1, 1, &best) == 9751545);
+    CHECK(ct_tvm_config_check(nullptr, 1, CT_TVM_LIMITS_PAGE, nullptr, nullptr) == CT_ERR_INVALID_ARG);
+
     // tuning log: resume order, then a log with malformed lines loads the
     // fastest successful record and ignores the rest
     std::vector<long long> order(n);

@@ -523,3 +523,86 @@ def test_tuning_log_loads_the_fastest_successful_record(tmp_path):
     assert from_cache == 1 and (cfg.variant, cfg.split_k, cfg.stages, cfg.kc) == (
         pts[1].variant, pts[1].split_k, pts[1].stages, pts[1].kc)
     ct.ct_cache_clear()
+
+
+# ---- the tutorial template's space and resource check in the runtime ------
+
+def _gist():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "tvm_tuning_log.json")) as f:
+        return json.load(f)
+
+
+_GIST_SHAPE = (1, 512, 7, 7, 512, 3, 3, 1, 1)  # N, CI, H, W, CO, KH, KW, stride, pad
+
+
+def test_tvm_space_size_matches_the_gist_dump():
+    g = _gist()
+    assert ct.ct_tvm_space_size(*_GIST_SHAPE) == g["space"]["total"] == 10454400
+
+
+def test_tvm_space_indices_match_the_gist_log():
+    g = _gist()
+    pairs = [(t["config"], t["index"]) for t in g["trials"]] + [(g["best"]["config"], g["best"]["index"])]
+    assert len(pairs) == 21
+    for cfg, idx in pairs:
+        assert ct.ct_tvm_space_index(*_GIST_SHAPE, cfg) == idx
+        st, got = ct.ct_tvm_space_entity(*_GIST_SHAPE, idx)
+        assert st == 0 and got == cfg
+
+
+def test_tvm_page_limits_reproduce_the_gist_rejections():
+    """Page-1 mode: exactly the trials the tutorial's run rejected before
+    timing them (error_no 1) exceed the 48 KiB shared-memory limit."""
+    g = _gist()
+    for t in g["trials"]:
+        fits, nbytes, threads = ct.ct_tvm_config_check(t["config"], 1, ct.CT_TVM_LIMITS_PAGE)
+        assert fits == (0 if t["error_no"] == 1 else 1), (t["no"], nbytes)
+        assert threads <= 1024
+    fits, nbytes, threads = ct.ct_tvm_config_check(g["best"]["config"], 1, ct.CT_TVM_LIMITS_PAGE)
+    # Y_b = X_b = 7, RC_s = 8, RY_s = RX_s = 3, F_b = 64 (threads 64)
+    assert (fits, nbytes, threads) == (1, 4 * (8 * 9 * 9 + 64 * 8 * 3 * 3), 64)
+    # gfx950's 160 KiB admits every config the page mode admits
+    for t in g["trials"]:
+        if ct.ct_tvm_config_check(t["config"], 1, ct.CT_TVM_LIMITS_PAGE)[0] == 1:
+            assert ct.ct_tvm_config_check(t["config"], 1, ct.CT_TVM_LIMITS_GFX950)[0] == 1
+
+
+def test_tvm_space_agrees_with_the_oracle_on_random_points():
+    sp = O.tvm_tutorial_space(*(_GIST_SHAPE[:1] + _GIST_SHAPE[2:4] + (_GIST_SHAPE[4], _GIST_SHAPE[1])
+                                + _GIST_SHAPE[5:]))
+    rng = np.random.default_rng(77)
+    for idx in rng.integers(0, 10454400, 300):
+        st, got = ct.ct_tvm_space_entity(*_GIST_SHAPE, int(idx))
+        assert st == 0 and got == sp.entity_at(int(idx))
+        for stride in (1, 2):
+            fits, nbytes, _ = ct.ct_tvm_config_check(got, stride, ct.CT_TVM_LIMITS_GFX950)
+            assert nbytes == O.tvm_template_shared_bytes(got, stride)
+            assert fits == int(nbytes <= 160 * 1024 and O.tvm_template_threads(got) <= 1024)
+    # a strided, non-square shape: the space is the product of its knob lengths
+    shape = (2, 48, 13, 9, 40, 3, 1, 2, 1)
+    N, CI, H, W, CO, KH, KW, s, p = shape
+    OH, OW = (H + 2 * p - KH) // s + 1, (W + 2 * p - KW) // s + 1
+    want = (ct.ct_split_count(CO, 4) * ct.ct_split_count(OH, 4) * ct.ct_split_count(OW, 4)
+            * ct.ct_split_count(CI, 3) * ct.ct_split_count(KH, 3) * ct.ct_split_count(KW, 3) * 3 * 2)
+    assert ct.ct_tvm_space_size(*shape) == want
+    for idx in (0, 1, want // 3, want - 1):
+        st, cfg = ct.ct_tvm_space_entity(*shape, idx)
+        assert st == 0 and ct.ct_tvm_space_index(*shape, cfg) == idx
+
+
+def test_tvm_space_argument_errors():
+    assert ct.ct_tvm_space_size(0, 512, 7, 7, 512, 3, 3, 1, 1) == ct.CT_ERR_INVALID_ARG
+    st, _ = ct.ct_tvm_space_entity(*_GIST_SHAPE, 10454400)
+    assert st == ct.CT_ERR_INVALID_ARG
+    st, _ = ct.ct_tvm_space_entity(*_GIST_SHAPE, -1)
+    assert st == ct.CT_ERR_INVALID_ARG
+    g = _gist()
+    cfg = dict(g["best"]["config"])
+    cfg["tile_f"] = [8, 1, 64, 2]  # product 1024, not a split of 512
+    assert ct.ct_tvm_space_index(*_GIST_SHAPE, cfg) == -1
+    cfg = dict(g["best"]["config"], auto_unroll_max_step=7)
+    assert ct.ct_tvm_space_index(*_GIST_SHAPE, cfg) == -1
+    cfg = dict(g["best"]["config"], tile_rc=[64, 0, 8])
+    assert ct.ct_tvm_config_check(cfg, 1)[0] == ct.CT_ERR_INVALID_ARG
+    assert ct.ct_tvm_config_check(g["best"]["config"], 1, 5)[0] == ct.CT_ERR_INVALID_ARG
+    assert ct.ct_tvm_config_check(g["best"]["config"], 0)[0] == ct.CT_ERR_INVALID_ARG
