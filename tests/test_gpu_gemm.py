@@ -150,3 +150,78 @@ def test_gemm_full_size(name):
     ref, absacc = _ref(inp, g.epilogue)
     _check(C.cpu().numpy().astype(np.float64), ref, absacc, g.dtype, g.epilogue,
            f"{name} {ct.variants()[cfg.variant]['name']} (from cache: {from_cache})")
+
+
+# ---- the dedicated fp32 matrix-product kernel -------------------------------
+
+GEMM_F32 = "f32g_m128n128_w2x2_r2x2_k32"
+# (M, N, K), K a multiple of 32 (32 channels a stage, one split): one tile
+# and one stage; ragged M with N not a multiple of 4 (4-byte loads); ragged M
+# and N with 16-byte loads; a grid of whole XCD rectangles (8 x 8 tiles)
+GEMM_F32_SHAPES = [(128, 128, 32), (300, 263, 64), (257, 1000, 96), (1024, 1024, 128), (70, 4, 32)]
+
+
+def _gemm_f32_config(w):
+    cfgs = [c for c in legal_configs(w) if ct.variants()[c.variant]["name"] == GEMM_F32]
+    assert len(cfgs) == 1, [ct.variants()[c.variant]["name"] for c in legal_configs(w)][:5]
+    return cfgs[0]
+
+
+@pytest.mark.parametrize("epi", [ct.CT_EPI_NONE, ct.CT_EPI_BIAS, ct.CT_EPI_EXP_BIAS_RSQRT])
+@pytest.mark.parametrize("mnk", GEMM_F32_SHAPES, ids=lambda t: "x".join(map(str, t)))
+def test_gemm_f32_kernel_vs_oracle(mnk, epi):
+    M, N, K = mnk
+    g = wl.GemmWorkload("gemm_f32_kernel", 74, M, N, K, wl.F32, epi)
+    w = g.conv_view()
+    inp = wl.gemm_inputs(g)
+    ref, absacc = _ref(inp, epi)
+    x = to_dev(inp["B"].reshape(1, K, w.H, w.W), wl.F32)
+    k = to_dev(inp["A"].reshape(M, K, 1, 1), wl.F32)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    v = torch.from_numpy(inp["var"]).to(DEV)
+    cfg = _gemm_f32_config(w)
+    y = ct.conv2d(x, k, 1, 0, epilogue=epi, bias=b, var=v, config=cfg)
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy().astype(np.float64).reshape(M, N), ref, absacc, wl.F32, epi,
+           f"{GEMM_F32} {M}x{N}x{K} epi={epi}")
+
+
+@pytest.mark.parametrize("mnk", [(300, 263, 64), (257, 1000, 96)], ids=lambda t: "x".join(map(str, t)))
+def test_gemm_f32_kernel_integers_and_alignment(mnk):
+    """Small-integer operands: bit-exact, with 16-byte aligned operands and
+    with each operand one float off alignment (4-byte loads); the summation
+    order is the same, so all runs agree bit for bit."""
+    M, N, K = mnk
+    g = wl.GemmWorkload("gemm_f32_int", 75, M, N, K, wl.F32)
+    w = g.conv_view()
+    r = np.random.default_rng(76)
+    A = r.integers(-3, 4, (M, K)).astype(np.float32)
+    B = r.integers(-3, 4, (K, N)).astype(np.float32)
+    want = O.gemm(A.astype(np.float64), B.astype(np.float64))[0]
+    cfg = _gemm_f32_config(w)
+
+    def placed(a, offset):
+        buf = torch.empty(a.size + offset, device=DEV)
+        t = buf[offset:].view(a.shape)
+        t.copy_(torch.from_numpy(a))
+        return t
+
+    for ox, ow in ((0, 0), (1, 0), (0, 1), (1, 1)):
+        x = placed(B.reshape(1, K, w.H, w.W), ox)
+        k = placed(A.reshape(M, K, 1, 1), ow)
+        assert (x.data_ptr() % 16 == 0) == (ox == 0) and (k.data_ptr() % 16 == 0) == (ow == 0)
+        y = torch.full((1, M, w.H, w.W), float("nan"), device=DEV)
+        ct.conv2d(x, k, 1, 0, config=cfg, out=y)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy().astype(np.float64).reshape(M, N), want), (ox, ow)
+
+
+def test_gemm_f32_kernel_is_legal_only_where_it_applies():
+    """Batch 1, 1x1, stride 1, no padding, 32 channels a stage, one split."""
+    def names(w):
+        return {ct.variants()[c.variant]["name"] for c in legal_configs(w)}
+    assert GEMM_F32 in names(wl.ConvWorkload("g", 1, 1, 64, 8, 8, 64, 1, 1, 1, 0))
+    assert GEMM_F32 not in names(wl.ConvWorkload("g", 1, 2, 64, 8, 8, 64, 1, 1, 1, 0))   # batch 2
+    assert GEMM_F32 not in names(wl.ConvWorkload("g", 1, 1, 64, 8, 8, 64, 3, 3, 1, 1))   # 3x3
+    assert GEMM_F32 not in names(wl.ConvWorkload("g", 1, 1, 64, 8, 8, 64, 1, 1, 2, 0))   # stride 2
+    assert GEMM_F32 not in names(wl.ConvWorkload("g", 1, 1, 60, 8, 8, 64, 1, 1, 1, 0))   # no kc of 32
