@@ -64,6 +64,8 @@ def kernel_sources(kernel: str):
         main = "igemm_f32_sk16.hip"
     elif kernel.startswith(("f32sk_", "f32skx_")):
         main = "igemm_f32_sk.hip"
+    elif kernel.startswith(("hgf16_", "hgbf16_")):
+        main = "igemm_f16_gemm.hip"
     elif kernel.startswith("f32g_"):
         main = "igemm_f32_gemm.hip"
     elif kernel.startswith("f32_"):

@@ -95,6 +95,7 @@ const IgemmVariant* igemm_f32_skt_variants(int* count);
 const IgemmVariant* igemm_f16_variants(int* count);
 const IgemmVariant* igemm_f16v2_variants(int* count);
 const IgemmVariant* igemm_f32_gemm_variants(int* count);
+const IgemmVariant* igemm_f16_gemm_variants(int* count);
 
 // Half-precision prepared filter: wp [CO][CI64/8][T][8] = w [CO][CI][T]
 // regrouped into 16-byte records of 8 channels at one tap, zeros past CI

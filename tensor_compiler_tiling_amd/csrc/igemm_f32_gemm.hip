@@ -28,6 +28,7 @@
 #include "igemm_common.hpp"
 
 #include <atomic>
+#include <type_traits>
 
 namespace ct {
 
@@ -224,22 +225,35 @@ __global__ __launch_bounds__(kNT) void igemm_f32_gemm_kernel(GemmParams p) {
         __syncthreads();                // and everybody's; this stage's reads are done
     }
 
-    // ---- epilogue and store (C: row 8*(r/4) + 4*(lane/32) + r%4, col lane%32)
+    // ---- epilogue and store (C: row 8*(r/4) + 4*(lane/32) + r%4, col lane%32).
+    // A lane's rows are m0 + wm*64 + 4*(lane/32) + (a wave-uniform offset),
+    // its columns n0 + wn*64 + lane%32 + 32 rn: one per-lane base address,
+    // a uniform row offset and an immediate column offset per store.
+    const int lrow = m0 + wm * 64 + 4 * lh;
+    const int lcol = n0 + wn * 64 + lj;
+    float* const cl = p.c + (long long)lrow * p.N + lcol;
+    // One branch-free store loop for every epilogue: the tables hold bias 0
+    // and scale 1 where the epilogue has none, and exp is selected by a
+    // uniform flag (a branch on the epilogue around the stores made the
+    // compiler copy accumulators out of their registers and spill).
+    const bool ex = p.epilogue == EPI_EXP_BIAS_RSQRT;
 #pragma unroll
     for (int rm = 0; rm < 2; ++rm) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const int row = wm * 64 + rm * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            if (m0 + row >= p.M) continue;
+            const int ro = rm * 32 + 8 * (r >> 2) + (r & 3);  // wave-uniform
+            if (lrow + ro >= p.M) continue;
+            const int row = lrow - m0 + ro;
             const float eb = e_bias[row], er = e_rs[row];
+            float* const crow = cl + (long long)ro * p.N;
 #pragma unroll
             for (int rn = 0; rn < 2; ++rn) {
-                const int col = n0 + wn * 64 + rn * 32 + lj;
-                if (col >= p.N) continue;
+                if (lcol + rn * 32 >= p.N) continue;
+                const float v = acc[rm][rn][r] + eb;
                 // streamed out: the results are not read again by this launch
-                __builtin_nontemporal_store(apply_epilogue(p.epilogue, acc[rm][rn][r], eb, er),
-                                            &p.c[(long long)(m0 + row) * p.N + col]);
+                __builtin_nontemporal_store(ex ? dev_exp(v) * er : v, crow + rn * 32);
             }
+            __builtin_amdgcn_sched_barrier(0);  // one row's values at a time
         }
     }
 }

@@ -143,7 +143,7 @@ const std::vector<Variant>& variants() {
             d.ig = nullptr;
             out.push_back(d);
         }
-        int n32 = 0, n16 = 0, nsk = 0, nsk16 = 0, nh2 = 0, nskc = 0, nskt = 0, ngm = 0;
+        int n32 = 0, n16 = 0, nsk = 0, nsk16 = 0, nh2 = 0, nskc = 0, nskt = 0, ngm = 0, nhgm = 0;
         const IgemmVariant* t32 = igemm_f32_variants(&n32);
         const IgemmVariant* tsk = igemm_f32_sk_variants(&nsk);
         const IgemmVariant* tsk16 = igemm_f32_sk16_variants(&nsk16);
@@ -152,6 +152,7 @@ const std::vector<Variant>& variants() {
         const IgemmVariant* t16 = igemm_f16_variants(&n16);
         const IgemmVariant* th2 = igemm_f16v2_variants(&nh2);
         const IgemmVariant* tgm = igemm_f32_gemm_variants(&ngm);
+        const IgemmVariant* thgm = igemm_f16_gemm_variants(&nhgm);
         auto add = [&](const IgemmVariant* t, int n) {
             for (int i = 0; i < n; ++i) {
                 Variant v{};
@@ -182,6 +183,7 @@ const std::vector<Variant>& variants() {
         add(t16, n16);
         add(th2, nh2);
         add(tgm, ngm);  // last: the flat indices of the earlier points stay as they were
+        add(thgm, nhgm);
         return out;
     }();
     return v;

@@ -152,76 +152,120 @@ def test_gemm_full_size(name):
            f"{name} {ct.variants()[cfg.variant]['name']} (from cache: {from_cache})")
 
 
-# ---- the dedicated fp32 matrix-product kernel -------------------------------
+# ---- the dedicated matrix-product kernels (no split, whole-K tiles) ---------
 
-GEMM_F32 = "f32g_m128n128_w2x2_r2x2_k32"
+GEMM_KERNELS = {wl.F32: "f32g_m128n128_w2x2_r2x2_k32", wl.F16: "hgf16_m256n256_w2x2_r4x4_k32",
+                wl.BF16: "hgbf16_m256n256_w2x2_r4x4_k32"}
 # (M, N, K), K a multiple of 32 (32 channels a stage, one split): one tile
-# and one stage; ragged M with N not a multiple of 4 (4-byte loads); ragged M
-# and N with 16-byte loads; a grid of whole XCD rectangles (8 x 8 tiles)
-GEMM_F32_SHAPES = [(128, 128, 32), (300, 263, 64), (257, 1000, 96), (1024, 1024, 128), (70, 4, 32)]
+# and one stage; ragged M with N not a multiple of 4 (narrow loads); ragged
+# M and N with the widest loads; a grid of whole XCD rectangles; a single
+# narrow column block; an odd N (2-byte loads in half precision)
+GEMM_KERNEL_SHAPES = [(128, 128, 32), (300, 263, 64), (257, 1000, 96), (1024, 1024, 128), (70, 4, 32),
+                      (260, 517, 64)]
 
 
-def _gemm_f32_config(w):
-    cfgs = [c for c in legal_configs(w) if ct.variants()[c.variant]["name"] == GEMM_F32]
-    assert len(cfgs) == 1, [ct.variants()[c.variant]["name"] for c in legal_configs(w)][:5]
+def _kernel_config(w, dtype, name=None):
+    name = name or GEMM_KERNELS[dtype]
+    cfgs = [c for c in legal_configs(w) if ct.variants()[c.variant]["name"] == name]
+    assert len(cfgs) == 1, (name, len(cfgs))
     return cfgs[0]
 
 
 @pytest.mark.parametrize("epi", [ct.CT_EPI_NONE, ct.CT_EPI_BIAS, ct.CT_EPI_EXP_BIAS_RSQRT])
-@pytest.mark.parametrize("mnk", GEMM_F32_SHAPES, ids=lambda t: "x".join(map(str, t)))
-def test_gemm_f32_kernel_vs_oracle(mnk, epi):
+@pytest.mark.parametrize("mnk", GEMM_KERNEL_SHAPES, ids=lambda t: "x".join(map(str, t)))
+@pytest.mark.parametrize("dtype", [wl.F32, wl.F16, wl.BF16])
+def test_gemm_kernel_vs_oracle(dtype, mnk, epi):
     M, N, K = mnk
-    g = wl.GemmWorkload("gemm_f32_kernel", 74, M, N, K, wl.F32, epi)
+    g = wl.GemmWorkload("gemm_kernel", 74, M, N, K, dtype, epi)
     w = g.conv_view()
     inp = wl.gemm_inputs(g)
     ref, absacc = _ref(inp, epi)
-    x = to_dev(inp["B"].reshape(1, K, w.H, w.W), wl.F32)
-    k = to_dev(inp["A"].reshape(M, K, 1, 1), wl.F32)
+    x = to_dev(inp["B"].reshape(1, K, w.H, w.W), dtype)
+    k = to_dev(inp["A"].reshape(M, K, 1, 1), dtype)
     b = torch.from_numpy(inp["bias"]).to(DEV)
     v = torch.from_numpy(inp["var"]).to(DEV)
-    cfg = _gemm_f32_config(w)
+    cfg = _kernel_config(w, dtype)
     y = ct.conv2d(x, k, 1, 0, epilogue=epi, bias=b, var=v, config=cfg)
     torch.cuda.synchronize()
-    _check(y.cpu().numpy().astype(np.float64).reshape(M, N), ref, absacc, wl.F32, epi,
-           f"{GEMM_F32} {M}x{N}x{K} epi={epi}")
+    _check(y.cpu().numpy().astype(np.float64).reshape(M, N), ref, absacc, dtype, epi,
+           f"{GEMM_KERNELS[dtype]} {M}x{N}x{K} epi={epi}")
 
 
-@pytest.mark.parametrize("mnk", [(300, 263, 64), (257, 1000, 96)], ids=lambda t: "x".join(map(str, t)))
-def test_gemm_f32_kernel_integers_and_alignment(mnk):
+@pytest.mark.parametrize("mnk", [(300, 263, 64), (257, 1000, 96), (260, 518, 64)],
+                         ids=lambda t: "x".join(map(str, t)))
+@pytest.mark.parametrize("dtype", [wl.F32, wl.F16, wl.BF16])
+def test_gemm_kernel_integers_and_alignment(dtype, mnk):
     """Small-integer operands: bit-exact, with 16-byte aligned operands and
-    with each operand one float off alignment (4-byte loads); the summation
-    order is the same, so all runs agree bit for bit."""
+    with each operand one element off alignment (narrower loads); the
+    summation order is the same, so all runs agree bit for bit."""
     M, N, K = mnk
-    g = wl.GemmWorkload("gemm_f32_int", 75, M, N, K, wl.F32)
+    g = wl.GemmWorkload("gemm_int", 75, M, N, K, dtype)
     w = g.conv_view()
     r = np.random.default_rng(76)
     A = r.integers(-3, 4, (M, K)).astype(np.float32)
     B = r.integers(-3, 4, (K, N)).astype(np.float32)
     want = O.gemm(A.astype(np.float64), B.astype(np.float64))[0]
-    cfg = _gemm_f32_config(w)
+    cfg = _kernel_config(w, dtype)
+    tdt = {wl.F32: torch.float32, wl.F16: torch.float16, wl.BF16: torch.bfloat16}[dtype]
 
     def placed(a, offset):
-        buf = torch.empty(a.size + offset, device=DEV)
+        buf = torch.empty(a.size + offset, dtype=tdt, device=DEV)
         t = buf[offset:].view(a.shape)
-        t.copy_(torch.from_numpy(a))
+        t.copy_(torch.from_numpy(a).to(tdt))
         return t
 
-    for ox, ow in ((0, 0), (1, 0), (0, 1), (1, 1)):
+    for ox, ow in ((0, 0), (1, 0), (0, 1), (1, 1), (2, 2)):
         x = placed(B.reshape(1, K, w.H, w.W), ox)
         k = placed(A.reshape(M, K, 1, 1), ow)
-        assert (x.data_ptr() % 16 == 0) == (ox == 0) and (k.data_ptr() % 16 == 0) == (ow == 0)
         y = torch.full((1, M, w.H, w.W), float("nan"), device=DEV)
         ct.conv2d(x, k, 1, 0, config=cfg, out=y)
         torch.cuda.synchronize()
         assert np.array_equal(y.cpu().numpy().astype(np.float64).reshape(M, N), want), (ox, ow)
 
 
-def test_gemm_f32_kernel_is_legal_only_where_it_applies():
+@pytest.mark.parametrize("dtype", [wl.F32, wl.F16, wl.BF16])
+def test_gemm_kernel_is_legal_only_where_it_applies(dtype):
     """Batch 1, 1x1, stride 1, no padding, 32 channels a stage, one split."""
-    def names(w):
-        return {ct.variants()[c.variant]["name"] for c in legal_configs(w)}
-    assert GEMM_F32 in names(wl.ConvWorkload("g", 1, 1, 64, 8, 8, 64, 1, 1, 1, 0))
-    assert GEMM_F32 not in names(wl.ConvWorkload("g", 1, 2, 64, 8, 8, 64, 1, 1, 1, 0))   # batch 2
-    assert GEMM_F32 not in names(wl.ConvWorkload("g", 1, 1, 64, 8, 8, 64, 3, 3, 1, 1))   # 3x3
-    assert GEMM_F32 not in names(wl.ConvWorkload("g", 1, 1, 64, 8, 8, 64, 1, 1, 2, 0))   # stride 2
-    assert GEMM_F32 not in names(wl.ConvWorkload("g", 1, 1, 60, 8, 8, 64, 1, 1, 1, 0))   # no kc of 32
+    name = GEMM_KERNELS[dtype]
+
+    def names(*shape):
+        return {ct.variants()[c.variant]["name"] for c in legal_configs(wl.ConvWorkload("g", 1, *shape, dtype))}
+    assert name in names(1, 64, 8, 8, 64, 1, 1, 1, 0)
+    assert name not in names(2, 64, 8, 8, 64, 1, 1, 1, 0)   # batch 2
+    assert name not in names(1, 64, 8, 8, 64, 3, 3, 1, 1)   # 3x3
+    assert name not in names(1, 64, 8, 8, 64, 1, 1, 2, 0)   # stride 2
+    assert name not in names(1, 60, 8, 8, 64, 1, 1, 1, 0)   # no split of 60 has 32 channels a stage
+
+
+# the half-precision kernel with 64 channels a stage (four instruction steps)
+HALF_K64 = {wl.F16: "hgf16_m256n256_w2x2_r4x4_k64", wl.BF16: "hgbf16_m256n256_w2x2_r4x4_k64"}
+
+
+@pytest.mark.parametrize("epi", [ct.CT_EPI_NONE, ct.CT_EPI_EXP_BIAS_RSQRT])
+@pytest.mark.parametrize("mnk", [(256, 256, 64), (300, 263, 64), (257, 1000, 192), (1024, 1024, 128)],
+                         ids=lambda t: "x".join(map(str, t)))
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+def test_gemm_half_k64_vs_oracle(dtype, mnk, epi):
+    M, N, K = mnk
+    g = wl.GemmWorkload("gemm_k64", 77, M, N, K, dtype, epi)
+    w = g.conv_view()
+    inp = wl.gemm_inputs(g)
+    ref, absacc = _ref(inp, epi)
+    x = to_dev(inp["B"].reshape(1, K, w.H, w.W), dtype)
+    k = to_dev(inp["A"].reshape(M, K, 1, 1), dtype)
+    b = torch.from_numpy(inp["bias"]).to(DEV)
+    v = torch.from_numpy(inp["var"]).to(DEV)
+    cfg = _kernel_config(w, dtype, HALF_K64[dtype])
+    y = ct.conv2d(x, k, 1, 0, epilogue=epi, bias=b, var=v, config=cfg)
+    torch.cuda.synchronize()
+    _check(y.cpu().numpy().astype(np.float64).reshape(M, N), ref, absacc, dtype, epi,
+           f"{HALF_K64[dtype]} {M}x{N}x{K} epi={epi}")
+    # small integers: bit-exact
+    r = np.random.default_rng(78)
+    A = r.integers(-3, 4, (M, K)).astype(np.float32)
+    B = r.integers(-3, 4, (K, N)).astype(np.float32)
+    y = ct.conv2d(to_dev(wl.to_dtype(B.reshape(1, K, w.H, w.W), dtype), dtype),
+                  to_dev(wl.to_dtype(A.reshape(M, K, 1, 1), dtype), dtype), 1, 0, config=cfg)
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64).reshape(M, N),
+                          O.gemm(A.astype(np.float64), B.astype(np.float64))[0])
