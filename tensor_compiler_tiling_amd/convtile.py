@@ -25,6 +25,8 @@ CT_ERR_IO = -5
 CT_ERR_TUNE_FAILED = -6
 
 CT_F32, CT_F16, CT_BF16 = 0, 1, 2
+# bytes of the no-allocation entry point's fixed scratch (partials and filter copy)
+CT_NOALLOC_SCRATCH_BYTES = 16 << 20
 CT_EPI_NONE, CT_EPI_BIAS, CT_EPI_EXP_BIAS_RSQRT = 0, 1, 2
 CT_BC_EXP = 0
 CT_BC_AUTO, CT_BC_CHANNEL, CT_BC_FLAT = 0, 1, 2

@@ -114,19 +114,23 @@ def test_noalloc_captures_without_an_earlier_launch():
 
 
 def test_noalloc_rejects_configs_beyond_its_scratch():
-    """The tuned 2048^3 fp32 product splits its reduction 8 ways (128 MiB of
-    partials), beyond the fixed scratch, so the call fails before any launch;
-    a call that fits still works afterwards."""
-    for g in (wl.GEMM_WORKLOADS["gemm_f32_m2048_n2048_k2048_epi"],):
-        w = g.conv_view()
-        tdt = torch.float32 if w.dtype == wl.F32 else torch.float16
-        x = torch.zeros((w.N, w.CI, w.H, w.W), dtype=tdt, device=DEV)
-        k = torch.zeros((w.CO, w.CI, w.KH, w.KW), dtype=tdt, device=DEV)
-        b = torch.zeros(w.CO, device=DEV)
-        v = torch.ones(w.CO, device=DEV)
-        y = torch.empty((w.N, w.CO, w.OH, w.OW), device=DEV)
-        st = _call(ct.ct_conv2d_nchw_fwd_noalloc, w, x, k, b, v, y)
-        msg = ct.library().ct_last_error().decode()
-        say(f"  {g.name}: status {st}: {msg}")
-        assert st == ct.CT_ERR_UNSUPPORTED and "above the" in msg
+    """A half-precision 3x3 layer whose filter the launch reorders into its
+    scratch (1024 x 1024 x 9 halves: 18.9 MB, beyond the fixed scratch), so
+    the call fails before any launch; a call that fits still works
+    afterwards."""
+    w = wl.ConvWorkload("noalloc_big_filter", 90, 1, 1024, 16, 16, 1024, 3, 3, 1, 1, wl.F16)
+    st, cfg, _ = ct.ct_conv2d_query(*w.shape_args(), ct.CT_F16, w.epilogue)
+    assert st == 0
+    name = ct.variants()[cfg.variant]["name"]
+    assert name.startswith("h2"), name  # the reordering kernel is the one chosen
+    assert 2 * 1024 * 1024 * 9 > ct.CT_NOALLOC_SCRATCH_BYTES
+    x = torch.zeros((w.N, w.CI, w.H, w.W), dtype=torch.float16, device=DEV)
+    k = torch.zeros((w.CO, w.CI, w.KH, w.KW), dtype=torch.float16, device=DEV)
+    b = torch.zeros(w.CO, device=DEV)
+    v = torch.ones(w.CO, device=DEV)
+    y = torch.empty((w.N, w.CO, w.OH, w.OW), device=DEV)
+    st = _call(ct.ct_conv2d_nchw_fwd_noalloc, w, x, k, b, v, y)
+    msg = ct.library().ct_last_error().decode()
+    say(f"  {w.name} ({name}): status {st}: {msg}")
+    assert st == ct.CT_ERR_UNSUPPORTED and "above the" in msg
     _check_pair(wl.CONV_WORKLOADS["resnet_c64_14x14_k3"])
