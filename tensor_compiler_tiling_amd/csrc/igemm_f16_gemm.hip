@@ -10,23 +10,25 @@
 // reduction, each wave a 128 x 128 block (4 x 4 instruction tiles of 32 x
 // 32): each instruction then reads half a KB of operand fragments from LDS,
 // half of what a 64 x 64 wave block needs.  The reduction runs in stages of
-// KS halves:
-//  - both operand tiles of a stage go from memory straight into LDS (loads
-//    that write LDS: 16 or 4 bytes a lane, the widest the operands'
-//    alignment and K, N allow; with 2-byte aligned operands or an odd K or N
-//    through registers instead, since a 2-byte load that writes LDS fills 4
-//    bytes of it a lane) into the other of two LDS copies.  The compiler
-//    waits for every load in flight before a transposing LDS read, so a
-//    stage first reads all its B fragments (the transposing reads), then
-//    issues the next stage's loads, which thus have the whole stage to land,
-//    and reads its A fragments (plain 16-byte reads) through two register
-//    sets, step t+1's while step t's instructions run; one barrier ends a
-//    stage;
+// KS halves, through two LDS copies.  Two forms stage the operand tiles:
+//  - with 16-byte aligned operands, K and N multiples of 8 and KS = 64, the
+//    register-staged form below (plain loads into registers, LDS writes by
+//    the waves, spread between the matrix instructions);
+//  - otherwise the first form: loads that write LDS directly (16 or 4 bytes
+//    a lane, the widest the operands' alignment and K, N allow; with 2-byte
+//    aligned operands or an odd K or N through registers, since a 2-byte
+//    load that writes LDS fills 4 bytes of it a lane).  The compiler waits
+//    for every such load in flight before a transposing LDS read of the
+//    same LDS object, so a stage first reads all its B fragments (the
+//    transposing reads), then issues the next stage's loads, which thus have
+//    the whole stage to land, and reads its A fragments (plain 16-byte
+//    reads) through two register sets, step t+1's while step t's
+//    instructions run; one barrier ends a stage.
+// Layouts, shared by both forms:
 //  - A is held [m][KS] in 16-byte chunks (8 k), chunk q of row m stored at
-//    q ^ rot(m): rot = (m/2) mod 4 for KS = 32 (64-byte rows, so row parity
-//    already splits 128 bytes of banks in two), m mod 8 for KS = 64 (128-byte
-//    rows): a lane's A operand (8 consecutive k of its row) is one 16-byte
-//    read, and the 8 lanes an LDS cycle serves hit 8 different bank groups;
+//    q ^ rot(m) (below): a lane's A operand (8 consecutive k of its row) is
+//    one 16-byte read, and the 16 lanes an LDS cycle serves hit 16 different
+//    bank groups;
 //  - B is held [k][256 n] in 16-byte chunks (8 n), chunk c of row k stored at
 //    c ^ (2 (k mod 4)).  The instruction wants 8 consecutive k of one column
 //    per lane: two transposing reads (ds_read_b64_tr_b16) give them, 4 k
@@ -102,9 +104,71 @@ struct HG {
     static constexpr int COPY = A_H + B_H;            // halves of one LDS copy
     static constexpr int LDS = 2 * COPY * 2 + 2 * kTM * 4;  // bytes
     static_assert(KS == 32 || KS == 64, "the chunk rotations below");
-    // A row m's rotation of its chunks
-    static __device__ __forceinline__ int rot(int m) { return KS == 32 ? (m >> 1) & 3 : m & 7; }
+    // A row m's rotation of its chunks.  LDS serves 16 lanes of a 16-byte
+    // read a cycle from 64 banks (256 bytes): the 16 rows m .. m+15 of one
+    // read sit at 256/(2 KS) row offsets a bank line, and the rotation gives
+    // rows with the same offset different chunks.
+    static __device__ __forceinline__ int rot(int m) { return KS == 32 ? (m >> 2) & 3 : (m >> 1) & 7; }
 };
+
+// The tile of this workgroup: XCD x = blockIdx % 8 takes one rectangle of
+// tiles (row tiles fastest), or, without XCD groups, a run of column tiles.
+// False for the padding of the grid (uniform over the workgroup).
+__device__ __forceinline__ bool block_tile(const HGemmParams& p, int& m0, int& n0) {
+    const uint32_t bx = blockIdx.x;
+    const uint32_t x = bx & 7, l = bx >> 3;
+    const uint32_t lq = fdiv(l, p.fd_lm);
+    const int lr = (int)(l - lq * p.fd_lm.d);
+    int tm, tn;
+    if (p.cgl >= 0) {
+        tm = (int)(x >> p.cgl) * (int)p.fd_lm.d + lr;
+        tn = (int)(x & ((1u << p.cgl) - 1)) * (p.tiles_n >> p.cgl) + (int)lq;
+    } else {
+        tm = lr;
+        tn = (int)x * (((p.tiles_n + 7) & ~7) >> 3) + (int)lq;
+        if (tn >= p.tiles_n) return false;
+    }
+    m0 = tm * kTM;
+    n0 = tn * kTN;
+    return true;
+}
+
+// Epilogue and store of a wave's 128 x 128 block (C: row 8*(r/4) +
+// 4*(lane/32) + r%4, column lane%32 of each 32 x 32 instruction tile).  A
+// lane's rows are m0 + wm*128 + 4*(lane/32) + (a wave-uniform offset), its
+// columns n0 + wn*128 + lane%32 + 32 rn: one per-lane base address, a uniform
+// row offset and an immediate column offset per store.  One branch-free store
+// loop serves every epilogue: the tables hold bias 0 and scale 1 where the
+// epilogue has none, and exp is selected by a uniform flag (a branch on the
+// epilogue around the stores made the compiler copy accumulators out of
+// their registers and spill).
+__device__ __forceinline__ void store_block(const HGemmParams& p, floatx16 (&acc)[4][4], int m0, int n0, int wm,
+                                            int wn, int lane, const float* e_bias, const float* e_rs) {
+    const int lj = lane & 31, lh = lane >> 5;
+    const int lrow = m0 + wm * 128 + 4 * lh;
+    const int lcol = n0 + wn * 128 + lj;
+    float* const cl = p.c + (long long)lrow * p.N + lcol;
+    const bool ex = p.epilogue == EPI_EXP_BIAS_RSQRT;
+#pragma unroll
+    for (int rm = 0; rm < 4; ++rm) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int ro = rm * 32 + 8 * (r >> 2) + (r & 3);  // wave-uniform
+            if (lrow + ro >= p.M) continue;
+            const int row = lrow - m0 + ro;
+            const float eb = e_bias[row], er = e_rs[row];
+            float* const crow = cl + (long long)ro * p.N;
+#pragma unroll
+            for (int rn = 0; rn < 4; ++rn) {
+                if (lcol + rn * 32 >= p.N) continue;
+                const float v = acc[rm][rn][r] + eb;
+                // streamed out: the results are not read again by this launch
+                __builtin_nontemporal_store(ex ? dev_exp(v) * er : v, crow + rn * 32);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one row's values at a time
+        }
+    }
+}
 
 // One wave fills 64 consecutive LDS slots of CB (16 or 4) bytes from
 // lane_off (bytes) within r, lane l the l-th; lds is wave-uniform.
@@ -151,21 +215,8 @@ __global__ __launch_bounds__(kNT) void igemm_h_gemm_kernel(HGemmParams p) {
     const int wm = wave & 1, wn = wave >> 1;
     const int lj = lane & 31, lh = lane >> 5;
 
-    // ---- workgroup -> tile (XCD rectangles, as in the fp32 product) --------
-    const uint32_t bx = blockIdx.x;
-    const uint32_t x = bx & 7, l = bx >> 3;
-    const uint32_t lq = fdiv(l, p.fd_lm);
-    const int lr = (int)(l - lq * p.fd_lm.d);
-    int tm, tn;
-    if (p.cgl >= 0) {
-        tm = (int)(x >> p.cgl) * (int)p.fd_lm.d + lr;
-        tn = (int)(x & ((1u << p.cgl) - 1)) * (p.tiles_n >> p.cgl) + (int)lq;
-    } else {
-        tm = lr;
-        tn = (int)x * (((p.tiles_n + 7) & ~7) >> 3) + (int)lq;
-        if (tn >= p.tiles_n) return;  // padding of the grid: uniform over the workgroup
-    }
-    const int m0 = tm * kTM, n0 = tn * kTN;
+    int m0, n0;
+    if (!block_tile(p, m0, n0)) return;
 
     // ---- epilogue values of row tid, loaded first
     float e_b = 0.0f, e_v = 0.0f;
@@ -300,37 +351,184 @@ __global__ __launch_bounds__(kNT) void igemm_h_gemm_kernel(HGemmParams p) {
         __syncthreads();                // and everybody's; this stage's reads are done
     }
 
-    // ---- epilogue and store (C: row 8*(r/4) + 4*(lane/32) + r%4, col lane%32).
-    // A lane's rows are m0 + wm*128 + 4*(lane/32) + (a wave-uniform offset),
-    // its columns n0 + wn*128 + lane%32 + 32 rn: one per-lane base address,
-    // a uniform row offset and an immediate column offset per store.
-    const int lrow = m0 + wm * 128 + 4 * lh;
-    const int lcol = n0 + wn * 128 + lj;
-    float* const cl = p.c + (long long)lrow * p.N + lcol;
-    // One branch-free store loop for every epilogue: the tables hold bias 0
-    // and scale 1 where the epilogue has none, and exp is selected by a
-    // uniform flag (a branch on the epilogue around the stores made the
-    // compiler copy accumulators out of their registers and spill).
-    const bool ex = p.epilogue == EPI_EXP_BIAS_RSQRT;
+    store_block(p, acc, m0, n0, wm, wn, lane, e_bias, e_rs);
+}
+
+// Register-staged form, for 16-byte aligned operands with K and N multiples
+// of 8 (every 16-byte chunk of a tile row either wholly inside or wholly
+// past the matrix) and stages of 64 channels.  Loads that write LDS directly hold up the wave that
+// issues them (on this chip each costs the issuing wave about as long as
+// the whole CU's LDS-load queue ahead of it), and with one wave a SIMD that
+// wave is the one that issues the matrix instructions.  Plain 16-byte loads
+// into registers and 16-byte LDS writes by the waves themselves cost the
+// matrix pipe almost nothing, so this form stages through registers:
+//  - a thread holds 2 KS/8 chunks of 16 bytes (KS/8 of A, KS/8 of B) of the
+//    next stage;
+//  - a stage's STEPS steps each run 16 instructions with one LDS access or
+//    load between consecutive instructions: the fragment reads of the next
+//    step (12 reads: 4 of A, 8 transposing of B), and in the two steps before
+//    the last, each held chunk is written to the other copy and its register
+//    at once reloaded with the matching chunk of the stage after next (so a
+//    load has a whole stage to land, and the writes are spread over two
+//    steps);
+//  - one barrier a stage, after the writes: the last step then already reads
+//    the next stage's first fragments from the other copy, so no step waits
+//    for its fragments after a barrier;
+//  - past the last stage the loads read zeros (an empty buffer range) into a
+//    copy that is no longer read, which keeps the loop free of branches.
+template <int DT, int KS>
+__global__ __launch_bounds__(kNT) void igemm_h_gemm_rs_kernel(HGemmParams p) {
+    asm volatile("" ::"s"(p.a), "s"(p.fd_lm.d));  // both argument lines in one batch
+    using C = HG<KS>;
+    constexpr int LPO = KS / 8;       // 16-byte chunks a thread holds, per operand
+    constexpr int STEPS = KS / 16;    // instruction steps a stage
+    constexpr int AMJ = 2048 / KS;    // A rows between a thread's chunks
+    static_assert(STEPS >= 3, "the writes take the two steps before the last");
+    // two LDS copies as two objects, named statically by the stage loop
+    __shared__ __align__(16) uint16_t lds0[C::COPY];
+    __shared__ __align__(16) uint16_t lds1[C::COPY];
+    __shared__ float e_bias[kTM], e_rs[kTM];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lj = lane & 31, lh = lane >> 5;
+
+    int m0, n0;
+    if (!block_tile(p, m0, n0)) return;
+
+    // ---- epilogue values of row tid, loaded first
+    float e_b = 0.0f, e_v = 0.0f;
+    const bool e_row = m0 + tid < p.M;
+    if (e_row && p.epilogue != EPI_NONE) e_b = p.bias[m0 + tid];
+    if (e_row && p.epilogue == EPI_EXP_BIAS_RSQRT) e_v = p.var[m0 + tid];
+
+    // ---- a thread's chunks.  A chunk j: row am + j*AMJ, chunk aq of the
+    // row's KS/8, stored at chunk aq ^ rot(row) (rot(row) = rot(am): AMJ is
+    // a multiple of the rotation's period).  B chunk j: row bk + 8 j of the
+    // stage, chunk bc of the row's 32, stored at bc ^ (2 (row % 4)).
+    const int aq = tid % (KS / 8), am = tid / (KS / 8);
+    const int bc = tid & 31, bk = tid >> 5;
+    unsigned aoff[LPO], boff[LPO];  // bytes from the stage's tile origin; past the matrix: kBufOut
+#pragma unroll
+    for (int j = 0; j < LPO; ++j) {
+        aoff[j] = (m0 + am + j * AMJ < p.M) ? (unsigned)(((am + j * AMJ) * p.K + aq * 8) * 2) : kBufOut;
+        boff[j] = (n0 + bc * 8 < p.N) ? (unsigned)(((bk + 8 * j) * p.N + bc * 8) * 2) : kBufOut;
+    }
+    const int aw = am * KS + ((aq ^ C::rot(am)) << 3);            // + j * AMJ * KS halves
+    const int bw = C::A_H + bk * kTN + ((bc ^ (2 * (bk & 3))) << 3);  // + j * 8 * kTN halves
+    const long long a_bytes = (long long)p.M * p.K * 2, b_bytes = (long long)p.K * p.N * 2;
+    const int NS = p.K / KS;
+
+    uint4v g[2 * LPO];
+    __amdgpu_buffer_rsrc_t ar, br;
+    auto stage_rsrc = [&](int st) {
+        const bool live = st < NS;
+        const long long abase = live ? (long long)m0 * p.K + (long long)st * KS : 0;
+        const long long bbase = live ? (long long)st * KS * p.N + n0 : 0;
+        const int anrec = __builtin_amdgcn_readfirstlane(live ? (int)(a_bytes - 2 * abase) : 0);
+        const int bnrec = __builtin_amdgcn_readfirstlane(live ? (int)(b_bytes - 2 * bbase) : 0);
+        ar = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.a + abase), 0, anrec, kBufRaw);
+        br = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.b + bbase), 0, bnrec, kBufRaw);
+    };
+    auto load_one = [&](int i) {
+        if (i < LPO) g[i] = __builtin_amdgcn_raw_buffer_load_b128(ar, aoff[i], 0, 0);
+        else g[i] = __builtin_amdgcn_raw_buffer_load_b128(br, boff[i - LPO], 0, 0);
+    };
+    auto write_one = [&](uint16_t* cp, int i) {
+        if (i < LPO) *reinterpret_cast<uint4v*>(cp + aw + i * AMJ * KS) = g[i];
+        else *reinterpret_cast<uint4v*>(cp + bw + (i - LPO) * 8 * kTN) = g[i];
+    };
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // fragment addresses (halves within a copy), as in the first form
+    int arow[4], arot[4];
 #pragma unroll
     for (int rm = 0; rm < 4; ++rm) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int ro = rm * 32 + 8 * (r >> 2) + (r & 3);  // wave-uniform
-            if (lrow + ro >= p.M) continue;
-            const int row = lrow - m0 + ro;
-            const float eb = e_bias[row], er = e_rs[row];
-            float* const crow = cl + (long long)ro * p.N;
-#pragma unroll
-            for (int rn = 0; rn < 4; ++rn) {
-                if (lcol + rn * 32 >= p.N) continue;
-                const float v = acc[rm][rn][r] + eb;
-                // streamed out: the results are not read again by this launch
-                __builtin_nontemporal_store(ex ? dev_exp(v) * er : v, crow + rn * 32);
-            }
-            __builtin_amdgcn_sched_barrier(0);  // one row's values at a time
-        }
+        const int row = wm * 128 + rm * 32 + lj;
+        arow[rm] = row * KS;
+        arot[rm] = C::rot(row);
     }
+    const int L = lane & 15;
+    const int brow = 8 * lh + (L >> 2);
+    int bcol[4];
+#pragma unroll
+    for (int rn = 0; rn < 4; ++rn) {
+        const int n = wn * 128 + rn * 32 + 16 * (lj >> 4) + 4 * (L & 3);
+        bcol[rn] = ((((n >> 3) ^ (2 * (brow & 3)))) << 3) | (n & 7);
+    }
+    // read r (0..11) of step t's fragments from copy cp: A rows first, then
+    // the two transposing reads of each B column block
+    uint4v a[2][4];
+    uint2v bl[2][4], bh[2][4];
+    auto read_one = [&](const uint16_t* cp, int t, int set, int r) {
+        if (r < 4) {
+            a[set][r] = *reinterpret_cast<const uint4v*>(cp + arow[r] + (((2 * t + lh) ^ arot[r]) << 3));
+        } else {
+            const int rn = (r - 4) >> 1;
+            const uint16_t* q = cp + C::A_H + (16 * t + brow + 4 * ((r - 4) & 1)) * kTN + bcol[rn];
+            const uint2v v = __builtin_bit_cast(uint2v, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)q));
+            if ((r & 1) == 0) bl[set][rn] = v;
+            else bh[set][rn] = v;
+        }
+    };
+
+    // ---- prologue: stage 0 into copy 0, stage 1 into registers
+    stage_rsrc(0);
+#pragma unroll
+    for (int i = 0; i < 2 * LPO; ++i) load_one(i);
+    e_bias[tid] = e_b;
+    e_rs[tid] = (e_row && p.epilogue == EPI_EXP_BIAS_RSQRT) ? dev_rsqrt(e_v + p.eps) : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 2 * LPO; ++i) write_one(lds0, i);
+    stage_rsrc(1);
+#pragma unroll
+    for (int i = 0; i < 2 * LPO; ++i) load_one(i);
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 12; ++r) read_one(lds0, 0, 0, r);
+
+    auto stage = [&](int st, const uint16_t* cur, uint16_t* oth) {
+#pragma unroll
+        for (int t = 0; t < STEPS; ++t) {
+            const int c = t & 1, n = c ^ 1;
+            uint4v bf[4];
+#pragma unroll
+            for (int rn = 0; rn < 4; ++rn)
+                bf[rn] = uint4v{bl[c][rn].x, bl[c][rn].y, bh[c][rn].x, bh[c][rn].y};
+            if (t == STEPS - 3) stage_rsrc(st + 2);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                acc[i >> 2][i & 3] = GMma<DT>::mma(a[c][i >> 2], bf[i & 3], acc[i >> 2][i & 3]);
+                if (i < 12) {
+                    if (t + 1 < STEPS) read_one(cur, t + 1, n, i);
+                    else read_one(oth, 0, n, i);  // the next stage's first step (written before the barrier)
+                }
+                // steps STEPS-3 and STEPS-2: write a held chunk, then load its successor into it
+                if (t == STEPS - 3 && i < LPO) { write_one(oth, i); load_one(i); }
+                if (t == STEPS - 2 && i < LPO) { write_one(oth, LPO + i); load_one(LPO + i); }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (t == STEPS - 2) __syncthreads();  // the other copy is whole; this copy's reads are done
+        }
+    };
+    static_assert(2 * LPO <= 16, "one load or write between instructions");
+    int st = 0;
+    for (; st + 1 < NS; st += 2) {
+        stage(st, lds0, lds1);
+        stage(st + 1, lds1, lds0);
+    }
+    if (st < NS) stage(st, lds0, lds1);
+
+    store_block(p, acc, m0, n0, wm, wn, lane, e_bias, e_rs);
 }
 
 // The shapes the kernel serves: batch 1, 1x1, stride 1, no padding, one
@@ -362,6 +560,14 @@ hipError_t hgemm_launch_v(const HGemmParams& q, int grid, hipStream_t stream) {
     }
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kNT), HG<KS>::LDS, stream, q);
+    return hipGetLastError();
+}
+
+template <int DT, int KS>
+hipError_t hgemm_launch_rs(const HGemmParams& q, int grid, hipStream_t stream) {
+    (void)hipGetLastError();
+    // all LDS is static (HG<KS>::LDS bytes)
+    hipLaunchKernelGGL((igemm_h_gemm_rs_kernel<DT, KS>), dim3((unsigned)grid), dim3(kNT), 0, stream, q);
     return hipGetLastError();
 }
 
@@ -404,7 +610,11 @@ hipError_t hgemm_launch(const ConvParams& p, hipStream_t stream) {
     const int grid = q.tiles_m * ((q.tiles_n + 7) & ~7);
     // the widest load every slot of both operands allows
     const uintptr_t al = reinterpret_cast<uintptr_t>(p.x) | reinterpret_cast<uintptr_t>(p.w);
-    if (al % 16 == 0 && q.K % 8 == 0 && q.N % 8 == 0) return hgemm_launch_v<DT, KS, 16>(q, grid, stream);
+    if (al % 16 == 0 && q.K % 8 == 0 && q.N % 8 == 0) {
+        // the register-staged form needs at least three steps a stage
+        if constexpr (KS == 64) return hgemm_launch_rs<DT, KS>(q, grid, stream);
+        else return hgemm_launch_v<DT, KS, 16>(q, grid, stream);
+    }
     if (al % 4 == 0 && q.K % 2 == 0 && q.N % 2 == 0) return hgemm_launch_v<DT, KS, 4>(q, grid, stream);
     return hgemm_launch_v<DT, KS, 2>(q, grid, stream);
 }
