@@ -508,7 +508,11 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
         auto load_x1 = [&](XRegs& rg, int i, int c0) {
             // one descriptor per channel (scalar work only)
             const int cb = __builtin_amdgcn_readfirstlane((int)((long long)(c0 + i) * HW));  // halves
-            const int nrec = __builtin_amdgcn_readfirstlane((int)(x_bytes - 2LL * cb));
+            // a descriptor at a channel past the whole tensor (batch 1, the
+            // last stage's channels past CI) gets an empty range: every load
+            // through it is padding and reads zeros, and none reaches memory
+            const long long left = x_bytes - 2LL * cb;
+            const int nrec = __builtin_amdgcn_readfirstlane((int)(left > 0 ? left : 0));
             const __amdgpu_buffer_rsrc_t xrs =
                 __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(xg + cb), 0, nrec, kBufRaw);
 #pragma unroll

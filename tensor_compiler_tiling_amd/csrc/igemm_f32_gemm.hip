@@ -15,9 +15,10 @@
 //    issued as the current stage starts, into the other of two LDS copies,
 //    and one barrier ends a stage;
 //  - A is held [m][32 k] with the eight 16-byte chunks of row m rotated by
-//    XOR with (m mod 8): a lane's 4 consecutive k of its row are one 16-byte
-//    read, and 8 lanes on consecutive rows read 8 different chunks (no bank
-//    conflicts).  B is held [k][128 n] and read one word a lane, lanes on
+//    XOR with ((m / 2) mod 8): a lane's 4 consecutive k of its row are one
+//    16-byte read, and the 16 lanes on consecutive rows that one LDS cycle
+//    serves (64 banks, 256 bytes: two 128-byte rows a bank line) read 16
+//    different 16-byte bank groups (no bank conflicts).  B is held [k][128 n] and read one word a lane, lanes on
 //    consecutive n;
 //  - the instruction's two k slots are the wave's two lane halves: in group
 //    g of 8 k, instruction i gives half h the k = 8g + 4h + i, so a lane's A
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(kNT) void igemm_f32_gemm_kernel(GemmParams p) {
 
     // ---- per-lane load offsets (bytes, without the stage term) -------------
     // A slot s of a stage: row r = s / (32/CS), position pos: the slot holds
-    // the CS floats of global k = ((chunk(pos) ^ (r % 8)) * 4) | (element % 4).
+    // the CS floats of global k = ((chunk(pos) ^ ((r / 2) % 8)) * 4) | (element % 4).
     // B slot s: k = s / (128/CS), columns n = (s % (128/CS)) * CS ...
     unsigned aoff[LPW], boff[LPW];
     int akk[LPW];  // the slot's k within the stage (for the k tail)
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kNT) void igemm_f32_gemm_kernel(GemmParams p) {
         {
             const int r = s / (kKS / CS);
             const int e = (s - r * (kKS / CS)) * CS;  // element of the row in LDS
-            const int k = (((e >> 2) ^ (r & 7)) << 2) | (e & 3);
+            const int k = (((e >> 2) ^ ((r >> 1) & 7)) << 2) | (e & 3);
             akk[j] = k;
             aoff[j] = (m0 + r < p.M) ? (unsigned)((r * p.K + k) * 4) : kBufOut;
         }
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kNT) void igemm_f32_gemm_kernel(GemmParams p) {
     for (int rm = 0; rm < 2; ++rm) {
         const int row = wm * 64 + rm * 32 + lj;
         arow[rm] = row * kKS;
-        ar7[rm] = row & 7;
+        ar7[rm] = (row >> 1) & 7;
     }
 #pragma unroll
     for (int rn = 0; rn < 2; ++rn) bcol[rn] = kTM * kKS + 4 * lh * kTN + wn * 64 + rn * 32 + lj;

@@ -347,6 +347,10 @@ HALF_SMALL = [
     # 12 channels, not a multiple of 8: the filter goes through the reordered
     # copy instead of being staged from the caller's layout
     ("half_ci12", 136, 2, 12, 9, 11, 40, 3, 3, 1, 1),
+    # batch 1 with a last stage that starts within 8 channels of CI: the
+    # window loads of its channels past CI come from descriptors placed past
+    # the whole tensor (an empty range: zeros)
+    ("half_n1_ci20", 137, 1, 20, 10, 10, 40, 3, 3, 1, 1),
 ]
 
 
