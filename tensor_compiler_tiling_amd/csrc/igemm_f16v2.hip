@@ -552,12 +552,17 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
             uint16_t* Xb = Xsb + buf * XB;
             if constexpr (HX) {
                 auto& xreg = rg.v;
+                // only a last stage that runs past CI has channels to zero
+                // (a uniform test: the selects cost as much as the packing)
+                const bool tail = c0 + KC > p.CI;
 #pragma unroll
                 for (int j = 0; j < XPT; ++j) {
                     if (xvo[j] == kBufOut) continue;
+                    if (tail) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        if (c0 + xch[j] + i >= p.CI) xreg[j][i] = XV{};
+                        for (int i = 0; i < 8; ++i)
+                            if (c0 + xch[j] + i >= p.CI) xreg[j][i] = XV{};
+                    }
 #pragma unroll
                     for (int u = 0; u < PX; ++u) {
                         uint4v o;
