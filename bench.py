@@ -87,10 +87,11 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str, cfg: dict):
+def measured_traffic(workload: str, kernel: str, cfg: dict, prepared: bool = False):
     """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE passes
     recorded for this workload, or None when no record matches the kernel
-    source and tile config as they are now."""
+    source, tile config and filter form (reordered per call, or prepared) as
+    they are now."""
     try:
         with open(TRAFFIC_LOG) as f:
             recs = json.load(f)
@@ -99,7 +100,8 @@ def measured_traffic(workload: str, kernel: str, cfg: dict):
     digest = source_digest(kernel)
     for r in recs:
         if (r.get("workload") == workload and r.get("kernel") == kernel
-                and r.get("source_sha256") == digest and r.get("tile", {}) == cfg):
+                and r.get("source_sha256") == digest and r.get("tile", {}) == cfg
+                and (r.get("filter") == "prepared") == prepared):
             return r.get("traffic_bytes_per_launch")
     return None
 
@@ -582,7 +584,7 @@ def per_shape(a) -> list:
             out.append({"workload": name + (" (prepared filter)" if prepared else ""), "dtype": w.dtype,
                         "us": round(ms * 1e3, 3), "TFLOP/s": round(tf, 2), "bound": "mfma",
                         "frac": round(tf / peak, 4), "kernel": vname, "tile": tile,
-                        "traffic": measured_traffic(name, vname, tile) if not prepared else None})
+                        "traffic": measured_traffic(name, vname, tile, prepared)})
     for name in ("bcast_exp_128x256x32x32_f16", "bcast_exp_128x256x32x32_f32"):
         bw = wl.BROADCAST_WORKLOADS[name]
         dt = torch.float16 if bw.out_dtype == wl.F16 else torch.float32
@@ -759,7 +761,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(tflops / peak, 4),
                      "traffic": measured_traffic(name, vdesc["name"],
                                                  {"split_k": cfg.split_k, "stages": cfg.stages,
-                                                  "kc": cfg.kc})},
+                                                  "kc": cfg.kc}, a.prepared)},
         "eager_ms_per_step": round(eager_ms, 6) if eager_ms else None,
         "wall_s": round(wall, 4),
     }
