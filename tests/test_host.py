@@ -246,6 +246,29 @@ def test_shipped_tuning_log_is_legal():
         ct.ct_cache_clear()
 
 
+def test_traffic_lookup_matches_the_filter_form(tmp_path, monkeypatch):
+    """bench.py reports a traffic record only for the kernel source, tile and
+    filter form (reordered per call or prepared) it was measured with."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    kern = "h2f16_m128n128_w2x2_r2x2_kc16"
+    tile = {"split_k": 1, "stages": 16, "kc": 16}
+    dig = bench.source_digest(kern)
+    recs = [{"workload": "w", "kernel": kern, "tile": tile, "source_sha256": dig, "traffic_bytes_per_launch": 11},
+            {"workload": "w", "kernel": kern, "tile": tile, "source_sha256": dig, "traffic_bytes_per_launch": 22,
+             "filter": "prepared"},
+            {"workload": "v", "kernel": kern, "tile": tile, "source_sha256": "0" * 64, "traffic_bytes_per_launch": 33}]
+    log = tmp_path / "traffic.json"
+    log.write_text(json.dumps(recs))
+    monkeypatch.setattr(bench, "TRAFFIC_LOG", str(log))
+    assert bench.measured_traffic("w", kern, tile) == 11
+    assert bench.measured_traffic("w", kern, tile, prepared=True) == 22
+    assert bench.measured_traffic("w", kern, {"split_k": 2, "stages": 16, "kc": 16}) is None
+    assert bench.measured_traffic("v", kern, tile) is None  # taken with another kernel source
+
+
 def test_traffic_records_point_at_summaries():
     recs = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
     for r in recs:
