@@ -242,7 +242,8 @@ HALF_K64 = {wl.F16: "hgf16_m256n256_w2x2_r4x4_k64", wl.BF16: "hgbf16_m256n256_w2
 
 
 @pytest.mark.parametrize("epi", [ct.CT_EPI_NONE, ct.CT_EPI_EXP_BIAS_RSQRT])
-@pytest.mark.parametrize("mnk", [(256, 256, 64), (300, 263, 64), (257, 1000, 192), (1024, 1024, 128), (512, 768, 320)],
+@pytest.mark.parametrize("mnk", [(256, 256, 64), (300, 263, 64), (257, 1000, 192), (1024, 1024, 128), (512, 768, 320),
+                                 (3, 8, 128)],
                          ids=lambda t: "x".join(map(str, t)))
 @pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
 def test_gemm_half_k64_vs_oracle(dtype, mnk, epi):
