@@ -356,12 +356,13 @@ __global__ __launch_bounds__(kNT) void igemm_h_gemm_kernel(HGemmParams p) {
 
 // Register-staged form, for 16-byte aligned operands with K and N multiples
 // of 8 (every 16-byte chunk of a tile row either wholly inside or wholly
-// past the matrix) and stages of 64 channels.  Loads that write LDS directly hold up the wave that
-// issues them (on this chip each costs the issuing wave about as long as
-// the whole CU's LDS-load queue ahead of it), and with one wave a SIMD that
-// wave is the one that issues the matrix instructions.  Plain 16-byte loads
-// into registers and 16-byte LDS writes by the waves themselves cost the
-// matrix pipe almost nothing, so this form stages through registers:
+// past the matrix) and stages of 64 channels.  Loads that write LDS
+// directly hold up the wave that issues them (on this chip each costs the
+// issuing wave about as long as the whole CU's queue of them ahead of it),
+// and with one wave a SIMD that wave is the one that issues the matrix
+// instructions.  Plain 16-byte loads into registers and 16-byte LDS writes
+// by the waves themselves cost the matrix pipe almost nothing, so this form
+// stages through registers:
 //  - a thread holds 2 KS/8 chunks of 16 bytes (KS/8 of A, KS/8 of B) of the
 //    next stage;
 //  - a stage's STEPS steps each run 16 instructions with one LDS access or
