@@ -526,9 +526,11 @@ def time_graph(step, stream, steps: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / steps
 
 
-def conv_step(w, prepared: bool = False):
+def conv_step(w, prepared: bool = False, stream_handle=None):
     """(step, config) for one convolution of workload w through the C ABI, on
-    the current stream at call time; inputs resident on the GPU."""
+    the stream `stream_handle` (default: the current stream at call time);
+    inputs resident on the GPU, their addresses bound once so that a step
+    costs the host little beyond the call itself."""
     import torch
     from tensor_compiler_tiling_amd import convtile as ct
     from tensor_compiler_tiling_amd import workloads as wl
@@ -546,13 +548,16 @@ def conv_step(w, prepared: bool = False):
     if prepared:
         k = ct.prepare_filter(k)
     fn = lib.ct_conv2d_nchw_fwd_prepared if prepared else lib.ct_conv2d_nchw_fwd
-    keep = (x, k, b, v, y)
+    keep = (x, k, b, v, y)  # owners of the bound addresses
+    head = (x.data_ptr(), k.data_ptr(), y.data_ptr()) + args
+    tail = (b.data_ptr(), v.data_ptr(), 1e-5)
 
     def step():
-        st = fn(keep[0].data_ptr(), keep[1].data_ptr(), keep[4].data_ptr(), *args, keep[2].data_ptr(),
-                keep[3].data_ptr(), 1e-5, torch.cuda.current_stream().cuda_stream)
+        h = stream_handle if stream_handle is not None else torch.cuda.current_stream().cuda_stream
+        st = fn(*head, *tail, h)
         if st != 0:
             raise ct.ConvTileError(st, "fwd")
+    step.keep = keep
 
     st, cfg, from_cache = ct.ct_conv2d_query(*args)
     ct.check(st, "query")
@@ -576,7 +581,7 @@ def per_shape(a) -> list:
         w = wl.CONV_WORKLOADS[name]
         peak = PEAK_TFLOPS[w.dtype]
         for prepared in ((False, True) if w.dtype != "f32" else (False,)):
-            step, cfg, _ = conv_step(w, prepared)
+            step, cfg, _ = conv_step(w, prepared, stream.cuda_stream)
             ms = time_graph(step, stream, steps, a.warmup)
             tf = w.flops / (ms * 1e-3) / 1e12
             vname = ct.variants()[cfg.variant]["name"]
@@ -679,11 +684,11 @@ def main():
         vg = torch.from_numpy(inp["var"]).to(dev)
         yg = torch.empty((w.N, w.CO, w.OH, w.OW), dtype=torch.float32, device=dev)
         lib = ct.library()
+        gargs = (kg.data_ptr(), xg.data_ptr(), yg.data_ptr(), gemm.M, gemm.N, gemm.K, dt, w.epilogue,
+                 bg.data_ptr(), vg.data_ptr(), 1e-5, stream.cuda_stream)
 
         def step():
-            st = lib.ct_gemm_fwd(kg.data_ptr(), xg.data_ptr(), yg.data_ptr(), gemm.M, gemm.N, gemm.K, dt,
-                                 w.epilogue, bg.data_ptr(), vg.data_ptr(), 1e-5,
-                                 torch.cuda.current_stream().cuda_stream)
+            st = lib.ct_gemm_fwd(*gargs)
             if st != 0:
                 raise ct.ConvTileError(st, "fwd")
 
@@ -693,7 +698,7 @@ def main():
         if a.prepared and w.dtype == "f32":
             print("--prepared applies to half-precision layers only", file=sys.stderr)
             sys.exit(2)
-        step, cfg, from_cache = conv_step(w, prepared=a.prepared)
+        step, cfg, from_cache = conv_step(w, prepared=a.prepared, stream_handle=stream.cuda_stream)
     vdesc = ct.variants()[cfg.variant]
 
     t0 = time.perf_counter()
