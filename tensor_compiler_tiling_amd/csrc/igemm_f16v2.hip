@@ -28,7 +28,12 @@
 //    set and are transposed into the other copy after the stage's matrix
 //    steps; one barrier per stage;
 //  - a stage's 9*KC/16 matrix steps are unrolled, each reading the next
-//    step's fragments before issuing its own instructions.
+//    step's fragments before issuing its own instructions;
+//  - in the variants with staging waves (names ending _x1, _x2), one or two
+//    further waves take every window task and no matrix work: they write
+//    stage st+1's window as stage st starts and then load stage st+3's, so
+//    that the register transposes run beside the matrix waves' steps rather
+//    than between their last step and the barrier.
 // The window's padding is zeroed once at kernel start and never written
 // again (only in-image pixels are staged).
 #include "ct_device.hpp"
@@ -130,24 +135,32 @@ __global__ __launch_bounds__(256) void h2_prepare_kernel(const uint16_t* __restr
     }
 }
 
-template <int WM, int WN, int RM, int RN, int KC, int T>
+// NXW: waves that only stage the window (0: the matrix waves stage it).
+template <int WM, int WN, int RM, int RN, int KC, int T, int NXW = 0>
 struct H2 {
     static constexpr int TM = WM * RM * 32;
     static constexpr int TN = WN * RN * 32;
-    static constexpr int NT = WM * WN * 64;
+    static constexpr int NTM = WM * WN * 64;   // threads of the matrix waves
+    static constexpr int NT = NTM + NXW * 64;  // threads of the workgroup
     static constexpr int CG = KC / 8;          // channel groups per stage
     static constexpr int G = T * CG;           // groups per stage
     static constexpr int NSTEP = G / 2;        // instruction steps per stage
     static constexpr int WST = (G + 1) * 8;    // halves per filter row in LDS (odd x 16 B)
     static constexpr int KCS = (CG + 1) * 8;   // halves per window pixel (odd x 16 B)
-    static constexpr int NW = WM * WN;         // waves
+    static constexpr int NW = WM * WN;         // matrix waves
     // the filter tile of a stage as 16-byte LDS slots [TM][G + 1] (the last
     // slot of a row is padding), filled 64 slots (one load per wave) at a time
     static constexpr int WSL = TM * (G + 1);
     static constexpr int WCK = WSL / 64;       // 64-slot chunks
     static constexpr int WLD = (WCK + NW - 1) / NW;  // chunk loads per wave
     static_assert(WSL % 64 == 0, "whole chunks");
-    static constexpr int XPT = NT >= 256 ? 1 : 2;  // window tasks per thread
+    // window tasks per staging thread and the task stride: with staging
+    // waves, as many tasks as 32 registers of one set hold (8 loads of PX
+    // halves a task, a 1- or 2-pixel load in one register)
+    static constexpr int xpt(int px) {
+        return NXW == 0 ? (NTM >= 256 ? 1 : 2) : (px >= 8 ? 1 : px == 4 ? 2 : 4);
+    }
+    static constexpr int XT = NXW == 0 ? NTM : NXW * 64;
     static constexpr int WB = TM * WST;        // halves per filter copy
     static_assert(G % 2 == 0, "a step takes two groups");
 };
@@ -239,12 +252,12 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv& f) {
     return (uint32_t)(((uint64_t)__umulhi(n, f.mul) + n) >> f.shift);
 }
 
-template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
-__global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
+template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX, int NXW>
+__global__ __launch_bounds__((WM * WN + NXW) * 64) void igemm_h2_kernel(H2Params p) {
     fetch_h2_kernargs(p);
-    using C = H2<WM, WN, RM, RN, KC, T>;
+    using C = H2<WM, WN, RM, RN, KC, T, NXW>;
     constexpr int TM = C::TM, TN = C::TN, NT = C::NT, CG = C::CG, G = C::G;
-    constexpr int NSTEP = C::NSTEP, WST = C::WST, KCS = C::KCS, XPT = C::XPT;
+    constexpr int NSTEP = C::NSTEP, WST = C::WST, KCS = C::KCS, XPT = C::xpt(PX);
     constexpr int NW = C::NW, WCK = C::WCK, WLD = C::WLD;
     extern __shared__ __align__(16) uint16_t hs[];
     __shared__ int s_last;
@@ -253,6 +266,8 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
     const int lane = tid & 63;
     // wave-uniform, and known to be: branches on it are not divergent
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // waves NW.. (when NXW > 0) only stage the window
+    const bool mma_wave = wave < NW;
     const int wm = wave % WM;
     const int wn = wave / WM;
     const int lj = lane & 31;
@@ -342,7 +357,7 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
     //      loads, so that waiting for them never waits for those) and written
     //      to the LDS tables once the first stage's loads are out; zero both
     //      windows -------------------------------------------------------------
-    static_assert(TM <= NT, "one epilogue row per thread");
+    static_assert(TM <= C::NTM, "one epilogue row per matrix thread");
     float e_b = 0.0f, e_v = 0.0f;
     const bool e_row = tid < TM && co0 + tid < p.CO;
     if (e_row && p.epilogue != EPI_NONE) e_b = p.bias[co0 + tid];
@@ -369,7 +384,9 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
         const int r = q - m * (G + 1);
         wsrc[j] = (q < C::WSL && r < G) ? (co0 + m) * CG8 * (T * 8) + r * 8 : -1;
     }
-    // window task q = (cg, window row r, run u): 8 channels x PX pixels
+    // window task q = (cg, window row r, run u): 8 channels x PX pixels, for
+    // thread tid - xt0 (the staging waves' threads with NXW > 0)
+    constexpr int xt0 = NXW == 0 ? 0 : C::NTM;
     const int nrun = p.W / PX;
     const int n_xt = CG * p.R * nrun;
     long long xsrc[XPT];  // halves, channel cg*8 without the stage term; -1: none
@@ -377,11 +394,11 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
     int xch[XPT];         // channel of the task's first lane within a stage
 #pragma unroll
     for (int j = 0; j < XPT; ++j) {
-        const int q = tid + j * NT;
+        const int q = tid - xt0 + j * C::XT;
         xsrc[j] = -1;
         xdst[j] = 0;
         xch[j] = 0;
-        if (q < n_xt) {
+        if (q >= 0 && q < n_xt) {
             const int cg = (int)fdiv((uint32_t)q, p.fd_rn);
             const int rem = q - cg * (int)p.fd_rn.d;
             const int r = (int)fdiv((uint32_t)rem, p.fd_run);
@@ -474,10 +491,13 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
     // last stage again and write the buffer no later stage reads).  The loop
     // comes in two copies, for the waves that stage window tasks (HX) and for
     // those that do not, so that in each the number of loads issued per step
-    // is fixed and the compiler waits for exactly the ones a step consumes.
+    // is fixed and the compiler waits for exactly the ones a step consumes
+    // (mode 1 and mode 0; mode 2 is a staging wave's loop: window staging
+    // and no matrix work).
     const int last = nst - 1;
-    auto run_stages = [&](auto hx_tag) {
-        constexpr bool HX = decltype(hx_tag)::value;
+    auto run_stages = [&](auto mode_tag) {
+        constexpr int MODE = decltype(mode_tag)::value;
+        constexpr bool HX = MODE != 0;
         XRegs xa, xb;
         // Load units: filter chunk j of stage s_abs (into LDS copy buf), and
         // window channel i of every task of the stage starting at channel c0.
@@ -575,6 +595,33 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
                 }
             }
         };
+        if constexpr (MODE == 2) {
+            // A staging wave stores stage st+1's window (loaded two stages
+            // earlier) as soon as stage st starts (its copy was last read in
+            // stage st-1), then loads stage st+3's into the freed registers;
+            // its register transposes run beside the matrix waves' steps.
+            // (The compiler waits for each register's own loads: the newer
+            // set stays in flight.)
+            if (nst > 0) {
+                load_x(xa, s_first * KC);
+                load_x(xb, (s_first + min(1, last)) * KC);
+                store_stage(xa, 0, s_first * KC);
+                load_x(xa, (s_first + min(2, last)) * KC);
+            }
+            __syncthreads();
+            auto sstep = [&](int st, XRegs& held) {
+                store_stage(held, (st + 1) & 1, (s_first + min(st + 1, last)) * KC);
+                load_x(held, (s_first + min(st + 3, last)) * KC);
+                __syncthreads();
+            };
+            int st = 0;
+            for (; st + 1 < nst; st += 2) {
+                sstep(st, xb);
+                sstep(st + 1, xa);
+            }
+            if (st < nst) sstep(st, xb);
+            return;
+        }
         if (nst > 0) {
             load_w(s_first, 0);
             load_x(xa, s_first * KC);
@@ -603,11 +650,18 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
         }
         if (st < nst) step(st, xb, xa);
     };
-    // wave-uniform: does this wave hold any window task (task q = tid + j*NT)?
-    if (wave * 64 < n_xt)
-        run_stages(std::true_type{});
-    else
-        run_stages(std::false_type{});
+    if constexpr (NXW > 0) {
+        if (mma_wave)
+            run_stages(std::integral_constant<int, 0>{});
+        else
+            run_stages(std::integral_constant<int, 2>{});
+    } else {
+        // wave-uniform: does this wave hold any window task (q = tid + j*NT)?
+        if (wave * 64 < n_xt)
+            run_stages(std::integral_constant<int, 1>{});
+        else
+            run_stages(std::integral_constant<int, 0>{});
+    }
 
     // ---- split reduction across workgroups (device-scope atomics) -------------
     const int wslot = wm + wn * WM;
@@ -616,14 +670,17 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
         float* part = p.ws + ((long long)tile * p.S) * tile_words;
         const int base = wslot * RM * RN * 16;
         float* mine = part + (long long)split * tile_words;
+        // (staging waves hold no results: they only take the barriers)
+        if (mma_wave) {
 #pragma unroll
-        for (int rm = 0; rm < RM; ++rm)
+            for (int rm = 0; rm < RM; ++rm)
 #pragma unroll
-            for (int rn = 0; rn < RN; ++rn)
+                for (int rn = 0; rn < RN; ++rn)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    __hip_atomic_store(&mine[(base + (rm * RN + rn) * 16 + r) * 64 + lane], acc[rm][rn][r],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int r = 0; r < 16; ++r)
+                        __hip_atomic_store(&mine[(base + (rm * RN + rn) * 16 + r) * 64 + lane], acc[rm][rn][r],
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
@@ -632,7 +689,7 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
             s_last = (old == (unsigned)(p.S - 1)) ? 1 : 0;
         }
         __syncthreads();
-        if (!s_last) return;
+        if (!s_last || !mma_wave) return;
 #pragma unroll
         for (int rm = 0; rm < RM; ++rm)
 #pragma unroll
@@ -655,6 +712,7 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h2_kernel(H2Params p) {
                                __HIP_MEMORY_SCOPE_AGENT);
     }
 
+    if (!mma_wave) return;
     // ---- epilogue and store (C: row 8*(r/4) + 4*(lane/32) + r%4, col lane%32)
 #pragma unroll
     for (int rm = 0; rm < RM; ++rm) {
@@ -683,9 +741,9 @@ inline int h2_px_for_shape(int W) {
     return 1;
 }
 
-template <int WM, int WN, int RM, int RN, int KC, int T>
+template <int WM, int WN, int RM, int RN, int KC, int T, int NXW>
 int h2_bytes_for(const ConvParams& p, int px) {
-    using C = H2<WM, WN, RM, RN, KC, T>;
+    using C = H2<WM, WN, RM, RN, KC, T, NXW>;
     if (p.T != T || p.kc != KC) return 1 << 30;
     if (p.P >= (1LL << 31) || (long long)p.N * p.Hp >= (1LL << 31)) return 1 << 30;
     // x and the prepared filter are read through buffer descriptors with
@@ -696,14 +754,14 @@ int h2_bytes_for(const ConvParams& p, int px) {
     static_assert(64 % KC == 0, "a stage divides a prepared row's 64-channel blocks");
     if ((long long)p.N * p.CI * p.H * p.W * 2 >= (1LL << 31)) return 1 << 30;
     // the window tasks must fit the per-thread slots
-    if ((long long)C::CG * p.R * (p.W / px) > (long long)C::XPT * C::NT) return 1 << 30;
+    if ((long long)C::CG * p.R * (p.W / px) > (long long)C::xpt(px) * C::XT) return 1 << 30;
     if ((long long)p.R * p.Wp * C::KCS >= (1LL << 28)) return 1 << 30;
     return 2 * (2 * C::WB + 2 * h2_xb(p.R, p.Wp, C::KCS) + 4 * C::TM);
 }
 
-template <int WM, int WN, int RM, int RN, int KC, int T>
+template <int WM, int WN, int RM, int RN, int KC, int T, int NXW>
 int h2_lds_bytes(const ConvParams& p) {
-    return h2_bytes_for<WM, WN, RM, RN, KC, T>(p, h2_px_for_shape(p.W));
+    return h2_bytes_for<WM, WN, RM, RN, KC, T, NXW>(p, h2_px_for_shape(p.W));
 }
 
 // The launch's own prepared copy of the filter (none when the caller passes
@@ -714,10 +772,10 @@ long long h2_aux_bytes(const ConvParams& p) {
     return 2LL * p.CO * round_up(p.CI, 64) * T;
 }
 
-template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int PX>
+template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int NXW, int PX>
 hipError_t h2_launch_px(const ConvParams& base, int bytes, hipStream_t stream) {
-    using C = H2<WM, WN, RM, RN, KC, T>;
-    auto kern = igemm_h2_kernel<DT, WM, WN, RM, RN, KC, T, PX>;
+    using C = H2<WM, WN, RM, RN, KC, T, NXW>;
+    auto kern = igemm_h2_kernel<DT, WM, WN, RM, RN, KC, T, PX, NXW>;
     H2Params q;
     static_cast<ConvParams&>(q) = base;
     q.fd_kw = make_fastdiv((uint32_t)base.KW);
@@ -767,14 +825,14 @@ hipError_t h2_launch_px(const ConvParams& base, int bytes, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int DT, int WM, int WN, int RM, int RN, int KC, int T>
+template <int DT, int WM, int WN, int RM, int RN, int KC, int T, int NXW>
 hipError_t h2_launch(const ConvParams& p, hipStream_t stream) {
     // the widest window vector the shape and the pointer's alignment allow
     // (every run starts at a multiple of PX pixels of a row)
     int px = h2_px_for_shape(p.W);
     const uintptr_t xa = reinterpret_cast<uintptr_t>(p.x);
     while (px > 1 && (xa % (2u * px) != 0 || (p.H * (long long)p.W) % px != 0)) px >>= 1;
-    const int bytes = h2_bytes_for<WM, WN, RM, RN, KC, T>(p, px);
+    const int bytes = h2_bytes_for<WM, WN, RM, RN, KC, T, NXW>(p, px);
     if (bytes > 163840 - 64) return hipErrorInvalidValue;
 
     ConvParams pp = p;
@@ -787,10 +845,10 @@ hipError_t h2_launch(const ConvParams& p, hipStream_t stream) {
         pp.aux = nullptr;  // the caller's filter is prepared: stage from p.w
     }
     switch (px) {
-        case 8: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 8>(pp, bytes, stream);
-        case 4: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 4>(pp, bytes, stream);
-        case 2: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 2>(pp, bytes, stream);
-        default: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, 1>(pp, bytes, stream);
+        case 8: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, NXW, 8>(pp, bytes, stream);
+        case 4: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, NXW, 4>(pp, bytes, stream);
+        case 2: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, NXW, 2>(pp, bytes, stream);
+        default: return h2_launch_px<DT, WM, WN, RM, RN, KC, T, NXW, 1>(pp, bytes, stream);
     }
 }
 
@@ -825,9 +883,10 @@ namespace {
 // descriptor: 32x32x16 instruction, waves WM x WN x 1, reps RM x RN; kc fixed
 // at KC (kc_max = KC); filters of T taps (3x3, and 1x1 for the matrix-product
 // view)
-#define CT_H2_VARIANT_T(NAME, DT, WM, WN, RM, RN, KC, T)                                         \
-    {NAME, DT, 32, 32, 16, WM, WN, 1, RM, RN, KC, &h2_lds_bytes<WM, WN, RM, RN, KC, T>,          \
-     &h2_launch<DT, WM, WN, RM, RN, KC, T>, &h2_aux_bytes<WM, WN, RM, RN, KC, T>, 0, 0, 1}
+#define CT_H2_VARIANT_X(NAME, DT, WM, WN, RM, RN, KC, T, NXW)                                   \
+    {NAME, DT, 32, 32, 16, WM, WN, 1, RM, RN, KC, &h2_lds_bytes<WM, WN, RM, RN, KC, T, NXW>,     \
+     &h2_launch<DT, WM, WN, RM, RN, KC, T, NXW>, &h2_aux_bytes<WM, WN, RM, RN, KC, T>, 0, 0, 1}
+#define CT_H2_VARIANT_T(NAME, DT, WM, WN, RM, RN, KC, T) CT_H2_VARIANT_X(NAME, DT, WM, WN, RM, RN, KC, T, 0)
 #define CT_H2_VARIANT(NAME, DT, WM, WN, RM, RN, KC) CT_H2_VARIANT_T(NAME, DT, WM, WN, RM, RN, KC, 9)
 
 const IgemmVariant kH2Variants[] = {
@@ -846,11 +905,29 @@ const IgemmVariant kH2Variants[] = {
     CT_H2_VARIANT_T("h2bf16_m128n256_w2x4_r2x2_kc64_t1", DT_BF16, 2, 4, 2, 2, 64, 1),
 };
 
+// the same with waves that only stage the window (the matrix waves never
+// pack it), and the number of those waves: registered after every other table
+const IgemmVariant kH2XVariants[] = {
+    CT_H2_VARIANT_X("h2f16_m128n256_w2x4_r2x2_kc16_x2", DT_F16, 2, 4, 2, 2, 16, 9, 2),
+    CT_H2_VARIANT_X("h2f16_m128n128_w2x2_r2x2_kc16_x2", DT_F16, 2, 2, 2, 2, 16, 9, 2),
+    CT_H2_VARIANT_X("h2f16_m128n128_w2x2_r2x2_kc16_x1", DT_F16, 2, 2, 2, 2, 16, 9, 1),
+    CT_H2_VARIANT_X("h2bf16_m128n128_w2x2_r2x2_kc16_x2", DT_BF16, 2, 2, 2, 2, 16, 9, 2),
+};
+const int kH2XExtraWaves[] = {2, 2, 1, 2};
+static_assert(sizeof(kH2XExtraWaves) / sizeof(int) == sizeof(kH2XVariants) / sizeof(kH2XVariants[0]),
+              "one wave count per variant");
+
 }  // namespace
 
 const IgemmVariant* igemm_f16v2_variants(int* count) {
     *count = (int)(sizeof(kH2Variants) / sizeof(kH2Variants[0]));
     return kH2Variants;
+}
+
+const IgemmVariant* igemm_f16v2x_variants(int* count, const int** extra_waves) {
+    *count = (int)(sizeof(kH2XVariants) / sizeof(kH2XVariants[0]));
+    *extra_waves = kH2XExtraWaves;
+    return kH2XVariants;
 }
 
 }  // namespace ct

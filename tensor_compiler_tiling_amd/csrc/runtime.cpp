@@ -37,6 +37,12 @@
 #include "igemm_common.hpp"
 
 namespace ct {
+
+// Half-precision convolution variants with staging waves (igemm_f16v2.hip):
+// the descriptors, and per variant the waves it runs beside its
+// waves_m x waves_n matrix waves.
+const IgemmVariant* igemm_f16v2x_variants(int* count, const int** extra_waves);
+
 namespace {
 
 constexpr int kMaxLds = 163840;       // bytes of LDS per workgroup on gfx950
@@ -143,7 +149,7 @@ const std::vector<Variant>& variants() {
             d.ig = nullptr;
             out.push_back(d);
         }
-        int n32 = 0, n16 = 0, nsk = 0, nsk16 = 0, nh2 = 0, nskc = 0, nskt = 0, ngm = 0, nhgm = 0;
+        int n32 = 0, n16 = 0, nsk = 0, nsk16 = 0, nh2 = 0, nskc = 0, nskt = 0, ngm = 0, nhgm = 0, nh2x = 0;
         const IgemmVariant* t32 = igemm_f32_variants(&n32);
         const IgemmVariant* tsk = igemm_f32_sk_variants(&nsk);
         const IgemmVariant* tsk16 = igemm_f32_sk16_variants(&nsk16);
@@ -153,7 +159,9 @@ const std::vector<Variant>& variants() {
         const IgemmVariant* th2 = igemm_f16v2_variants(&nh2);
         const IgemmVariant* tgm = igemm_f32_gemm_variants(&ngm);
         const IgemmVariant* thgm = igemm_f16_gemm_variants(&nhgm);
-        auto add = [&](const IgemmVariant* t, int n) {
+        const int* h2x_waves = nullptr;
+        const IgemmVariant* th2x = igemm_f16v2x_variants(&nh2x, &h2x_waves);
+        auto add = [&](const IgemmVariant* t, int n, const int* extra_waves = nullptr) {
             for (int i = 0; i < n; ++i) {
                 Variant v{};
                 snprintf(v.desc.name, sizeof(v.desc.name), "%s", t[i].name);
@@ -170,7 +178,7 @@ const std::vector<Variant>& variants() {
                 v.desc.tile_m = t[i].waves_m * t[i].reps_m * t[i].mfma_m;
                 v.desc.tile_n = t[i].tile_n ? t[i].tile_n : t[i].waves_n * t[i].reps_n * t[i].mfma_n;
                 v.desc.kc_max = t[i].kc_max;
-                v.desc.threads = t[i].waves_m * t[i].waves_n * t[i].waves_k * 64;
+                v.desc.threads = (t[i].waves_m * t[i].waves_n * t[i].waves_k + (extra_waves ? extra_waves[i] : 0)) * 64;
                 v.ig = &t[i];
                 out.push_back(v);
             }
@@ -184,6 +192,7 @@ const std::vector<Variant>& variants() {
         add(th2, nh2);
         add(tgm, ngm);  // last: the flat indices of the earlier points stay as they were
         add(thgm, nhgm);
+        add(th2x, nh2x, h2x_waves);
         return out;
     }();
     return v;
