@@ -32,10 +32,20 @@
 //     of LDS, so that five fit a CU with all of their loads in flight;
 //     consecutive workgroups of one XCD take neighbouring row blocks, whose
 //     halo rows then meet in one L2.
+// Small planes (3x3, stride 1, pad 0 or 1, rows of at most 32 pixels, 32 rows
+// of output at most) take a second kernel: there the first one's index
+// arithmetic (a division per staged element when a row is not a whole number
+// of 16-byte vectors, two per 4-row strip) costs more than the data moves.
+// A workgroup holds PPW whole planes; each staging lane copies one input row
+// with 4-byte loads, and each compute lane walks one output column top to
+// bottom with the filter and a 3-row window in registers (3 LDS reads and 9
+// FMAs an output).  The planes' outputs are one contiguous run of y: they go
+// through LDS and out in 16-byte stores.
 #include "ct_device.hpp"
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 
 namespace ct {
@@ -371,6 +381,153 @@ __global__ __launch_bounds__(kDwThreads) void conv_depthwise_kernel(DwParams p) 
     }
 }
 
+// ---- small planes ----------------------------------------------------------
+struct DwSmallParams {
+    const void* x;
+    const void* w;
+    float* y;
+    const float* bias;
+    const float* var;
+    float eps;
+    int NC, C, H, W, pad, OH, OW;
+    int HP;       // staged rows per plane: H + 2*pad
+    int LDSW;     // LDS row pitch (floats): W + 2*pad rounded up to odd
+    int PPW;      // planes a workgroup holds
+    int groups;   // workgroups with work: ceil(NC / PPW)
+    int epilogue;
+    double rHP, rOW;  // 1 / HP and 1 / OW for the lane-to-(plane, row/column) divisions
+};
+
+constexpr int kDwSmallMaxW = 32;
+constexpr int kDwSmallMaxOH = 32;
+constexpr int kDwSmallLds = 32 * 1024;
+
+// One input row of plane pl, image row iy, into LDS row `dst` (WPAD = W +
+// 2*pad floats, the padding columns zero); rows outside the image or past
+// the last plane are all zeros.  16-bit rows are read as 4-byte words (W even,
+// x 4-byte aligned), fp32 rows as words, all of a row's loads in flight
+// before its writes.
+template <int DT>
+__device__ __forceinline__ void dws_stage_row(const DwSmallParams& p, int pl, int iy, float* dst) {
+    using T = typename Elem<DT>::T;
+    constexpr bool H16 = DT != DT_F32;
+    constexpr int MAXD = H16 ? kDwSmallMaxW / 2 : kDwSmallMaxW;  // words of the widest row
+    const int WPAD = p.W + 2 * p.pad;
+    if (pl < p.NC && iy >= 0 && iy < p.H) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(static_cast<const T*>(p.x) +
+                                                                ((long long)pl * p.H + iy) * p.W);
+        const int nd = H16 ? p.W / 2 : p.W;
+        uint32_t v[MAXD];
+#pragma unroll
+        for (int i = 0; i < MAXD; ++i) v[i] = i < nd ? src[i] : 0u;
+        if (p.pad) {
+            dst[0] = 0.0f;
+            dst[WPAD - 1] = 0.0f;
+        }
+        float* d = dst + p.pad;
+#pragma unroll
+        for (int i = 0; i < MAXD; ++i) {
+            if (i < nd) {
+                if constexpr (H16) {
+                    d[2 * i] = Elem<DT>::to_f32(__builtin_bit_cast(T, (uint16_t)(v[i] & 0xffffu)));
+                    d[2 * i + 1] = Elem<DT>::to_f32(__builtin_bit_cast(T, (uint16_t)(v[i] >> 16)));
+                } else {
+                    d[i] = __uint_as_float(v[i]);
+                }
+            }
+        }
+    } else {
+        for (int j = 0; j < WPAD; ++j) dst[j] = 0.0f;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kDwThreads) void conv_depthwise_small_kernel(DwSmallParams p) {
+    using T = typename Elem<DT>::T;
+    extern __shared__ float lds[];  // PPW x [HP][LDSW]
+    const int tid = threadIdx.x;
+    const int grp = blockIdx.x;
+    if (grp >= p.groups) return;
+    const int pl0 = grp * p.PPW;
+
+    // this lane's output column and its filter and epilogue values, loaded
+    // first (their latency overlaps the staging)
+    const int pp = fdiv(tid, p.OW, p.rOW);
+    const int ox = tid - pp * p.OW;
+    const int pl = pl0 + pp;
+    const bool active = pp < p.PPW && pl < p.NC;
+    const int c = (active ? pl : pl0) % p.C;
+    float tw[9];
+    const T* w = static_cast<const T*>(p.w) + (long long)c * 9;
+#pragma unroll
+    for (int i = 0; i < 9; ++i) tw[i] = Elem<DT>::to_f32(w[i]);
+    // bias and var always point at C readable floats (the host substitutes
+    // what the epilogue does not read)
+    const float e_b = p.epilogue != EPI_NONE ? p.bias[c] : 0.0f;
+    const float e_v = p.var[c];
+
+    // staging: row r = (plane r / HP, row r % HP) of the workgroup's planes,
+    // one row a lane
+    for (int r = tid; r < p.PPW * p.HP; r += kDwThreads) {
+        const int q = fdiv(r, p.HP, p.rHP);
+        const int rr = r - q * p.HP;
+        dws_stage_row<DT>(p, pl0 + q, rr - p.pad, lds + r * p.LDSW);
+    }
+    __syncthreads();
+
+    // the column, top to bottom, into registers
+    float res[kDwSmallMaxOH];
+    if (active) {
+        const float e_r = p.epilogue == EPI_EXP_BIAS_RSQRT ? dev_rsqrt(e_v + p.eps) : 1.0f;
+        const float* col = lds + pp * p.HP * p.LDSW + ox;
+        float a0 = col[0], a1 = col[1], a2 = col[2];
+        float b0 = col[p.LDSW], b1 = col[p.LDSW + 1], b2 = col[p.LDSW + 2];
+#pragma unroll
+        for (int oy = 0; oy < kDwSmallMaxOH; ++oy) {
+            if (oy < p.OH) {
+                const float* r2 = col + (oy + 2) * p.LDSW;
+                const float c0 = r2[0], c1 = r2[1], c2 = r2[2];
+                float acc = a0 * tw[0];
+                acc = __builtin_fmaf(a1, tw[1], acc);
+                acc = __builtin_fmaf(a2, tw[2], acc);
+                acc = __builtin_fmaf(b0, tw[3], acc);
+                acc = __builtin_fmaf(b1, tw[4], acc);
+                acc = __builtin_fmaf(b2, tw[5], acc);
+                acc = __builtin_fmaf(c0, tw[6], acc);
+                acc = __builtin_fmaf(c1, tw[7], acc);
+                acc = __builtin_fmaf(c2, tw[8], acc);
+                res[oy] = apply_epilogue(p.epilogue, acc, e_b, e_r);
+                a0 = b0; a1 = b1; a2 = b2;
+                b0 = c0; b1 = c1; b2 = c2;
+            }
+        }
+    }
+    // The workgroup's output, planes pl0 .. pl0+np-1, is one contiguous run
+    // of y in y's own layout: it goes through LDS (over the windows, no longer
+    // read) and out in 16-byte stores (4-byte ones when y's run is not
+    // 16-byte aligned).
+    __syncthreads();
+    const int OHW = p.OH * p.OW;
+    if (active) {
+        float* o = lds + pp * OHW + ox;
+#pragma unroll
+        for (int oy = 0; oy < kDwSmallMaxOH; ++oy)
+            if (oy < p.OH) o[oy * p.OW] = res[oy];
+    }
+    __syncthreads();
+    const int np = min(p.PPW, p.NC - pl0);
+    const int total = np * OHW;  // <= PPW * HP * LDSW floats: within the windows
+    float* yb = p.y + (long long)pl0 * OHW;
+    if (reinterpret_cast<uintptr_t>(yb) % 16 == 0) {
+        const int n4 = total >> 2;
+        for (int i = tid; i < n4; i += kDwThreads)
+            reinterpret_cast<float4*>(yb)[i] = reinterpret_cast<const float4*>(lds)[i];
+        for (int i = 4 * n4 + tid; i < total; i += kDwThreads) yb[i] = lds[i];
+    } else {
+        for (int i = tid; i < total; i += kDwThreads) yb[i] = lds[i];
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -472,6 +629,38 @@ hipError_t launch_depthwise(const void* x, const void* w, float* y, int N, int C
     p.OW = (W + 2 * pad - KW) / stride + 1;
     p.epilogue = epilogue;
     if (KH * KW > kDwMaxTaps || p.OH <= 0 || p.OW <= 0) return hipErrorInvalidValue;
+    if (KH == 3 && KW == 3 && stride == 1 && pad <= 1 && W <= kDwSmallMaxW && p.OH <= kDwSmallMaxOH &&
+        reinterpret_cast<uintptr_t>(x) % 4 == 0 && (dtype == DT_F32 || W % 2 == 0)) {
+        // small planes: whole planes a workgroup, one output column a lane
+        DwSmallParams q{};
+        q.x = x; q.w = w; q.y = y; q.bias = p.bias; q.var = p.var; q.eps = eps;
+        q.NC = p.NC; q.C = C; q.H = H; q.W = W; q.pad = pad; q.OH = p.OH; q.OW = p.OW;
+        q.HP = H + 2 * pad;
+        q.LDSW = (W + 2 * pad) | 1;  // odd pitch: a wave's rows start on different banks
+        q.PPW = std::min(kDwThreads / q.OW, kDwSmallLds / (q.HP * q.LDSW * 4));
+        q.groups = (q.NC + q.PPW - 1) / q.PPW;
+        q.epilogue = epilogue;
+        q.rHP = 1.0 / (double)q.HP;
+        q.rOW = 1.0 / (double)q.OW;
+        const int bytes = q.PPW * q.HP * q.LDSW * 4;
+        (void)hipGetLastError();
+        switch (dtype) {
+            case DT_F32:
+                hipLaunchKernelGGL(conv_depthwise_small_kernel<DT_F32>, dim3((unsigned)q.groups), dim3(kDwThreads),
+                                   bytes, stream, q);
+                break;
+            case DT_F16:
+                hipLaunchKernelGGL(conv_depthwise_small_kernel<DT_F16>, dim3((unsigned)q.groups), dim3(kDwThreads),
+                                   bytes, stream, q);
+                break;
+            case DT_BF16:
+                hipLaunchKernelGGL(conv_depthwise_small_kernel<DT_BF16>, dim3((unsigned)q.groups), dim3(kDwThreads),
+                                   bytes, stream, q);
+                break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     if ((long long)H * W >= (1LL << 31)) return hipErrorInvalidValue;
     const int bytes = depthwise_plan(p.NC, p.OH, p.OW, KH, KW, stride, &p.RB, &p.RIN, &p.WPAD, &p.LDSW,
                                      &p.PPW, &p.TAPS);

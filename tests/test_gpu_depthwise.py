@@ -47,6 +47,14 @@ SHAPES = [
     (1, 1, 4, 4, 3, 3, 1, 10),
     (2, 3, 20, 20, 3, 3, 5, 9),
     (3, 2, 7, 9, 2, 2, 3, 4),
+    # small-plane form (3x3, stride 1, pad <= 1, rows of at most 32): planes
+    # packed 18 a workgroup with a ragged last group, the widest row, pad 0,
+    # the tallest output, and a single output pixel per plane
+    (3, 37, 14, 14, 3, 3, 1, 1),
+    (2, 5, 16, 32, 3, 3, 1, 1),
+    (2, 4, 12, 10, 3, 3, 1, 0),
+    (1, 3, 34, 6, 3, 3, 1, 0),
+    (1, 2, 3, 3, 3, 3, 1, 0),
 ]
 EPIS = [ct.CT_EPI_NONE, ct.CT_EPI_BIAS, ct.CT_EPI_EXP_BIAS_RSQRT]
 
