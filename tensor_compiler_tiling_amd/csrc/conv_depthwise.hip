@@ -638,6 +638,9 @@ hipError_t launch_depthwise(const void* x, const void* w, float* y, int N, int C
         q.HP = H + 2 * pad;
         q.LDSW = (W + 2 * pad) | 1;  // odd pitch: a wave's rows start on different banks
         q.PPW = std::min(kDwThreads / q.OW, kDwSmallLds / (q.HP * q.LDSW * 4));
+        // a power of two: with N*C one too, the grid is whole rounds of
+        // workgroups (18 planes of 14x14 left the last round 78% full)
+        while (q.PPW & (q.PPW - 1)) q.PPW &= q.PPW - 1;
         q.groups = (q.NC + q.PPW - 1) / q.PPW;
         q.epilogue = epilogue;
         q.rHP = 1.0 / (double)q.HP;
