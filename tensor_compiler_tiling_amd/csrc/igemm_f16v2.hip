@@ -696,13 +696,16 @@ __global__ __launch_bounds__((WM * WN + NXW) * 64) void igemm_h2_kernel(H2Params
             for (int rn = 0; rn < RN; ++rn)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
+                    // every split's partial from memory, this one's too (the
+                    // same value as its registers, so the sum is unchanged):
+                    // selecting the registers for s2 == split compiled, in
+                    // some of the forms with staging waves, to code that read
+                    // a wrong value for the first element of each block
                     const int o = (base + (rm * RN + rn) * 16 + r) * 64 + lane;
                     float sum = 0.0f;
                     for (int s2 = 0; s2 < p.S; ++s2) {
-                        const float v = (s2 == split)
-                                            ? acc[rm][rn][r]
-                                            : __hip_atomic_load(&part[(long long)s2 * tile_words + o],
-                                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        const float v = __hip_atomic_load(&part[(long long)s2 * tile_words + o], __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
                         sum = (s2 == 0) ? v : sum + v;
                     }
                     acc[rm][rn][r] = sum;
