@@ -379,13 +379,15 @@ __global__ __launch_bounds__(WM * WN * 64) void igemm_h_kernel(ConvParams p) {
             for (int rn = 0; rn < RN; ++rn)
                 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
+                    // every split's partial from memory, this one's too (its
+                    // registers hold the same values; a per-split choice
+                    // between registers and memory is a form the compiler
+                    // has mistranslated in the second fp16 kernel)
                     const int o = (base + (rm * RN + rn) * 16 + r) * 64 + lane;
                     float sum = 0.0f;
                     for (int s2 = 0; s2 < p.S; ++s2) {
-                        const float v = (s2 == split)
-                                            ? acc[rm][rn][r]
-                                            : __hip_atomic_load(&part[(long long)s2 * tile_words + o],
-                                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        const float v = __hip_atomic_load(&part[(long long)s2 * tile_words + o], __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
                         sum = (s2 == 0) ? v : sum + v;
                     }
                     acc[rm][rn][r] = sum;
