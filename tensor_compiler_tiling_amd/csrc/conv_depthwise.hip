@@ -40,7 +40,8 @@
 // with 4-byte loads, and each compute lane walks one output column top to
 // bottom with the filter and a 3-row window in registers (3 LDS reads and 9
 // FMAs an output).  The planes' outputs are one contiguous run of y: they go
-// through LDS and out in 16-byte stores.
+// through LDS and out in 16-byte non-temporal stores (whole lines, not read
+// again by the launch).
 #include "ct_device.hpp"
 
 #include <hip/hip_runtime.h>
@@ -382,6 +383,8 @@ __global__ __launch_bounds__(kDwThreads) void conv_depthwise_kernel(DwParams p) 
 }
 
 // ---- small planes ----------------------------------------------------------
+typedef float floatv4 __attribute__((ext_vector_type(4)));  // for the non-temporal 16-byte stores
+
 struct DwSmallParams {
     const void* x;
     const void* w;
@@ -521,7 +524,7 @@ __global__ __launch_bounds__(kDwThreads) void conv_depthwise_small_kernel(DwSmal
     if (reinterpret_cast<uintptr_t>(yb) % 16 == 0) {
         const int n4 = total >> 2;
         for (int i = tid; i < n4; i += kDwThreads)
-            reinterpret_cast<float4*>(yb)[i] = reinterpret_cast<const float4*>(lds)[i];
+            __builtin_nontemporal_store(reinterpret_cast<const floatv4*>(lds)[i], &reinterpret_cast<floatv4*>(yb)[i]);
         for (int i = 4 * n4 + tid; i < total; i += kDwThreads) yb[i] = lds[i];
     } else {
         for (int i = tid; i < total; i += kDwThreads) yb[i] = lds[i];
