@@ -173,6 +173,32 @@ def test_legality_rejects_oversized_stage():
                 assert cfg.kc * 9 <= v["kc_max"]
 
 
+def test_staging_wave_variants_describe_their_workgroup():
+    """The fp16 variants with window-staging waves (names ending _x1, _x2)
+    report the whole workgroup: the matrix waves' threads plus 64 a staging
+    wave; every other tiled variant reports its matrix waves alone."""
+    seen = 0
+    for v in ct.variants():
+        if v["kind"] != 1:
+            continue
+        matrix = v["waves_m"] * v["waves_n"] * v["waves_k"] * 64
+        tail = v["name"].rsplit("_", 1)[-1]
+        if v["name"].startswith(("h2f16_", "h2bf16_")) and tail in ("x1", "x2"):
+            assert v["threads"] == matrix + 64 * int(tail[1]), v
+            seen += 1
+        else:
+            assert v["threads"] == matrix, v
+    assert seen >= 3
+    # the shipped tuning log picks one of them for the 64x256x14x14 fp16 layer,
+    # and it is legal there
+    w = wl.CONV_WORKLOADS["f16_n64_c256_14x14_k3"]
+    by_name = {v["name"]: v for v in ct.variants()}
+    x2 = by_name["h2f16_m128n128_w2x2_r2x2_kc16_x2"]
+    legal = [cfg for i in range(ct.ct_conv2d_space_size(*_args(w)))
+             for st, cfg, ok in [ct.ct_conv2d_space_entity(*_args(w), i)] if ok and cfg.variant == x2["id"]]
+    assert legal
+
+
 def test_query_default_without_gpu():
     ct.ct_cache_clear()
     for w in wl.CONV_WORKLOADS.values():
