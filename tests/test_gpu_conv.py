@@ -450,6 +450,22 @@ def test_half_precision_full_size_every_variant(name):
 
 
 @pytest.mark.parametrize("name", HALF_FULL)
+def test_half_precision_full_size_staging_waves_split(name):
+    """Full-size half-precision workloads through every variant with
+    window-staging waves at a two-way split (the last arriving workgroup of
+    a tile sums both partials), every output against the oracle."""
+    w = wl.CONV_WORKLOADS[name]
+    inp, y, a = _half_full_reference(name)
+    cfgs = [cfg for cfg in legal_configs(w, epilogue=ct.CT_EPI_NONE)
+            if cfg.split_k == 2 and ct.variants()[cfg.variant]["name"].rsplit("_", 1)[-1] in ("x1", "x2")]
+    say(f"[conv-f16-staging-split] {name}: {len(cfgs)} configs")
+    assert cfgs
+    for cfg in cfgs:
+        got = run(w, inp, config=cfg, epilogue=ct.CT_EPI_NONE)
+        assert_conv_close(got, y, a, w.dtype, f"{ct.variants()[cfg.variant]['name']} S=2 stages={cfg.stages}")
+
+
+@pytest.mark.parametrize("name", HALF_FULL)
 def test_half_precision_full_size_integers_bit_exact(name):
     """Full-size half-precision workloads on integer inputs in [-2, 2] (exact
     in fp16): every partial sum is an integer of at most 4*CI*KH*KW (9,216 for
