@@ -23,7 +23,8 @@ bracket the K steps.
 With no --workload the line also carries `per_shape`: every other row of
 the workload table (the batch-1 fp32 layers, both half-precision layers with
 the filter reordered per call and prepared once, the standalone broadcast in
-fp16 and fp32), each timed the same way.
+fp16 and fp32, the two matrix products, the three depthwise layers and the
+batch-norm chain), each timed the same way.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -568,7 +569,8 @@ def per_shape(a) -> list:
     """Every other row of the workload table, each timed the way the headline
     is (a HIP graph of back-to-back launches, HIP events on its stream): the
     batch-1 fp32 layers, both half-precision layers (the filter reordered per
-    call, and prepared once), and the standalone broadcast in fp16 and fp32."""
+    call, and prepared once), the standalone broadcast in fp16 and fp32, the
+    matrix products, the depthwise layers and the batch-norm chain."""
     import torch
     from tensor_compiler_tiling_amd import convtile as ct
     from tensor_compiler_tiling_amd import workloads as wl
@@ -616,6 +618,51 @@ def per_shape(a) -> list:
                     "traffic": measured_traffic(name, "broadcast", {"mode": "channel"})})
         del outs
         torch.cuda.empty_cache()
+    # the matrix products, through ct_gemm_fwd with the tuned config (their
+    # 1x1 convolution views give the seeded operands)
+    dev = torch.device("cuda:0")
+    for name, g in wl.GEMM_WORKLOADS.items():
+        w = g.conv_view()
+        tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+        dt = ct.dtype_code(tdt)
+        inp = wl.conv_inputs(w)
+        xg = torch.from_numpy(inp["x"]).to(dev).to(tdt)
+        kg = torch.from_numpy(inp["w"]).to(dev).to(tdt)
+        bg = torch.from_numpy(inp["bias"]).to(dev)
+        vg = torch.from_numpy(inp["var"]).to(dev)
+        yg = torch.empty((w.N, w.CO, w.OH, w.OW), dtype=torch.float32, device=dev)
+        lib = ct.library()
+        gargs = (kg.data_ptr(), xg.data_ptr(), yg.data_ptr(), g.M, g.N, g.K, dt, w.epilogue,
+                 bg.data_ptr(), vg.data_ptr(), 1e-5, stream.cuda_stream)
+
+        def gstep():
+            st = lib.ct_gemm_fwd(*gargs)
+            if st != 0:
+                raise ct.ConvTileError(st, "gemm")
+
+        st, cfg, _ = ct.ct_gemm_query(g.M, g.N, g.K, dt, w.epilogue)
+        ct.check(st, "query")
+        ms = time_graph(gstep, stream, max(20, steps // 5), a.warmup)
+        tf = w.flops / (ms * 1e-3) / 1e12
+        vname = ct.variants()[cfg.variant]["name"]
+        tile = {"split_k": cfg.split_k, "stages": cfg.stages, "kc": cfg.kc}
+        out.append({"workload": name, "dtype": w.dtype, "us": round(ms * 1e3, 3), "TFLOP/s": round(tf, 2),
+                    "bound": "mfma", "frac": round(tf / PEAK_TFLOPS[w.dtype], 4), "kernel": vname,
+                    "tile": tile, "traffic": measured_traffic(name, vname, tile)})
+        del xg, kg, yg
+        torch.cuda.empty_cache()
+    # the depthwise layers and the batch-norm chain, timed by their own
+    # --workload functions (rotating buffers), summarised
+    sub = argparse.Namespace(**vars(a))
+    sub.eager, sub.no_cpu_baseline, sub.steps = False, True, steps
+    for name, fn, kernel in ([(n, bench_depthwise, "depthwise") for n in wl.DEPTHWISE_WORKLOADS] +
+                             [(n, bench_chain, "chain_channel") for n in wl.CHAIN_WORKLOADS]):
+        r = fn(sub, name)
+        out.append({"workload": name, "dtype": r["dtype"], "us": round(r["ms_per_step"] * 1e3, 3),
+                    "GB/s": r["value"], "bound": "hbm", "frac": r["roofline"]["frac"], "kernel": kernel,
+                    "rotating_buffers": r["config"]["rotating_buffers"], "traffic": r["roofline"]["traffic"]})
+        torch.cuda.empty_cache()
+    torch.cuda.set_stream(stream)
     return out
 
 
