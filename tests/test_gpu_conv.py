@@ -465,6 +465,22 @@ def test_half_precision_full_size_staging_waves_split(name):
         assert_conv_close(got, y, a, w.dtype, f"{ct.variants()[cfg.variant]['name']} S=2 stages={cfg.stages}")
 
 
+def test_bf16_full_size_staging_waves():
+    """The 64x256x14x14 layer in bf16 (inputs rounded to bf16, the same
+    seeded draw) through every bf16 variant with window-staging waves, at
+    one and two splits, every output against the oracle."""
+    w = wl.ConvWorkload("bf16_n64_c256_14x14_k3", 4, 64, 256, 14, 14, 256, 3, 3, 1, 1, wl.BF16)
+    inp = wl.conv_inputs(w)
+    y, a = oracle_full(w, inp)
+    cfgs = [cfg for cfg in legal_configs(w, epilogue=ct.CT_EPI_NONE)
+            if cfg.split_k <= 2 and ct.variants()[cfg.variant]["name"].rsplit("_", 1)[-1] in ("x1", "x2")]
+    say(f"[conv-bf16-staging] {len(cfgs)} configs")
+    assert cfgs
+    for cfg in cfgs:
+        got = run(w, inp, config=cfg, epilogue=ct.CT_EPI_NONE)
+        assert_conv_close(got, y, a, w.dtype, f"{ct.variants()[cfg.variant]['name']} S={cfg.split_k}")
+
+
 @pytest.mark.parametrize("name", HALF_FULL)
 def test_half_precision_full_size_integers_bit_exact(name):
     """Full-size half-precision workloads on integer inputs in [-2, 2] (exact
